@@ -1,0 +1,215 @@
+"""Expert-FFN oracle in fp64, step by step (test infrastructure).
+
+Test infrastructure (see the package docstring).
+
+What is computed, and where the pages say it
+--------------------------------------------
+For every token t and route j with expert e = topk_ids[t, j] in [0, E):
+
+  1. dequantize x[t], w1[e], w2[e] exactly into fp64
+       * bf16 path: the bf16 values themselves;
+       * blockwise FP8 path: e4m3 value times the fp32 scale of its block,
+         1 x 128 for activations and 128 x 128 for weights (the blockwise W8A8
+         format the [hpc-ops RFC] "Background" section names, with the block
+         shapes of the blockwise configurations);
+       * mxfp8 path: e4m3 value times the e8m0 scale of its 32-wide block along
+         the contraction dimension ([prime-flash] "Scale layout (mxfp8)").
+  2. gate/up GEMM: G = x[t] . w1[e]^T, N = 2I columns; gate = G[:I],
+     up = G[I:] ([hpc-ops RFC] "Background" stage 2; [prime-flash] "Shapes":
+     w1 is (E, N, K) with N the fused gate+up columns).
+  3. SwiGLU: h = silu(gate) * up, silu(g) = g / (1 + e^-g)
+     ([hpc-ops RFC] "Background" stage 3; [prime-flash] intro).
+  4. requantize h before the down GEMM
+       * blockwise: per row and 128 columns, amax clamped below at 1e-10,
+         sf = amax * (1/448), sf_inv = 1/sf, q = e4m3(h * sf_inv), value q*sf
+         ([DeepGEMM #88] "Before you merge": the requant scale expression and
+         the per-128 grouping);
+       * mxfp8: per row and 32 columns, OCP MX rule: shared exponent
+         floor(log2 amax) - 8 (8 = exponent of e4m3's largest power of two),
+         elements rounded to e4m3 with saturation ([prime-flash] intro: the
+         intermediate is requantized to mxfp8 on chip; "Scale layout" names the
+         OCP MX quantizer);
+       * bf16: h rounded to bf16, since the down GEMM takes bf16 operands (the
+         pages are silent; plainest reading).
+  5. down GEMM: y = hq . w2[e]^T, w2 is (E, K, I) ([hpc-ops RFC] stage 4;
+     [prime-flash] "Shapes").
+  6. top-k weighted combine: out[t] = sum_j topk_weights[t, j] * y_j, the
+     weight applied after the down GEMM, summed in fp64; the bf16 output is
+     one rounding of that sum ([hpc-ops RFC] stage 5; [prime-flash] intro:
+     "top-k weighted reduction").
+
+Requantization decisions (rounding to e4m3 / bf16, the power-of-two MX scale)
+are taken on h rounded to binary32, the precision the kernels hold h in; the
+GEMMs and the combine stay in fp64.
+
+The loop runs per expert so that only one expert's dequantized weights are
+held at a time.
+"""
+
+import numpy as np
+
+from . import codecs
+
+
+def _silu(g):
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def _swiglu(G, I):
+    """silu(gate) * up with gate = first I columns, up = last I columns."""
+    return _silu(G[:, :I]) * G[:, I:]
+
+
+def dequant_x(kind, x, x_scale, rows):
+    """fp64 activations for the given token rows."""
+    if kind == "bf16":
+        return codecs.bf16_decode(x[rows])
+    v = codecs.e4m3_decode(x[rows])
+    if kind == "fp8_blockwise":
+        return v * np.repeat(x_scale[rows].astype(np.float64), 128, axis=1)
+    if kind == "mxfp8":
+        return v * np.repeat(codecs.e8m0_decode(x_scale[rows]), 32, axis=1)
+    raise ValueError(kind)
+
+
+def dequant_w(kind, w, w_scale, e):
+    """fp64 weight matrix of expert e (rows = output features)."""
+    if kind == "bf16":
+        return codecs.bf16_decode(w[e])
+    v = codecs.e4m3_decode(w[e])
+    if kind == "fp8_blockwise":
+        s = w_scale[e].astype(np.float64)
+        return v * np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
+    if kind == "mxfp8":
+        return v * np.repeat(codecs.e8m0_decode(w_scale[e]), 32, axis=1)
+    raise ValueError(kind)
+
+
+def requant_blockwise(h):
+    """Per row and 128 columns: (codes uint8, scales fp32, dequantized fp64)."""
+    rows, I = h.shape
+    h32 = codecs.fp32(h).reshape(rows, I // 128, 128)
+    amax = np.max(np.abs(h32), axis=2)                        # exact in fp32
+    amax = np.maximum(amax, np.float32(1e-10))
+    sf = (amax * np.float32(1.0 / 448.0)).astype(np.float32)  # fp32 product
+    sf_inv = (np.float64(1.0) / sf.astype(np.float64)).astype(np.float32)
+    p = (h32 * sf_inv[:, :, None]).astype(np.float32)         # fp32 product
+    q = codecs.e4m3_encode(p.astype(np.float64))
+    hd = codecs.e4m3_decode(q) * sf.astype(np.float64)[:, :, None]
+    return q.reshape(rows, I), sf, hd.reshape(rows, I)
+
+
+def requant_mx(h):
+    """Per row and 32 columns: (codes uint8, e8m0 codes uint8, dequantized fp64)."""
+    rows, I = h.shape
+    h32 = codecs.fp32(h).reshape(rows, I // 32, 32)
+    amax = np.max(np.abs(h32), axis=2).astype(np.float64)
+    with np.errstate(divide="ignore"):
+        lg = np.floor(np.log2(np.where(amax > 0, amax, 1.0)))
+    s = np.where(amax > 0, np.clip(lg - 8, -127, 127), -127).astype(np.int64)
+    p = h32.astype(np.float64) * np.ldexp(1.0, -s)[:, :, None]
+    p = codecs.fp32(p).astype(np.float64)   # binary32 product, as the kernels
+    q = codecs.e4m3_encode(p)
+    hd = codecs.e4m3_decode(q) * np.ldexp(1.0, s)[:, :, None]
+    return q.reshape(rows, I), (s + 127).astype(np.uint8), hd.reshape(rows, I)
+
+
+def requant_bf16(h):
+    """h rounded to binary32 then to bfloat16: (bits uint16, None, fp64)."""
+    hd = codecs.bf16_round(codecs.fp32(h).astype(np.float64))
+    return codecs.bf16_encode(hd), None, hd
+
+
+def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
+            topk_weights, tokens=None, exact_h=False, keep_h=False):
+    """Fused MoE forward, fp64.
+
+    Arrays are numpy: bf16 data as uint16 bit patterns, e4m3 data as uint8
+    codes, blockwise scales as float32, MX scales as uint8 e8m0 codes.
+    Shapes: x (T, K); w1 (E, N, K); w2 (E, K, N/2); topk_ids, topk_weights
+    (T, top_k).
+
+    ``tokens``: optional sorted array of token indices; only those outputs are
+    computed (rows of the result follow that order).
+    ``exact_h``: bf16 path only, skip the bf16 rounding of h (used by the
+    dense-FFN special-case check).
+    ``keep_h``: also return, per computed route (t, j), the requantized
+    intermediate: codes, scales and dequantized values.
+
+    Returns a dict with ``out64`` (n, K) fp64, ``out_bf16`` (n, K) uint16, and
+    when ``keep_h`` a dict ``h`` mapping pair id t*top_k+j to
+    (codes, scales, values).
+    """
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    wts = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
+    T, k = ids.shape
+    E = w1.shape[0]
+    K = w1.shape[2]
+    I = w1.shape[1] // 2
+    if tokens is None:
+        tokens = np.arange(T)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    out64 = np.zeros((tokens.size, K), dtype=np.float64)
+    local = {int(t): i for i, t in enumerate(tokens)}
+    sel = ids[tokens]                                   # (n, k)
+    hkeep = {}
+    if kind == "bf16":
+        requant = requant_bf16
+    elif kind == "fp8_blockwise":
+        requant = requant_blockwise
+    elif kind == "mxfp8":
+        requant = requant_mx
+    else:
+        raise ValueError(kind)
+    for e in np.unique(sel):
+        if e < 0 or e >= E:
+            continue                                    # not a local expert
+        n_idx, j_idx = np.nonzero(sel == e)
+        t_rows = tokens[n_idx]
+        xd = dequant_x(kind, x, x_scale, t_rows)        # (m, K)
+        w1d = dequant_w(kind, w1, w1_scale, e)          # (N, K)
+        G = xd @ w1d.T                                  # (m, N)
+        del w1d
+        h = _swiglu(G, I)
+        if exact_h:
+            q, s, hd = None, None, h
+        else:
+            q, s, hd = requant(h)
+        w2d = dequant_w(kind, w2, w2_scale, e)          # (K, I)
+        y = hd @ w2d.T                                  # (m, K)
+        del w2d
+        for r in range(t_rows.size):
+            t = int(t_rows[r])
+            j = int(j_idx[r])
+            out64[local[t]] += wts[t, j] * y[r]
+            if keep_h:
+                hkeep[t * k + j] = (None if q is None else q[r],
+                                    None if s is None else s[r], hd[r])
+    res = {"out64": out64, "out_bf16": codecs.bf16_encode(out64)}
+    if keep_h:
+        res["h"] = hkeep
+    return res
+
+
+def tolerance_check(out_bits, out64, tol):
+    """Gate used by the parity tests (reading of the max-error and
+    mean-relative-error bounds for a bf16 output).
+
+    Element-wise: |out - out64| <= tol * rms(out64) + half a bf16 spacing at
+    out64 (the output format's own rounding).  Global: sum|out - out64| /
+    sum|out64| <= 5e-3.  Returns (ok, stats dict).
+    """
+    got = codecs.bf16_decode(out_bits)
+    ref = np.asarray(out64, dtype=np.float64)
+    err = np.abs(got - ref)
+    rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
+    bound = tol * rms + codecs.bf16_half_ulp(ref)
+    finite = bool(np.all(np.isfinite(got)))
+    max_ratio = float(np.max(err / np.where(rms > 0, rms, 1.0))) if ref.size else 0.0
+    denom = float(np.sum(np.abs(ref)))
+    mre = float(np.sum(err) / denom) if denom > 0 else 0.0
+    n_bad = int(np.sum(err > bound))
+    ok = finite and n_bad == 0 and mre <= 5e-3
+    return ok, {"rms": rms, "max_err_over_rms": max_ratio, "mean_rel_err": mre,
+                "n_over_bound": n_bad, "finite": finite}

@@ -1,0 +1,286 @@
+"""Pins for the expert-FFN oracle (CPU only).
+
+* hand-derived requantization goldens (tests/golden/requant_*.json);
+* a special case that reduces to a dense FFN written with np.matmul;
+* per-token brute-force loops in plain Python, with requantization done by
+  exhaustive nearest-code search (a different method from the oracle's);
+* invariants: linearity in the routing weights, empty experts contribute
+  nothing (their weights are NaN-poisoned), relabelling experts together with
+  their weights changes nothing, routing weights sum to 1.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from oracle import codecs
+from oracle.moe import moe_ref, requant_blockwise, requant_mx
+
+HERE = os.path.dirname(__file__)
+
+
+def _int(s):
+    return int(s, 16)
+
+
+# ---------------------------------------------------------------------------
+# requantization goldens and properties
+# ---------------------------------------------------------------------------
+
+def test_requant_blockwise_golden():
+    with open(os.path.join(HERE, "golden", "requant_blockwise.json")) as f:
+        g = json.load(f)
+    h = np.zeros((1, 256))
+    for i, v in g["row_values"].items():
+        h[0, int(i)] = v
+    q, s, hd = requant_blockwise(h)
+    for i, c in g["expected_codes"].items():
+        assert q[0, int(i)] == _int(c), (i, hex(q[0, int(i)]), c)
+    assert np.all(q[0, 9:128] == 0)
+    assert s[0, 0] == np.float32(eval(g["expected_scale"]))
+    z = np.float32(np.float32(1e-10) * np.float32(9586981 * 2.0 ** -32))
+    assert s[0, 1] == z and np.all(q[0, 128:] == 0)
+    assert np.all(hd[0] == codecs.e4m3_decode(q[0]) * np.repeat(s[0].astype(np.float64), 128))
+
+
+def test_requant_mx_golden():
+    with open(os.path.join(HERE, "golden", "requant_mx.json")) as f:
+        g = json.load(f)
+    n = len(g["groups"])
+    h = np.zeros((1, 32 * n))
+    for gi, grp in enumerate(g["groups"]):
+        for i, v in grp["values"].items():
+            h[0, 32 * gi + int(i)] = v
+    q, s, hd = requant_mx(h)
+    for gi, grp in enumerate(g["groups"]):
+        assert s[0, gi] == grp["expected_e8m0"]
+        for i, c in grp["expected_codes"].items():
+            assert q[0, 32 * gi + int(i)] == _int(c)
+        rest = [j for j in range(32) if str(j) not in grp["expected_codes"]]
+        assert np.all(q[0, [32 * gi + j for j in rest]] == 0)
+
+
+def test_requant_blockwise_properties():
+    rng = np.random.default_rng(11)
+    h = rng.normal(0, 3, (64, 512)) * np.exp2(rng.integers(-20, 20, (64, 1)))
+    q, s, hd = requant_blockwise(h)
+    mag = q & 0x7F
+    assert np.all(mag <= 0x7E)                                # |q| <= 448
+    # the amax element of each group lands on +-448
+    grp = np.abs(codecs.fp32(h)).reshape(64, 4, 128)
+    arg = np.argmax(grp, axis=2)
+    qg = q.reshape(64, 4, 128)
+    top = np.take_along_axis(qg, arg[:, :, None], axis=2)[:, :, 0]
+    assert np.all((top & 0x7F) == 0x7E)
+    # relative quantization error within e4m3's half-spacing (2^-4) of amax*...
+    rel = np.abs(hd - h) / np.repeat(grp.max(axis=2), 128, axis=1).reshape(64, 512)
+    assert rel.max() <= 2.0 ** -4 * 1.0001
+
+
+def test_requant_mx_properties():
+    rng = np.random.default_rng(12)
+    h = rng.normal(0, 1, (32, 256)) * np.exp2(rng.integers(-30, 30, (32, 1)))
+    q, s, hd = requant_mx(h)
+    amax = np.abs(codecs.fp32(h)).reshape(32, 8, 32).max(axis=2)
+    assert np.all(s.astype(int) - 127 == np.floor(np.log2(amax)) - 8)
+    # values already on the scaled grid round-trip exactly
+    q2, s2, hd2 = requant_mx(hd)
+    assert np.array_equal(hd2, hd) and np.array_equal(q2, q)
+
+
+# ---------------------------------------------------------------------------
+# brute force
+# ---------------------------------------------------------------------------
+
+TABLE = codecs.e4m3_decode(np.arange(256, dtype=np.uint8))
+FIN = [c for c in range(256) if not math.isnan(TABLE[c])]
+
+
+def nearest_e4m3(v):
+    v = min(max(v, -448.0), 448.0)
+    best = min(abs(TABLE[c] - v) for c in FIN)
+    cands = [c for c in FIN if abs(TABLE[c] - v) == best]
+    if len(cands) > 1:
+        cands = [c for c in cands if c % 2 == 0]
+    return TABLE[cands[0]]
+
+
+def brute_requant(kind, h):
+    f32 = np.float32
+    h32 = [f32(v) for v in h]
+    if kind == "bf16":
+        return [float(torch.tensor(float(v), dtype=torch.float32).to(torch.bfloat16))
+                for v in h32]
+    out = []
+    G = 128 if kind == "fp8_blockwise" else 32
+    for g0 in range(0, len(h32), G):
+        grp = h32[g0:g0 + G]
+        amax = max(abs(v) for v in grp)
+        if kind == "fp8_blockwise":
+            amax = max(amax, f32(1e-10))
+            sf = f32(amax * f32(1.0 / 448.0))
+            inv = f32(f32(1.0) / sf)
+            out += [nearest_e4m3(float(f32(v * inv))) * float(sf) for v in grp]
+        else:
+            if amax == 0:
+                s = -127
+            else:
+                _, ex = math.frexp(float(amax))
+                s = max(-127, min(127, ex - 1 - 8))
+            out += [nearest_e4m3(float(f32(float(v) * 2.0 ** -s))) * 2.0 ** s
+                    for v in grp]
+    return out
+
+
+def brute_force(kind, d, t):
+    x, xs, w1, s1, w2, s2 = d["x"], d["x_scale"], d["w1"], d["w1_scale"], d["w2"], d["w2_scale"]
+    ids, wts = d["topk_ids"], d["topk_weights"]
+    E, N, K = w1.shape
+    I = N // 2
+
+    def deq(arr, scale, e, r, c, rowwise):
+        if kind == "bf16":
+            return float(codecs.bf16_decode(np.array([arr[e][r, c] if e is not None else arr[r, c]]))[0])
+        v = TABLE[arr[e][r, c] if e is not None else arr[r, c]]
+        if kind == "fp8_blockwise":
+            if rowwise:
+                return v * float(scale[r, c // 128])
+            return v * float(scale[e][r // 128, c // 128])
+        sc = scale[e][r, c // 32] if e is not None else scale[r, c // 32]
+        return v * 2.0 ** (int(sc) - 127)
+
+    out = [0.0] * K
+    xv = [deq(x, xs, None, t, c, True) for c in range(K)]
+    for j in range(ids.shape[1]):
+        e = int(ids[t, j])
+        if not 0 <= e < E:
+            continue
+        g = [sum(xv[c] * deq(w1, s1, e, n, c, False) for c in range(K)) for n in range(I)]
+        u = [sum(xv[c] * deq(w1, s1, e, I + n, c, False) for c in range(K)) for n in range(I)]
+        h = [g[n] / (1.0 + math.exp(-g[n])) * u[n] for n in range(I)]
+        hq = brute_requant(kind, h)
+        for c in range(K):
+            y = sum(hq[n] * deq(w2, s2, e, c, n, False) for n in range(I))
+            out[c] += float(wts[t, j]) * y
+    return np.array(out)
+
+
+def small_case(kind, T, K, I, E, k, routing="normal", seed="pin"):
+    c = datagen.make_case(kind, T, K, I, E, k, routing=routing, tag=seed)
+    return datagen.to_numpy(c)
+
+
+def run(d, **kw):
+    return moe_ref(d["kind"], d["x"], d["x_scale"], d["w1"], d["w1_scale"], d["w2"],
+                   d["w2_scale"], d["topk_ids"], d["topk_weights"], **kw)
+
+
+@pytest.mark.parametrize("kind,K,I", [("bf16", 64, 32), ("fp8_blockwise", 256, 128),
+                                      ("mxfp8", 64, 64)])
+def test_brute_force_per_token(kind, K, I):
+    d = small_case(kind, 4, K, I, 4, 2)
+    ref = run(d)["out64"]
+    for t in range(4):
+        bf = brute_force(kind, d, t)
+        np.testing.assert_allclose(ref[t], bf, rtol=1e-10, atol=1e-12 * np.abs(bf).max())
+
+
+def test_brute_force_out_of_range_ids_skipped():
+    d = small_case("fp8_blockwise", 3, 128, 128, 4, 2)
+    d["topk_ids"] = d["topk_ids"].copy()
+    d["topk_ids"][0, 1] = -1
+    d["topk_ids"][2, 0] = 7
+    ref = run(d)["out64"]
+    for t in range(3):
+        np.testing.assert_allclose(ref[t], brute_force("fp8_blockwise", d, t), rtol=1e-10,
+                                   atol=1e-14)
+
+
+def test_dense_ffn_special_case():
+    """E=1, top-1 with weight 1 and no rounding of h is a dense SwiGLU FFN."""
+    d = small_case("bf16", 16, 128, 64, 1, 1)
+    d["topk_weights"] = np.ones_like(d["topk_weights"])
+    out = run(d, exact_h=True)["out64"]
+    X = codecs.bf16_decode(d["x"])
+    W1 = codecs.bf16_decode(d["w1"][0])
+    W2 = codecs.bf16_decode(d["w2"][0])
+    gate = X @ W1[:64].T
+    up = X @ W1[64:].T
+    dense = (gate * (1.0 / (1.0 + np.exp(-gate))) * up) @ W2.T
+    np.testing.assert_allclose(out, dense, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("kind,K,I", [("bf16", 128, 64), ("fp8_blockwise", 256, 256),
+                                      ("mxfp8", 128, 64)])
+def test_linearity_in_routing_weights(kind, K, I):
+    d = small_case(kind, 8, K, I, 6, 3)
+    full = run(d)["out64"]
+    acc = np.zeros_like(full)
+    for j in range(3):
+        dj = dict(d)
+        w = np.zeros_like(d["topk_weights"])
+        w[:, j] = 1.0
+        dj["topk_weights"] = w
+        acc += d["topk_weights"][:, j:j + 1].astype(np.float64) * run(dj)["out64"]
+    np.testing.assert_allclose(full, acc, rtol=1e-12, atol=1e-14 * np.abs(full).max())
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8"])
+def test_empty_experts_contribute_nothing(kind):
+    d = small_case(kind, 4, 256, 128, 16, 2)
+    base = run(d)["out64"]
+    used = set(np.unique(d["topk_ids"]).tolist())
+    empty = [e for e in range(16) if e not in used]
+    assert empty
+    p = {n: (v.copy() if isinstance(v, np.ndarray) else v) for n, v in d.items()}
+    for e in empty:
+        if kind == "bf16":
+            p["w1"][e] = 0x7FC0
+            p["w2"][e] = 0x7FC0
+        else:
+            p["w1"][e] = 0x7F
+            p["w2"][e] = 0x7F
+            if kind == "fp8_blockwise":
+                p["w1_scale"][e] = np.nan
+                p["w2_scale"][e] = np.nan
+            else:
+                p["w1_scale"][e] = 255
+                p["w2_scale"][e] = 255
+    out = run(p)["out64"]
+    assert np.all(np.isfinite(out))
+    assert np.array_equal(out, base)
+
+
+def test_expert_relabelling_invariance():
+    d = small_case("fp8_blockwise", 6, 256, 128, 8, 3)
+    base = run(d)["out64"]
+    perm = np.random.default_rng(5).permutation(8)
+    p = dict(d)
+    p["topk_ids"] = perm[d["topk_ids"]].astype(np.int32)
+    for n in ("w1", "w1_scale", "w2", "w2_scale"):
+        arr = np.empty_like(d[n])
+        arr[perm] = d[n]
+        p[n] = arr
+    np.testing.assert_allclose(run(p)["out64"], base, rtol=1e-12, atol=1e-15)
+
+
+def test_routing_weights_sum_to_one():
+    for routing in ("uniform", "normal", "normal_masked", "zipf"):
+        ids, w = datagen.make_routing(500, 64, 6, routing)
+        s = w.double().sum(dim=1)
+        assert torch.all((s - 1).abs() < 1e-6)
+        assert torch.all(w > 0)
+        # ids distinct per token
+        assert all(len(set(r)) == 6 for r in ids.tolist())
+
+
+def test_token_subset_matches_full():
+    d = small_case("fp8_blockwise", 10, 256, 128, 8, 2)
+    full = run(d)["out64"]
+    sub = run(d, tokens=np.array([1, 4, 9]))["out64"]
+    np.testing.assert_allclose(sub, full[[1, 4, 9]], rtol=1e-12, atol=1e-15)
