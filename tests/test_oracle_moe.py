@@ -19,7 +19,8 @@ import torch
 
 import datagen
 from oracle import codecs
-from oracle.moe import moe_ref, requant_blockwise, requant_mx
+from oracle.moe import (ABS_BAND, REL_BAND, moe_ref, requant_blockwise, requant_bf16, requant_mx,
+                        tolerance_check)
 
 HERE = os.path.dirname(__file__)
 
@@ -38,7 +39,7 @@ def test_requant_blockwise_golden():
     h = np.zeros((1, 256))
     for i, v in g["row_values"].items():
         h[0, int(i)] = v
-    q, s, hd = requant_blockwise(h)
+    q, s, hd, alt = requant_blockwise(h)
     for i, c in g["expected_codes"].items():
         assert q[0, int(i)] == _int(c), (i, hex(q[0, int(i)]), c)
     assert np.all(q[0, 9:128] == 0)
@@ -56,7 +57,7 @@ def test_requant_mx_golden():
     for gi, grp in enumerate(g["groups"]):
         for i, v in grp["values"].items():
             h[0, 32 * gi + int(i)] = v
-    q, s, hd = requant_mx(h)
+    q, s, hd, alt = requant_mx(h)
     for gi, grp in enumerate(g["groups"]):
         assert s[0, gi] == grp["expected_e8m0"]
         for i, c in grp["expected_codes"].items():
@@ -68,7 +69,7 @@ def test_requant_mx_golden():
 def test_requant_blockwise_properties():
     rng = np.random.default_rng(11)
     h = rng.normal(0, 3, (64, 512)) * np.exp2(rng.integers(-20, 20, (64, 1)))
-    q, s, hd = requant_blockwise(h)
+    q, s, hd, _ = requant_blockwise(h)
     mag = q & 0x7F
     assert np.all(mag <= 0x7E)                                # |q| <= 448
     # the amax element of each group lands on +-448
@@ -85,11 +86,11 @@ def test_requant_blockwise_properties():
 def test_requant_mx_properties():
     rng = np.random.default_rng(12)
     h = rng.normal(0, 1, (32, 256)) * np.exp2(rng.integers(-30, 30, (32, 1)))
-    q, s, hd = requant_mx(h)
+    q, s, hd, _ = requant_mx(h)
     amax = np.abs(codecs.fp32(h)).reshape(32, 8, 32).max(axis=2)
     assert np.all(s.astype(int) - 127 == np.floor(np.log2(amax)) - 8)
     # values already on the scaled grid round-trip exactly
-    q2, s2, hd2 = requant_mx(hd)
+    q2, s2, hd2, _ = requant_mx(hd)
     assert np.array_equal(hd2, hd) and np.array_equal(q2, q)
 
 
@@ -284,3 +285,81 @@ def test_token_subset_matches_full():
     full = run(d)["out64"]
     sub = run(d, tokens=np.array([1, 4, 9]))["out64"]
     np.testing.assert_allclose(sub, full[[1, 4, 9]], rtol=1e-12, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# near-tie allowance
+# ---------------------------------------------------------------------------
+
+def test_near_tie_alt_blockwise():
+    """h = 2 sets sf_inv = 224 - 2^-16 (see the blockwise golden); an element
+    whose scaled value sits on the 352/384 midpoint (368) is a near-tie with
+    alternative distance one step (32 * sf); one 0.3 step away is not."""
+    sf_inv = 224.0 - 2.0 ** -16
+    h = np.zeros((1, 128))
+    h[0, 0] = 2.0
+    h[0, 1] = 368.0 / sf_inv * (1 + 1e-7)       # a hair above the midpoint
+    h[0, 2] = (352.0 + 0.3 * 32) / sf_inv       # 30% into the step: clear
+    q, s, hd, alt = requant_blockwise(h)
+    sf = float(s[0, 0])
+    assert q[0, 1] == 0x7C                      # 384: rounds up
+    assert alt[0, 1] == pytest.approx(32 * sf)
+    assert alt[0, 2] == 0.0
+    assert alt[0, 0] == 0.0                     # the amax element is 448, exact
+    # near zero the absolute band (448 * 2^-16 in scaled units) reaches the
+    # smallest subnormal codes: the allowance there is about that band
+    assert 0 <= alt[0, 100] <= (448.0 * ABS_BAND + 2.0 ** -9) * sf
+
+
+def test_near_tie_alt_mx_scale():
+    """amax a hair below a power of two: the shared exponent itself is a
+    near-tie and the allowance covers the other exponent's result."""
+    h = np.zeros((1, 32))
+    h[0, 0] = 4.0 * (1 - 1e-6)
+    h[0, 1] = 1.3
+    q, s, hd, alt = requant_mx(h)
+    assert s[0, 0] == 127 + 1 - 8               # floor(log2 3.999996) = 1
+    # with exponent -7 the amax element saturates (511.99 -> 448, 3.5) while
+    # exponent -6 gives 256 (4.0): the allowance covers that 0.5
+    assert alt[0, 0] == pytest.approx(0.5)
+    # a normal element lands on the same value under either exponent (the
+    # e4m3 grid is invariant under power-of-two scaling), so no allowance
+    assert alt[0, 1] == 0.0
+    h[0, 0] = 3.0
+    q, s, hd, alt = requant_mx(h)
+    assert alt[0, 0] == 0.0
+
+
+def test_near_tie_alt_bf16():
+    h = np.zeros((1, 128))
+    h[0, 0] = 1.0
+    h[0, 1] = 0.5 + 2.0 ** -9                   # midpoint (bf16 spacing at 0.5 is 2^-8)
+    h[0, 2] = 0.5 + 2.0 ** -10                  # 2^-10 from the midpoint, band ~2^-14
+    _, _, hd, alt = requant_bf16(h)
+    assert alt[0, 1] == pytest.approx(2.0 ** -8)
+    assert alt[0, 2] == 0.0
+
+
+@pytest.mark.parametrize("kind,K,I,T", [("fp8_blockwise", 512, 384, 600), ("mxfp8", 256, 256, 300),
+                                        ("bf16", 256, 256, 300)])
+def test_flip_bound_covers_fp32_deviation(kind, K, I, T):
+    """Soundness of the allowance: perturb h by relative noise of the size a
+    kernel's fp32 summation leaves (4e-5, twice the deviations measured on the
+    GPU) and requantize.  The perturbed outputs pass the gate with the
+    allowance; for the blockwise case the strict bound alone fails (so the
+    near-ties are real and the allowance is what covers them)."""
+    d = small_case(kind, T, K, I, 8, 4, routing="uniform", seed="tie")
+    base = run(d)
+    rng = np.random.default_rng(1)
+
+    def perturb(h):
+        return h * (1 + rng.uniform(-1, 1, h.shape) * 4e-5)
+
+    moved = run(d, h_perturb=perturb)
+    tol = 2e-2 if kind != "bf16" else 5e-3
+    got = codecs.bf16_encode(moved["out64"])
+    ok, stats = tolerance_check(got, base["out64"], tol, base["flip_bound"])
+    assert ok, stats
+    if kind == "fp8_blockwise":
+        _, strict = tolerance_check(got, base["out64"], tol, None)
+        assert strict["n_over_bound"] > 0

@@ -48,8 +48,8 @@ def _silu_sign(g):
 
 
 def _requant_256(h):
-    q, s, hd = ORIG["requant_blockwise"](h * (448.0 / 256.0))
-    return q, s, hd * (256.0 / 448.0)
+    q, s, hd, alt = ORIG["requant_blockwise"](h * (448.0 / 256.0))
+    return q, s, hd * (256.0 / 448.0), alt
 
 
 def _mx_shift(h):
@@ -62,7 +62,7 @@ def _mx_shift(h):
     p = codecs.fp32(h32.astype(np.float64) * np.ldexp(1.0, -s)[:, :, None])
     q = codecs.e4m3_encode(p.astype(np.float64))
     hd = codecs.e4m3_decode(q) * np.ldexp(1.0, s)[:, :, None]
-    return q.reshape(rows, I), (s + 127).astype(np.uint8), hd.reshape(rows, I)
+    return q.reshape(rows, I), (s + 127).astype(np.uint8), hd.reshape(rows, I), np.zeros((rows, I))
 
 
 def _dequant_w_T(kind, w, w_scale, e):
