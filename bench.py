@@ -1,0 +1,269 @@
+"""Benchmark of the fused MoE expert-FFN forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--tokens 8,64,256] [--no-cpu-baseline]
+
+A step is one whole forward on one batch: the planner (moe_align) and the
+fused expert FFN (gather, gate/up GEMM, SwiGLU + requantization, down GEMM,
+top-k weighted combine), inputs resident in HBM, on synthetic seeded data of
+the workload's shapes (random-init weights; no trained checkpoint exists
+here).  Every token count of the workload is timed; the JSON line's ``value``
+is the largest one's throughput and ``sweep`` lists all of them.
+
+Throughput: algorithmic FLOPs 6 * R * K * I per step (R = routes to local
+experts; padding rows do not count) over the step time.  Roofline: the
+dominant kernel (the fused kernel in fused mode, the gate/up kernel in split
+mode) is timed with HIP events recorded around it on its own stream, and its
+algorithmic HBM bytes (weights and scales of the experts it reads once, the
+token rows, its outputs) are divided by that time.
+
+The CPU baseline runs the fp64 oracle on a bounded sample of the same
+workload (a few tokens of the largest token count) on the host cores.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_blockwise": 5000.0, "mxfp8": 5000.0}
+DTYPE_NAME = {"bf16": "bf16", "fp8_blockwise": "e4m3/fp32-blockwise", "mxfp8": "e4m3/e8m0-mx"}
+METRIC = ("fused MoE fwd µs and TFLOP/s (% FP8 MFMA / % HBM roofline) vs tokens T")
+KERNEL_SOURCES = ["mixture_experts_ffn_moe_amd/csrc/moe_kernels.hip",
+                  "mixture_experts_ffn_moe_amd/csrc/device.h"]
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its stream)."""
+
+    def __init__(self, n):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def byte_model(kind, K, I, E_act, T, R, split):
+    """Algorithmic HBM bytes: (step total, dominant kernel)."""
+    N = 2 * I
+    es = 2 if kind == "bf16" else 1
+    if kind == "bf16":
+        w1e, w2e = N * K * 2, K * I * 2
+    elif kind == "fp8_blockwise":
+        w1e = N * K + (N // 128) * (K // 128) * 4
+        w2e = K * I + (K // 128) * (I // 128) * 4
+    else:
+        w1e = N * K + N * (K // 32)
+        w2e = K * I + K * (I // 32)
+    xs = 0 if kind == "bf16" else (T * (K // 128) * 4 if kind == "fp8_blockwise" else T * (K // 32))
+    x_b = T * K * es + xs
+    out_b = T * K * 2
+    route_b = R * 8
+    step = E_act * (w1e + w2e) + x_b + out_b + route_b
+    if split:
+        hs = 0 if kind == "bf16" else (R * (I // 128) * 4 if kind == "fp8_blockwise" else R * (I // 32))
+        dom = E_act * w1e + x_b + R * I * es + hs          # gate/up kernel: w1, x, H write
+    else:
+        dom = E_act * (w1e + w2e) + x_b + 2 * T * K * 4    # fused: weights, x, fp32 acc r/w
+    return step, dom
+
+
+def load_traffic(workload, T, kernel_name):
+    """HBM traffic per launch from a committed rocprofv3 counter summary, or
+    None when absent or taken on another revision of the kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except Exception:
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    e = d.get("entries", {}).get(f"{workload}/T={T}/{kernel_name}")
+    return None if e is None else e.get("bytes_per_launch")
+
+
+def cpu_baseline(case, n_tokens, K, I):
+    import numpy as np
+
+    import datagen
+    from oracle.moe import moe_ref
+    tokens = np.arange(min(n_tokens, case.T))
+    ids = case.topk_ids.cpu().numpy()[tokens]
+    experts = sorted(set(int(e) for e in np.unique(ids) if 0 <= e < case.E))
+    d = datagen.to_numpy(case, experts=experts)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    moe_ref(d["kind"], d["x"], d["x_scale"], d["w1"], d["w1_scale"], d["w2"], d["w2_scale"],
+            d["topk_ids"], d["topk_weights"], tokens=tokens)
+    dt = time.perf_counter() - t0
+    R = int(((ids >= 0) & (ids < case.E)).sum())
+    flops = 6.0 * R * K * I
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{len(tokens)} tokens ({R} routes, {len(experts)} experts dequantized) of "
+                       f"the T={case.T} batch; fp64 numpy oracle, {dt:.2f} s"),
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fp8-k4096-i2048-e256-top6")
+    ap.add_argument("--tokens", default=None, help="comma list; default: the workload's")
+    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--split", type=int, default=-1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=4)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the fused MoE forward here runs on one GPU's local "
+              "experts with no collectives; --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import datagen
+    import mixture_experts_ffn_moe_amd as moe
+
+    spec = datagen.WORKLOADS[args.workload]
+    kind, K, I, E, k = spec["kind"], spec["K"], spec["I"], spec["E"], spec["top_k"]
+    N = 2 * I
+    tokens = ([int(t) for t in args.tokens.split(",")] if args.tokens else list(spec["tokens"]))
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    moe.lib()
+    print(f"[bench] generating {args.workload} weights on the GPU", file=sys.stderr, flush=True)
+    weights = datagen.make_weights(kind, K, I, E, device=dev, tag=args.workload,
+                                   w_std=spec.get("w_std"))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sweep = []
+    last_case = None
+    for T in tokens:
+        case = datagen.make_workload_case(args.workload, T, device=dev, weights=weights)
+        ids = case.topk_ids
+        valid = (ids >= 0) & (ids < E)
+        R = int(valid.sum().item())
+        E_act = int(torch.unique(ids[valid]).numel())
+        bm = args.block_m or moe.moe_select_block_m(T, k, E)
+        split = args.split if args.split >= 0 else moe.moe_select_split(kind, T, K, N, E, k, bm)
+        rows, blocks = moe.moe_align_capacity(T, k, E, bm)
+        align_out = (torch.empty(rows, dtype=torch.int32, device=dev),
+                     torch.empty(blocks, dtype=torch.int32, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev))
+        ws = torch.empty(max(moe.moe_workspace_size(kind, T, K, N, E, k, bm, split), 256),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
+
+        def step():
+            moe.run_case(case, block_m=bm, split=split, workspace=ws, out=out, align_out=align_out)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        hev = HipEvents(2 * args.steps)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(args.steps):
+            moe.moe_set_timing_events(hev.ev[2 * i], hev.ev[2 * i + 1], 1)
+            step()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        moe.moe_set_timing_events(None, None)
+        ms = t0.elapsed_time(t1) / args.steps
+        kms = sum(hev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)) / args.steps
+        hev.close()
+        flops = 6.0 * R * K * I
+        step_bytes, dom_bytes = byte_model(kind, K, I, E_act, T, R, split)
+        kname = "k_up" if split else "k_fused"
+        sweep.append({
+            "T": T, "routes": R, "active_experts": E_act, "block_m": bm,
+            "mode": "split" if split else "fused",
+            "us_per_step": ms * 1e3, "tflops": flops / (ms * 1e-3) / 1e12,
+            "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[kind],
+            "step_gbs": step_bytes / (ms * 1e-3) / 1e9,
+            "pct_hbm_peak": 100.0 * step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "dominant_kernel": kname, "dominant_us": kms * 1e3,
+            "dominant_bytes": dom_bytes, "dominant_gbs": dom_bytes / (kms * 1e-3) / 1e9,
+        })
+        print(f"[bench] T={T} bm={bm} {'split' if split else 'fused'}: {ms*1e3:.1f} us/step, "
+              f"{kname} {kms*1e3:.1f} us = {dom_bytes/(kms*1e-3)/1e9:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        last_case = case
+        del ws
+
+    head = sweep[-1]
+    roof = {"bound": "hbm", "achieved": head["dominant_gbs"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": head["dominant_gbs"] / HBM_PEAK_GBS,
+            "traffic": load_traffic(args.workload, head["T"], head["dominant_kernel"]),
+            "kernel": head["dominant_kernel"], "bytes_per_launch": head["dominant_bytes"],
+            "us_per_launch": head["dominant_us"]}
+    result = {
+        "metric": METRIC, "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["us_per_step"] / 1e3,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE_NAME[kind], "data": "synthetic (seeded random weights, tokens, routing)",
+        "config": {"workload": args.workload, "tokens": head["T"], "hidden": K,
+                   "intermediate": I, "experts": E, "top_k": k, "block_m": head["block_m"],
+                   "mode": head["mode"], "parallelism": "single GPU, all experts local"},
+        "roofline": roof,
+        "sweep": sweep,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(last_case, args.cpu_tokens, K, I)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

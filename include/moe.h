@@ -1,0 +1,245 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused MoE expert-FFN forward.
+ *
+ * The library computes, on one GPU's local experts, the expert FFN of a
+ * mixture-of-experts layer: a planner that groups the top-k routes by expert
+ * (moe_align), then for every routed token row the gate/up GEMM, SwiGLU, an
+ * on-chip requantization of the intermediate, the down GEMM and the top-k
+ * weighted combine (fused_moe_*).
+ *
+ * Sources (web pages on fused MoE kernels):
+ *   [hpc-ops RFC]  "[RFC] Fused W8A8 MoE megakernel on H20", sections
+ *                  "Background" (the five stages) and "Design" (planner +
+ *                  compute kernel).
+ *   [prime-flash]  "Prime Flash MoE: Fused MoE Kernels for Blackwell",
+ *                  sections "API", "Shapes", "Scale layout (mxfp8)",
+ *                  "Constraints" and the introduction (split / fused modes).
+ *   [DeepGEMM #88] "[SM90] Ring-buffered FP8 MegaMoE with a lag-ordered L1/L2
+ *                  schedule", section "Before you merge" (per-128 FP8
+ *                  requantization expression of the intermediate).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - Pointers are DEVICE pointers unless an argument says "host".  All tensors
+ *   are dense and row-major (C order), and must be 16-byte aligned.
+ * - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *   Every call only enqueues work on `stream`: it never synchronizes with the
+ *   device and never copies between host and device.
+ * - The caller allocates and owns every buffer, including the workspace.  The
+ *   library allocates no device memory and keeps no state between calls.
+ * - Return value: MOE_OK (0) or a negative moe_status.  All argument checks
+ *   run on the host BEFORE anything is enqueued, so on an error nothing has
+ *   been launched.  moe_last_error() returns a message for the last failing
+ *   call of the calling thread (host string owned by the library).
+ * - Numbers: e4m3 means OCP FP8 E4M3FN (bias 7, max 448, no infinities);
+ *   e8m0 means the OCP MX power-of-two scale 2^(c-127); bf16 is bfloat16.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,       /* negative / zero / inconsistent sizes */
+  MOE_ERR_UNSUPPORTED = -3, /* a size or option this build does not cover */
+  MOE_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required */
+  MOE_ERR_HIP = -6          /* a HIP launch failed; message has the text */
+} moe_status;
+
+typedef enum {
+  MOE_BF16 = 0,          /* bf16 x, w1, w2; fp32 accumulate */
+  MOE_FP8_BLOCKWISE = 1, /* e4m3 with fp32 scales per 1x128 (x) and 128x128 (w) */
+  MOE_MXFP8 = 2          /* e4m3 with e8m0 scales per 32 along the contraction */
+} moe_dtype;
+
+/* Message describing the last error of the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * Capacities of the planner outputs for any routing of T tokens with top_k
+ * routes each over E experts:
+ *   *sorted_cap = T*top_k + min(E, T*top_k) * (block_m - 1)
+ *   *blocks_cap = ceil(*sorted_cap / block_m)
+ * (each non-empty expert pads fewer than block_m rows).  Host out-params.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (T < 0, top_k < 1, E < 1,
+ * T*top_k >= 2^31), MOE_ERR_UNSUPPORTED (block_m not 16, 32, 64 or 128).
+ */
+int moe_align_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m,
+                       int64_t* sorted_cap, int64_t* blocks_cap);
+
+/*
+ * Planner ([hpc-ops RFC] "Design": expert histogram, prefix sums and the
+ * row-to-token mapping; [prime-flash] "API" moe_align and "Shapes").
+ *
+ *   topk_ids                 (T, top_k) int32, expert id of each route.
+ *   sorted_token_ids  [out]  (sorted_cap) int32: the flat pair ids
+ *                            t*top_k + j grouped by expert (experts in
+ *                            ascending id, ids ascending inside an expert),
+ *                            each expert padded to a multiple of block_m
+ *                            with -1, and -1 from num_tokens_post_padded to
+ *                            the end.
+ *   expert_ids        [out]  (blocks_cap) int32: expert of each block_m
+ *                            block; -1 for blocks past the last used one.
+ *   num_tokens_post_padded [out] int32[1]: padded row count (multiple of
+ *                            block_m).
+ * Routes whose expert id is outside [0, E) are not placed (they contribute
+ * nothing downstream).  Experts with no route get no block.  The output is
+ * unique (bit-exact, deterministic).  E must be <= 1024.
+ * Errors: as moe_align_capacity, plus MOE_ERR_ALIGN, MOE_ERR_UNSUPPORTED
+ * (E > 1024), MOE_ERR_HIP.  T == 0 writes the all -1 outputs and a 0 count.
+ */
+int moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
+              int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
+              int32_t* num_tokens_post_padded, void* stream);
+
+/*
+ * Mode choice by size ([prime-flash] introduction: split=False keeps the
+ * intermediate on chip and accumulates a split-K down projection into the
+ * output; split=True writes the H-wide activation once and runs the down
+ * projection with no split-K, trading one HBM round trip for a reduction
+ * cost that grows with token count; [hpc-ops RFC] "Results so far": the
+ * fused kernel helps small-token workloads).
+ *   *split (host out) = 1 for split mode, 0 for the fused mode.
+ * Errors: MOE_ERR_NULL.
+ */
+int moe_select_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E,
+                     int32_t top_k, int32_t block_m, int32_t* split);
+
+/*
+ * Suggested block_m for a call (small blocks for decode-sized batches, so
+ * that padding does not dominate; larger blocks once experts hold many
+ * rows).  *block_m is a host out-param.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE.
+ */
+int moe_select_block_m(int64_t T, int32_t top_k, int32_t E, int32_t* block_m);
+
+/*
+ * Workspace bytes a fused_moe_* call with these sizes needs (host out-param).
+ * split = -1 means "as moe_select_split picks".  Errors: as the fused calls'
+ * size checks.
+ */
+int moe_workspace_size(int32_t dtype, int64_t T, int64_t K, int64_t N,
+                       int32_t E, int32_t top_k, int32_t block_m,
+                       int32_t split, size_t* bytes);
+
+/*
+ * Byte offsets, inside the workspace of a split-mode call, of the
+ * requantized intermediate: rows follow sorted_token_ids positions
+ * (sorted_cap rows), I = N/2 columns.
+ *   *h_offset      values: bf16 (rows, I) / e4m3 (rows, I)
+ *   *hs_offset     scales: fp32 (rows, I/128) blockwise, e8m0 (rows, I/32) MX,
+ *                  unused (equal to *h_offset) for bf16
+ * Rows whose sorted id is -1 hold unspecified bytes.  For inspection only.
+ * Errors: as moe_workspace_size.
+ */
+int moe_workspace_layout(int32_t dtype, int64_t T, int64_t K, int64_t N,
+                         int32_t E, int32_t top_k, int32_t block_m,
+                         size_t* h_offset, size_t* hs_offset);
+
+/*
+ * Fused expert FFN forward ([hpc-ops RFC] "Background" stages 1-5:
+ * gather, gate/up grouped GEMM, SwiGLU + requantization, down grouped GEMM,
+ * top-k weighted reduction; [prime-flash] "API" / "Shapes").
+ *
+ * Common arguments (all three dtypes):
+ *   sorted_token_ids, expert_ids, num_tokens_post_padded
+ *                    moe_align outputs for the same topk_ids, E and block_m
+ *                    (read on the device; no host synchronization).
+ *   topk_weights     (T, top_k) fp32 routing weights.
+ *   out       [out]  (T, K) bf16.  EVERY element is written: a token whose
+ *                    routes are all outside [0, E) gets zeros.  out is
+ *                    sum_j topk_weights[t, j] * y_j summed in fp32 with one
+ *                    rounding to bf16.
+ *   T, K, N, E, top_k, block_m
+ *                    tokens, hidden size, fused gate+up width (N = 2I; rows
+ *                    [0, I) of w1 are the gate, [I, N) the up projection),
+ *                    experts, routes per token, planner block.
+ *                    K % 128 == 0 and I % 128 == 0 are required.
+ *   split            -1: choose by size (moe_select_split); 0: fused mode
+ *                    (the intermediate stays on chip, the down GEMM is
+ *                    split-K over 128-wide slices of I accumulated in fp32);
+ *                    1: split mode (the requantized intermediate is written
+ *                    to the workspace once, the down GEMM runs with no
+ *                    split-K, and the combine is deterministic: the same
+ *                    inputs give bitwise the same output).
+ *   workspace, workspace_bytes
+ *                    device scratch of at least moe_workspace_size bytes;
+ *                    contents undefined on return; concurrent calls need
+ *                    separate workspaces.
+ *   stream           hipStream_t as void*.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN,
+ * MOE_ERR_WORKSPACE, MOE_ERR_HIP.  T == 0 is a successful no-op.
+ */
+
+/* bf16 path: x (T, K), w1 (E, N, K), w2 (E, K, N/2), all bf16.  The
+ * intermediate is rounded to bf16 before the down GEMM. */
+int fused_moe_bf16(const void* x, const void* w1, const void* w2,
+                   const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                   const int32_t* num_tokens_post_padded,
+                   const float* topk_weights, void* out, int64_t T, int64_t K,
+                   int64_t N, int32_t E, int32_t top_k, int32_t block_m,
+                   int32_t split, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Blockwise FP8 W8A8 path ([hpc-ops RFC] "Background": blockwise FP8 MoE;
+ * [DeepGEMM #88] "Before you merge": the intermediate is requantized per
+ * row and 128 columns with amax floored at 1e-10, sf = amax*(1/448),
+ * sf_inv = 1/sf, q = e4m3(h*sf_inv), saturating).
+ *   x (T, K) e4m3, x_scale (T, K/128) fp32;
+ *   w1 (E, N, K) e4m3, w1_scale (E, N/128, K/128) fp32;
+ *   w2 (E, K, N/2) e4m3, w2_scale (E, K/128, (N/2)/128) fp32. */
+int fused_moe_fp8_blockwise(const void* x, const float* x_scale,
+                            const void* w1, const float* w1_scale,
+                            const void* w2, const float* w2_scale,
+                            const int32_t* sorted_token_ids,
+                            const int32_t* expert_ids,
+                            const int32_t* num_tokens_post_padded,
+                            const float* topk_weights, void* out, int64_t T,
+                            int64_t K, int64_t N, int32_t E, int32_t top_k,
+                            int32_t block_m, int32_t split, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* MXFP8 path ([prime-flash] "Scale layout (mxfp8)": e4m3 values with e8m0
+ * scales per 32 along K, activation scales row-major; the intermediate is
+ * requantized to mxfp8 on chip before the down GEMM, shared exponent
+ * floor(log2 amax) - 8 per 32 columns, elements saturating).  All scales are
+ * row-major here (the page's blocked weight-scale tiles are an addressing
+ * scheme of its hardware and are not used).
+ *   x (T, K) e4m3, x_scale (T, K/32) e8m0;
+ *   w1 (E, N, K) e4m3, w1_scale (E, N, K/32) e8m0;
+ *   w2 (E, K, N/2) e4m3, w2_scale (E, K, (N/2)/32) e8m0. */
+int fused_moe_mxfp8(const void* x, const uint8_t* x_scale, const void* w1,
+                    const uint8_t* w1_scale, const void* w2,
+                    const uint8_t* w2_scale, const int32_t* sorted_token_ids,
+                    const int32_t* expert_ids,
+                    const int32_t* num_tokens_post_padded,
+                    const float* topk_weights, void* out, int64_t T, int64_t K,
+                    int64_t N, int32_t E, int32_t top_k, int32_t block_m,
+                    int32_t split, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * Profiling hook (changes no result): the next fused_moe_* calls made by the
+ * calling thread record the caller's hipEvent_t handles `before` and `after`
+ * (passed as void*) on their stream immediately before and after one kernel:
+ *   which = 1: the main weight-streaming kernel (the fused kernel in fused
+ *              mode, the gate/up kernel in split mode);
+ *   which = 2: the down kernel (split mode only; fused mode records nothing).
+ * which = 0 or NULL events switch the hook off.  The handles stay owned by
+ * the caller and must outlive the calls that record them.
+ * Errors: MOE_ERR_UNSUPPORTED (which outside 0..2).
+ */
+int moe_set_timing_events(void* before, void* after, int32_t which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,236 @@
+"""MI355X (gfx950) fused MoE expert-FFN forward: Python binding.
+
+Thin ctypes layer over the C ABI in ``include/moe.h`` (library
+``libmoe_mi355x.so`` next to this file, built by
+``python -m mixture_experts_ffn_moe_amd.build``).  The functions here only
+marshal arguments: torch tensors provide device memory and the current HIP
+stream; every step of the forward runs in the library's kernels.  There is no
+fallback: if the library is missing, every call raises.
+
+Entry points (same names as the C ABI):
+  moe_align(topk_ids, num_experts, block_m)
+      -> (sorted_token_ids, expert_ids, num_tokens_post_padded)
+  fused_moe_bf16(x, w1, w2, sorted_token_ids, expert_ids,
+                 num_tokens_post_padded, topk_weights, top_k, block_m, ...)
+  fused_moe_fp8_blockwise(x, x_scale, w1, w1_scale, w2, w2_scale, ...)
+  fused_moe_mxfp8(x, x_scale, w1, w1_scale, w2, w2_scale, ...)
+plus the host helpers moe_align_capacity, moe_workspace_size,
+moe_workspace_layout, moe_select_split and moe_select_block_m.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MoeError", "lib", "LIB_PATH", "MOE_BF16", "MOE_FP8_BLOCKWISE", "MOE_MXFP8",
+    "moe_align_capacity", "moe_align", "moe_select_split", "moe_select_block_m",
+    "moe_workspace_size", "moe_workspace_layout", "fused_moe_bf16",
+    "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
+
+MOE_BF16, MOE_FP8_BLOCKWISE, MOE_MXFP8 = 0, 1, 2
+_DTYPE_CODE = {"bf16": MOE_BF16, "fp8_blockwise": MOE_FP8_BLOCKWISE, "mxfp8": MOE_MXFP8}
+
+EXPORTED_SYMBOLS = (
+    "moe_last_error", "moe_align_capacity", "moe_align", "moe_select_split",
+    "moe_select_block_m", "moe_workspace_size", "moe_workspace_layout",
+    "fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "moe_set_timing_events",
+)
+
+_STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
+           -4: "MOE_ERR_ALIGN", -5: "MOE_ERR_WORKSPACE", -6: "MOE_ERR_HIP"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+
+def lib():
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m mixture_experts_ffn_moe_amd.build` (no fallback path exists)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.moe_last_error.restype = ctypes.c_char_p
+    L.moe_last_error.argtypes = []
+    L.moe_align_capacity.argtypes = [_I64, _I32, _I32, _I32, ctypes.POINTER(_I64),
+                                     ctypes.POINTER(_I64)]
+    L.moe_align.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]
+    L.moe_select_split.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32,
+                                   ctypes.POINTER(_I32)]
+    L.moe_select_block_m.argtypes = [_I64, _I32, _I32, ctypes.POINTER(_I32)]
+    L.moe_workspace_size.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
+                                     ctypes.POINTER(_SZ)]
+    L.moe_workspace_layout.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32,
+                                       ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
+    tail = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]
+    L.fused_moe_bf16.argtypes = [_P, _P, _P] + tail
+    L.fused_moe_fp8_blockwise.argtypes = [_P, _P, _P, _P, _P, _P] + tail
+    L.fused_moe_mxfp8.argtypes = [_P, _P, _P, _P, _P, _P] + tail
+    L.moe_set_timing_events.argtypes = [_P, _P, _I32]
+    for name in EXPORTED_SYMBOLS:
+        if name != "moe_last_error":
+            getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != 0:
+        raise MoeError(status, lib().moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def moe_align_capacity(T, top_k, num_experts, block_m):
+    rows, blocks = _I64(), _I64()
+    _check(lib().moe_align_capacity(T, top_k, num_experts, block_m, ctypes.byref(rows),
+                                    ctypes.byref(blocks)))
+    return rows.value, blocks.value
+
+
+def moe_set_timing_events(before, after, which=1):
+    """Record the hipEvent_t handles ``before`` / ``after`` (ctypes.c_void_p
+    or int) around one kernel of the next fused_moe_* calls of this thread
+    (which=1: fused or gate/up kernel, 2: down kernel); ``None`` switches the
+    hook off."""
+    if before is None or after is None:
+        _check(lib().moe_set_timing_events(None, None, 0))
+        return
+    _check(lib().moe_set_timing_events(before, after, which))
+
+
+def moe_align(topk_ids, num_experts, block_m, stream=None, out=None):
+    """Planner: returns (sorted_token_ids, expert_ids, num_tokens_post_padded)
+    as int32 device tensors (the last one of shape (1,)).  ``out`` may pass
+    preallocated tensors of the capacities moe_align_capacity gives."""
+    T, k = topk_ids.shape
+    rows, blocks = moe_align_capacity(T, k, num_experts, block_m)
+    dev = topk_ids.device
+    if out is not None:
+        sorted_ids, expert_ids, ntp = out
+    else:
+        sorted_ids = torch.empty(max(rows, 1), dtype=torch.int32, device=dev)[:rows]
+        expert_ids = torch.empty(max(blocks, 1), dtype=torch.int32, device=dev)[:blocks]
+        ntp = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().moe_align(_ptr(topk_ids.contiguous()), T, k, num_experts, block_m,
+                           _ptr(sorted_ids), _ptr(expert_ids), _ptr(ntp), _stream(stream)))
+    return sorted_ids, expert_ids, ntp
+
+
+def moe_select_split(dtype, T, K, N, num_experts, top_k, block_m):
+    out = _I32()
+    _check(lib().moe_select_split(_DTYPE_CODE.get(dtype, dtype), T, K, N, num_experts, top_k,
+                                  block_m, ctypes.byref(out)))
+    return out.value
+
+
+def moe_select_block_m(T, top_k, num_experts):
+    out = _I32()
+    _check(lib().moe_select_block_m(T, top_k, num_experts, ctypes.byref(out)))
+    return out.value
+
+
+def moe_workspace_size(dtype, T, K, N, num_experts, top_k, block_m, split=-1):
+    out = _SZ()
+    _check(lib().moe_workspace_size(_DTYPE_CODE.get(dtype, dtype), T, K, N, num_experts, top_k,
+                                    block_m, split, ctypes.byref(out)))
+    return out.value
+
+
+def moe_workspace_layout(dtype, T, K, N, num_experts, top_k, block_m):
+    h, hs = _SZ(), _SZ()
+    _check(lib().moe_workspace_layout(_DTYPE_CODE.get(dtype, dtype), T, K, N, num_experts,
+                                      top_k, block_m, ctypes.byref(h), ctypes.byref(hs)))
+    return h.value, hs.value
+
+
+def _run(fn, dtype, operands, w1, sorted_token_ids, expert_ids, num_tokens_post_padded,
+         topk_weights, top_k, block_m, split, out, workspace, stream, T, K):
+    E, N, _ = w1.shape
+    dev = w1.device
+    if out is None:
+        out = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
+    need = moe_workspace_size(dtype, T, K, N, E, top_k, block_m, split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(fn(*[_ptr(t) for t in operands], _ptr(sorted_token_ids), _ptr(expert_ids),
+              _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(out), T, K, N, E, top_k,
+              block_m, split, _ptr(workspace), workspace.numel() * workspace.element_size(),
+              _stream(stream)))
+    return out
+
+
+def fused_moe_bf16(x, w1, w2, sorted_token_ids, expert_ids, num_tokens_post_padded,
+                   topk_weights, top_k, block_m, split=-1, out=None, workspace=None,
+                   stream=None):
+    T, K = x.shape
+    return _run(lib().fused_moe_bf16, MOE_BF16, [x, w1, w2], w1, sorted_token_ids, expert_ids,
+                num_tokens_post_padded, topk_weights, top_k, block_m, split, out, workspace,
+                stream, T, K)
+
+
+def fused_moe_fp8_blockwise(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids,
+                            expert_ids, num_tokens_post_padded, topk_weights, top_k, block_m,
+                            split=-1, out=None, workspace=None, stream=None):
+    T, K = x.shape
+    return _run(lib().fused_moe_fp8_blockwise, MOE_FP8_BLOCKWISE,
+                [x, x_scale, w1, w1_scale, w2, w2_scale], w1, sorted_token_ids, expert_ids,
+                num_tokens_post_padded, topk_weights, top_k, block_m, split, out, workspace,
+                stream, T, K)
+
+
+def fused_moe_mxfp8(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
+                    num_tokens_post_padded, topk_weights, top_k, block_m, split=-1, out=None,
+                    workspace=None, stream=None):
+    T, K = x.shape
+    return _run(lib().fused_moe_mxfp8, MOE_MXFP8, [x, x_scale, w1, w1_scale, w2, w2_scale], w1,
+                sorted_token_ids, expert_ids, num_tokens_post_padded, topk_weights, top_k,
+                block_m, split, out, workspace, stream, T, K)
+
+
+def run_case(case, block_m=None, split=-1, stream=None, workspace=None, out=None,
+             align_out=None):
+    """Planner + forward for a ``datagen.Case``-like object (attributes kind,
+    x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, E, top_k).
+    Returns (out, (sorted_token_ids, expert_ids, num_tokens_post_padded))."""
+    T = case.x.shape[0]
+    if block_m is None:
+        block_m = moe_select_block_m(T, case.top_k, case.E)
+    align = moe_align(case.topk_ids, case.E, block_m, stream=stream, out=align_out)
+    args = dict(top_k=case.top_k, block_m=block_m, split=split, out=out, workspace=workspace,
+                stream=stream)
+    if case.kind == "bf16":
+        o = fused_moe_bf16(case.x, case.w1, case.w2, *align, case.topk_weights, **args)
+    elif case.kind == "fp8_blockwise":
+        o = fused_moe_fp8_blockwise(case.x, case.x_scale, case.w1, case.w1_scale, case.w2,
+                                    case.w2_scale, *align, case.topk_weights, **args)
+    else:
+        o = fused_moe_mxfp8(case.x, case.x_scale, case.w1, case.w1_scale, case.w2,
+                            case.w2_scale, *align, case.topk_weights, **args)
+    return o, align

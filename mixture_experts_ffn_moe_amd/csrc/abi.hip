@@ -1,0 +1,294 @@
+// abi.hip -- host side of the C ABI declared in include/moe.h: argument
+// validation (before anything is enqueued), capacities, workspace layout,
+// mode / block heuristics, and the launches.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local TimingHook g_hook;
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+
+int check_routes(int64_t T, int32_t top_k, int32_t E) {
+  if (T < 0) return fail(MOE_ERR_SHAPE, "T must be >= 0 (got %lld)", (long long)T);
+  if (top_k < 1) return fail(MOE_ERR_SHAPE, "top_k must be >= 1 (got %d)", top_k);
+  if (E < 1) return fail(MOE_ERR_SHAPE, "E must be >= 1 (got %d)", E);
+  if (T * (int64_t)top_k >= (int64_t(1) << 31))
+    return fail(MOE_ERR_SHAPE, "T*top_k must be < 2^31");
+  return MOE_OK;
+}
+
+void capacity(int64_t T, int32_t top_k, int32_t E, int32_t bm, int64_t* rows, int64_t* blocks) {
+  const int64_t R = T * top_k;
+  const int64_t r = R + (R < E ? R : (int64_t)E) * (bm - 1);
+  *rows = r;
+  *blocks = (r + bm - 1) / bm;
+}
+
+int check_ffn(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+              int32_t block_m) {
+  int rc = check_routes(T, top_k, E);
+  if (rc) return rc;
+  if (dtype < MOE_BF16 || dtype > MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (K <= 0 || N <= 0) return fail(MOE_ERR_SHAPE, "K and N must be > 0");
+  if (N % 2) return fail(MOE_ERR_SHAPE, "N (fused gate+up width) must be even");
+  if (K % 128) return fail(MOE_ERR_UNSUPPORTED, "K must be a multiple of 128 (got %lld)", (long long)K);
+  if ((N / 2) % 128)
+    return fail(MOE_ERR_UNSUPPORTED, "I = N/2 must be a multiple of 128 (got %lld)", (long long)(N / 2));
+  if (!valid_block_m(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m must be 16, 32, 64 or 128 (got %d)", block_m);
+  // 32-bit offsets inside one expert's weights and element indices of out
+  if (N * K >= (int64_t(1) << 31) || T * K >= (int64_t(1) << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "per-expert weight or output element count must be < 2^31");
+  int64_t rows, blocks;
+  capacity(T, top_k, E, block_m, &rows, &blocks);
+  if (blocks * block_m * (N / 2) * 2 >= (int64_t(1) << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "intermediate workspace must stay below 4 GiB");
+  return MOE_OK;
+}
+
+int pick_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+               int32_t block_m) {
+  (void)dtype; (void)K; (void)N; (void)E; (void)block_m;
+  // The fused mode's split-K accumulation costs R*K*(I/128) fp32 atomic adds;
+  // it stays cheap against the weight stream only for decode-sized calls.
+  return (T * top_k <= 512) ? 0 : 1;
+}
+
+struct Layout {
+  size_t flags, hq, hs, yr, acc, total;
+};
+
+Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+              int32_t block_m, int split) {
+  Layout L{};
+  const int64_t I = N / 2;
+  const size_t R = (size_t)T * top_k;
+  const size_t es = dtype == MOE_BF16 ? 2 : 1;
+  int64_t rows, blocks;
+  capacity(T, top_k, E, block_m, &rows, &blocks);
+  rows = blocks * block_m;  // whole blocks, so every block's rows exist
+  size_t off = 0;
+  if (split) {
+    L.flags = off;
+    off = round_up(off + R * 4, 256);
+    L.hq = off;
+    off = round_up(off + (size_t)rows * I * es, 256);
+    L.hs = off;
+    if (dtype == MOE_FP8_BLOCKWISE) off = round_up(off + (size_t)rows * (I / 128) * 4, 256);
+    if (dtype == MOE_MXFP8) off = round_up(off + (size_t)rows * (I / 32), 256);
+    if (dtype == MOE_BF16) L.hs = L.hq;
+    L.yr = off;
+    off = round_up(off + R * (size_t)K * 4, 256);
+  } else {
+    L.acc = off;
+    off = round_up(off + (size_t)T * K * 4, 256);
+  }
+  L.total = off;
+  return L;
+}
+
+int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const void* w1s,
+            const void* w2, const void* w2s, const int32_t* sorted, const int32_t* expert_ids,
+            const int32_t* ntp, const float* topk_w, void* out, int64_t T, int64_t K, int64_t N,
+            int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* ws, size_t ws_bytes,
+            void* stream) {
+  int rc = check_ffn(dtype, T, K, N, E, top_k, block_m);
+  if (rc) return rc;
+  if (split < -1 || split > 1) return fail(MOE_ERR_UNSUPPORTED, "split must be -1, 0 or 1");
+  if (T == 0) return ok();
+  if (!x || !w1 || !w2 || !sorted || !expert_ids || !ntp || !topk_w || !out)
+    return fail(MOE_ERR_NULL, "a required pointer is NULL");
+  if (dtype != MOE_BF16 && (!xs || !w1s || !w2s))
+    return fail(MOE_ERR_NULL, "scale pointers are required for FP8 paths");
+  const void* p16[] = {x, w1, w2, out, sorted, expert_ids, topk_w, ws};
+  for (const void* p : p16)
+    if (p && !aligned(p, 16)) return fail(MOE_ERR_ALIGN, "tensors must be 16-byte aligned");
+  if (dtype == MOE_FP8_BLOCKWISE && (!aligned(xs, 4) || !aligned(w1s, 4) || !aligned(w2s, 4)))
+    return fail(MOE_ERR_ALIGN, "fp32 scales must be 4-byte aligned");
+  if (!aligned(ntp, 4)) return fail(MOE_ERR_ALIGN, "num_tokens_post_padded must be 4-byte aligned");
+  const int sp = split < 0 ? pick_split(dtype, T, K, N, E, top_k, block_m) : split;
+  const Layout L = layout(dtype, T, K, N, E, top_k, block_m, sp);
+  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (ws_bytes < L.total)
+    return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  int64_t rows, blocks;
+  capacity(T, top_k, E, block_m, &rows, &blocks);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  MoeArgs a{};
+  a.x = static_cast<const uint8_t*>(x);
+  a.xs = xs;
+  a.w1 = static_cast<const uint8_t*>(w1);
+  a.w1s = w1s;
+  a.w2 = static_cast<const uint8_t*>(w2);
+  a.w2s = w2s;
+  a.sorted = sorted;
+  a.expert_ids = expert_ids;
+  a.ntp = ntp;
+  a.topk_w = topk_w;
+  a.out = static_cast<uint16_t*>(out);
+  if (sp) {
+    a.flags = reinterpret_cast<int32_t*>(w + L.flags);
+    a.hq = w + L.hq;
+    a.hs = w + L.hs;
+    a.yr = reinterpret_cast<float*>(w + L.yr);
+  } else {
+    a.acc = reinterpret_cast<float*>(w + L.acc);
+  }
+  a.T = (int)T;
+  a.K = (int)K;
+  a.I = (int)(N / 2);
+  a.E = E;
+  a.top_k = top_k;
+  a.blocks_cap = (int)blocks;
+  const int kind = dtype;  // MOE_BF16 / MOE_FP8_BLOCKWISE / MOE_MXFP8 match the kernel kinds
+  hipError_t e = launch_moe(kind, block_m, sp, a, static_cast<hipStream_t>(stream), g_hook);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+int moe_align_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m, int64_t* sorted_cap,
+                       int64_t* blocks_cap) {
+  if (!sorted_cap || !blocks_cap) return fail(MOE_ERR_NULL, "output pointers are NULL");
+  int rc = check_routes(T, top_k, E);
+  if (rc) return rc;
+  if (!valid_block_m(block_m))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m must be 16, 32, 64 or 128 (got %d)", block_m);
+  capacity(T, top_k, E, block_m, sorted_cap, blocks_cap);
+  return ok();
+}
+
+int moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int32_t block_m,
+              int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
+              void* stream) {
+  int64_t rows, blocks;
+  int rc = moe_align_capacity(T, top_k, E, block_m, &rows, &blocks);
+  if (rc) return rc;
+  if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "moe_align supports E <= 1024 (got %d)", E);
+  if (!num_tokens_post_padded || (rows > 0 && (!sorted_token_ids || !expert_ids)) ||
+      (T > 0 && !topk_ids))
+    return fail(MOE_ERR_NULL, "a required pointer is NULL");
+  const void* ps[] = {topk_ids, sorted_token_ids, expert_ids};
+  for (const void* p : ps)
+    if (p && !aligned(p, 16)) return fail(MOE_ERR_ALIGN, "tensors must be 16-byte aligned");
+  if (!aligned(num_tokens_post_padded, 4))
+    return fail(MOE_ERR_ALIGN, "num_tokens_post_padded must be 4-byte aligned");
+  hipError_t e = launch_align(topk_ids, (int)(T * top_k), E, block_m, sorted_token_ids, expert_ids,
+                              num_tokens_post_padded, (int)rows, (int)blocks,
+                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int moe_set_timing_events(void* before, void* after, int32_t which) {
+  if (which < 0 || which > 2) return fail(MOE_ERR_UNSUPPORTED, "which must be 0, 1 or 2");
+  g_hook.before = static_cast<hipEvent_t>(before);
+  g_hook.after = static_cast<hipEvent_t>(after);
+  g_hook.which = which;
+  return ok();
+}
+
+int moe_select_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+                     int32_t block_m, int32_t* split) {
+  if (!split) return fail(MOE_ERR_NULL, "split is NULL");
+  *split = pick_split(dtype, T, K, N, E, top_k, block_m);
+  return ok();
+}
+
+int moe_select_block_m(int64_t T, int32_t top_k, int32_t E, int32_t* block_m) {
+  if (!block_m) return fail(MOE_ERR_NULL, "block_m is NULL");
+  int rc = check_routes(T, top_k, E);
+  if (rc) return rc;
+  // mean rows per non-empty expert, if routes spread evenly
+  const int64_t R = T * top_k;
+  const int64_t act = R < E ? (R > 0 ? R : 1) : E;
+  const double per = (double)R / (double)act;
+  *block_m = per <= 16 ? 16 : per <= 48 ? 32 : per <= 160 ? 64 : 128;
+  return ok();
+}
+
+int moe_workspace_size(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+                       int32_t block_m, int32_t split, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+  int rc = check_ffn(dtype, T, K, N, E, top_k, block_m);
+  if (rc) return rc;
+  if (split < -1 || split > 1) return fail(MOE_ERR_UNSUPPORTED, "split must be -1, 0 or 1");
+  const int sp = split < 0 ? pick_split(dtype, T, K, N, E, top_k, block_m) : split;
+  *bytes = layout(dtype, T, K, N, E, top_k, block_m, sp).total;
+  return ok();
+}
+
+int moe_workspace_layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+                         int32_t block_m, size_t* h_offset, size_t* hs_offset) {
+  if (!h_offset || !hs_offset) return fail(MOE_ERR_NULL, "output pointers are NULL");
+  int rc = check_ffn(dtype, T, K, N, E, top_k, block_m);
+  if (rc) return rc;
+  const Layout L = layout(dtype, T, K, N, E, top_k, block_m, 1);
+  *h_offset = L.hq;
+  *hs_offset = L.hs;
+  return ok();
+}
+
+int fused_moe_bf16(const void* x, const void* w1, const void* w2, const int32_t* sorted_token_ids,
+                   const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                   const float* topk_weights, void* out, int64_t T, int64_t K, int64_t N, int32_t E,
+                   int32_t top_k, int32_t block_m, int32_t split, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return run_ffn(MOE_BF16, x, nullptr, w1, nullptr, w2, nullptr, sorted_token_ids, expert_ids,
+                 num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m, split,
+                 workspace, workspace_bytes, stream);
+}
+
+int fused_moe_fp8_blockwise(const void* x, const float* x_scale, const void* w1,
+                            const float* w1_scale, const void* w2, const float* w2_scale,
+                            const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                            const int32_t* num_tokens_post_padded, const float* topk_weights,
+                            void* out, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+                            int32_t block_m, int32_t split, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return run_ffn(MOE_FP8_BLOCKWISE, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids,
+                 expert_ids, num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m,
+                 split, workspace, workspace_bytes, stream);
+}
+
+int fused_moe_mxfp8(const void* x, const uint8_t* x_scale, const void* w1, const uint8_t* w1_scale,
+                    const void* w2, const uint8_t* w2_scale, const int32_t* sorted_token_ids,
+                    const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                    const float* topk_weights, void* out, int64_t T, int64_t K, int64_t N,
+                    int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return run_ffn(MOE_MXFP8, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
+                 num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m, split,
+                 workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

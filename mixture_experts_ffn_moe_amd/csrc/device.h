@@ -1,0 +1,153 @@
+// device.h -- gfx950 device helpers shared by the MoE kernels.
+//
+// MFMA operand layout used throughout (16x16 tiles, wave64):
+//   A (rows x K) : lane l supplies row (l % 16); B (K x cols): lane l supplies
+//   column (l % 16).  Per 128-wide K step a lane holds, for its row/column,
+//   the bytes at offsets c*64 + 16*g .. +16 of the step (g = l / 16 is the
+//   lane group, c = 0..NCHUNK-1).  For e4m3 (NCHUNK = 2) this is the
+//   instruction's own K order of v_mfma_*_16x16x128_f8f6f4, so the MX scale
+//   a lane passes (lane group g) is the scale of the 32-wide K block g of the
+//   step.  For bf16 (NCHUNK = 4) chunk c feeds the c-th 16x16x32 MFMA of the
+//   step; A and B use the same order, so the contraction covers the 128
+//   elements once.
+//   C/D : lane l holds column (l % 16), rows 4*(l/16) + i, i = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+enum : int { KIND_BF16 = 0, KIND_FP8B = 1, KIND_MX = 2 };
+
+template <int KIND>
+struct KindTraits {
+  static constexpr int ES = (KIND == KIND_BF16) ? 2 : 1;  // bytes per element
+  static constexpr int NCHUNK = (KIND == KIND_BF16) ? 4 : 2;  // 16B chunks / lane / step
+  static constexpr int STEP_BYTES = 128 * ES;                 // bytes of one row per K step
+};
+
+// One lane's share of a 16-row (or 16-column) operand for one 128-wide K step.
+template <int KIND>
+struct Frag {
+  uint4 c[KindTraits<KIND>::NCHUNK];
+};
+
+// Buffer resource over [base, base + bytes): loads past the end return 0.
+// Word 3 = 0x00020000 is the raw (untyped) dword format of CDNA buffers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+__device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+
+__device__ __forceinline__ int buf_loadu8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (int)__builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+
+// Fragment of one row for one K step: `voff` is the row's byte offset plus
+// 16 * lane group, `soff` the step's byte offset (wave-uniform).
+template <int KIND>
+__device__ __forceinline__ void load_frag(Frag<KIND>& f, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                          uint32_t soff) {
+#pragma unroll
+  for (int c = 0; c < KindTraits<KIND>::NCHUNK; ++c) f.c[c] = buf_load16(r, voff + c * 64, soff);
+}
+
+template <int KIND>
+__device__ __forceinline__ void load_frag_ptr(Frag<KIND>& f, const uint8_t* row_step_ptr, int g) {
+#pragma unroll
+  for (int c = 0; c < KindTraits<KIND>::NCHUNK; ++c)
+    f.c[c] = *reinterpret_cast<const uint4*>(row_step_ptr + c * 64 + 16 * g);
+}
+
+template <int KIND>
+__device__ __forceinline__ void zero_frag(Frag<KIND>& f) {
+#pragma unroll
+  for (int c = 0; c < KindTraits<KIND>::NCHUNK; ++c) f.c[c] = make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x8 as_i32x8(const uint4& lo, const uint4& hi) {
+  i32x8 v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// acc += A . B over one 128-wide K step, no scales (bf16 and e4m3).
+template <int KIND>
+__device__ __forceinline__ f32x4 mfma_step(const Frag<KIND>& a, const Frag<KIND>& b, f32x4 acc) {
+  if constexpr (KIND == KIND_BF16) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a.c[c]), as_bf16x8(b.c[c]), acc, 0, 0, 0);
+    return acc;
+  } else {
+    // format 0 = e4m3 for both operands; zero scale operands select the
+    // unscaled instruction
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        as_i32x8(a.c[0], a.c[1]), as_i32x8(b.c[0], b.c[1]), acc, 0, 0, 0, 0, 0, 0);
+  }
+}
+
+// acc += (A * 2^(sa-127)) . (B * 2^(sb-127)) with per-lane e8m0 scales
+// (lane group g: K block g of the step).
+__device__ __forceinline__ f32x4 mfma_step_mx(const Frag<KIND_MX>& a, const Frag<KIND_MX>& b,
+                                              f32x4 acc, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+      as_i32x8(a.c[0], a.c[1]), as_i32x8(b.c[0], b.c[1]), acc, 0, 0, 0, sa, 0, sb);
+}
+
+// silu(g) * u in fp32: g / (1 + 2^(-g*log2 e)) with the hardware exp2 and an
+// IEEE division.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g / (1.0f + e) * u;
+}
+
+// fp32 -> e4m3 code, round to nearest even, saturating at +-448.  The
+// hardware conversion rounds to nearest even but returns NaN past the 464
+// midpoint, so the value is clamped first.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  v = __builtin_fminf(__builtin_fmaxf(v, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// floor(log2 a) - 8 clamped to [-127, 127] for a >= 0 (a == 0 or subnormal
+// gives -127): the OCP MX shared exponent for e4m3 elements.
+__device__ __forceinline__ int mx_shared_exp(float a) {
+  uint32_t bits = __float_as_uint(a);
+  int ef = (int)((bits >> 23) & 0xFFu);
+  if (ef == 0) return -127;
+  int s = ef - 127 - 8;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+__device__ __forceinline__ float wave_max16(float v) {
+  // max over the 16 lanes sharing l / 16 (xor offsets stay inside the group)
+  v = __builtin_fmaxf(v, __shfl_xor(v, 1));
+  v = __builtin_fmaxf(v, __shfl_xor(v, 2));
+  v = __builtin_fmaxf(v, __shfl_xor(v, 4));
+  v = __builtin_fmaxf(v, __shfl_xor(v, 8));
+  return v;
+}

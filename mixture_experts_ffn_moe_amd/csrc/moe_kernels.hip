@@ -1,0 +1,633 @@
+// moe_kernels.hip -- expert FFN kernels for gfx950 (bf16, blockwise FP8, MXFP8).
+//
+// Stages ([hpc-ops RFC] "Background": gather, gate/up GroupGEMM, SiLU * gate
+// with FP8 requantization, down GroupGEMM, top-k weighted reduction):
+//
+//   split mode ([prime-flash] introduction, split=True):
+//     k_zero     clear the per-route "placed" flags
+//     k_up       per (block_m rows of one expert, 128-wide slice of I):
+//                gather x rows, gate/up GEMM on MFMA, SwiGLU, requantize,
+//                write the intermediate slice (+ scales) to the workspace
+//     k_down     per (block_m rows, 256 output columns): intermediate . w2^T
+//                over all of I (no split-K), fp32 per-route result rows
+//     k_combine  out[t] = bf16(sum_j w[t,j] * y[t,j]) in route order
+//                (deterministic)
+//   fused mode ([prime-flash] introduction, split=False):
+//     k_zero     clear the fp32 (T, K) accumulator
+//     k_fused    per (block_m rows, 128-wide slice of I): k_up's work with
+//                the requantized slice kept in LDS, then the slice's
+//                partial down GEMM over all K output columns, weighted by
+//                the route weight and added into the accumulator (fp32
+//                atomics: split-K over I)
+//     k_finalize accumulator -> bf16 out
+//
+// Blockwise FP8 promotion: each 128-wide K step is one MFMA into a zeroed
+// tile, then acc += tile * (row scale * weight block scale) in fp32 (one
+// scale group and one rescale per step).  MX: the e8m0 scales go straight
+// into the block-scaled MFMA.  bf16: plain MFMA accumulation.
+//
+// Waves: a workgroup has 4 waves per 64 rows (256 threads for block_m <= 64,
+// 512 for block_m = 128).  Wave (wm, wn) owns rows [64*wm, 64*wm+64) of the
+// block and, in the up GEMM, gate and up columns [32*wn, 32*wn+32) of the
+// slice, so SwiGLU pairs gate and up inside one wave's accumulators.
+#include "device.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kSlice = 128;  // width of an I slice (= blockwise scale group)
+
+// Operands of a wave's GEMM: A rows (l % 16 of each 16-row subtile) and B
+// rows (l % 16 of each 16-column subtile) as buffer resources plus per-lane
+// 32-bit byte offsets (row offset + 16 * lane group); the K step's offset is
+// the wave-uniform soffset.
+template <int MI, int NI>
+struct Operand {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t a[MI], b[NI];
+  // FP8B: fp32 scale of each of the lane's C rows (byte offsets, step stride
+  // 4 bytes) and the weight block scale row of each n-subtile (uniform)
+  __amdgpu_buffer_rsrc_t rsa;
+  uint32_t as[MI][4];
+  const float* bs[NI];
+  // MX: e8m0 rows of the lane's A row and B row (+ lane group), 4 bytes per step
+  __amdgpu_buffer_rsrc_t rxa, rxb;
+  uint32_t ax[MI], bx[NI];
+};
+
+template <int KIND, int MI, int NI, int D>
+struct Ring {
+  Frag<KIND> fa[D][MI];
+  Frag<KIND> fb[D][NI];
+  float sa[D][MI][4];
+  float sb[D][NI];
+  int xa[D][MI];
+  int xb[D][NI];
+};
+
+template <int KIND, int MI, int NI, int D>
+__device__ __forceinline__ void ring_load(Ring<KIND, MI, NI, D>& r, int slot, int ks,
+                                          const Operand<MI, NI>& op) {
+  const uint32_t soff = (uint32_t)ks * KindTraits<KIND>::STEP_BYTES;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) load_frag<KIND>(r.fa[slot][mi], op.ra, op.a[mi], soff);
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) load_frag<KIND>(r.fb[slot][ni], op.rb, op.b[ni], soff);
+  if constexpr (KIND == KIND_FP8B) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.sa[slot][mi][i] = buf_loadf(op.rsa, op.as[mi][i], ks * 4);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) r.sb[slot][ni] = op.bs[ni][ks];
+  }
+  if constexpr (KIND == KIND_MX) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) r.xa[slot][mi] = buf_loadu8(op.rxa, op.ax[mi], ks * 4);
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) r.xb[slot][ni] = buf_loadu8(op.rxb, op.bx[ni], ks * 4);
+  }
+}
+
+template <int KIND, int MI, int NI, int D>
+__device__ __forceinline__ void ring_compute(const Ring<KIND, MI, NI, D>& r, int slot,
+                                             f32x4 (&acc)[MI][NI]) {
+  if constexpr (KIND == KIND_FP8B) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 t = mfma_step<KIND>(r.fa[slot][mi], r.fb[slot][ni], z);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[mi][ni][i] += t[i] * (r.sa[slot][mi][i] * r.sb[slot][ni]);
+      }
+  } else if constexpr (KIND == KIND_MX) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = mfma_step_mx(r.fa[slot][mi], r.fb[slot][ni], acc[mi][ni], r.xa[slot][mi],
+                                   r.xb[slot][ni]);
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = mfma_step<KIND>(r.fa[slot][mi], r.fb[slot][ni], acc[mi][ni]);
+  }
+}
+
+// acc[mi][ni] = sum over ksteps 128-wide steps of A rows . B rows (with the
+// dtype's scales), D steps of operands prefetched into registers.
+template <int KIND, int MI, int NI, int D>
+__device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int ksteps,
+                                           f32x4 (&acc)[MI][NI]) {
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Ring<KIND, MI, NI, D> r;
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < ksteps) ring_load<KIND>(r, d, d, op);
+  for (int k0 = 0; k0 < ksteps; k0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int ks = k0 + d;
+      if (ks < ksteps) {
+        ring_compute<KIND>(r, d, acc);
+        if (ks + D < ksteps) ring_load<KIND>(r, d, ks + D, op);
+      }
+    }
+  }
+}
+
+template <int BM>
+struct BlockShape {
+  static constexpr int MI = (BM < 64 ? BM : 64) / 16;  // 16-row subtiles per wave
+  static constexpr int WM = (BM + 63) / 64;            // wave rows
+  static constexpr int THREADS = 256 * WM;
+};
+
+__device__ __forceinline__ int token_of(int id, int top_k) {
+  return id >= 0 ? id / top_k : 0;  // padding rows read token 0 and are discarded
+}
+
+// Gate/up GEMM + SwiGLU for one (block, slice) tile: h[mi][j] holds the
+// lane's C elements of gate/up column pair j (columns 32*wn + 16*j + l%16 of
+// the slice), rows 64*wm + 16*mi + 4*(l/16) + i.
+template <int KIND, int BM, int D>
+__device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const int* ids,
+                                        f32x4 (&h)[BlockShape<BM>::MI][2]) {
+  constexpr int MI = BlockShape<BM>::MI;
+  constexpr int ES = KindTraits<KIND>::ES;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wn = wid & 3, wm = wid >> 2;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int K = p.K, I = p.I, N = 2 * p.I;
+  const int KS = K / 128, S = I / kSlice;
+  Operand<MI, 4> op;
+  op.ra = make_rsrc(p.x, (uint32_t)((size_t)p.T * K * ES));
+  op.rb = make_rsrc(p.w1 + (size_t)e * N * K * ES, (uint32_t)((size_t)N * K * ES));
+  if constexpr (KIND == KIND_FP8B) op.rsa = make_rsrc(p.xs, (uint32_t)((size_t)p.T * KS * 4));
+  if constexpr (KIND == KIND_MX) {
+    op.rxa = make_rsrc(p.xs, (uint32_t)((size_t)p.T * (K / 32)));
+    op.rxb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w1s) + (size_t)e * N * (K / 32),
+                       (uint32_t)((size_t)N * (K / 32)));
+  }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int row = wm * 64 + mi * 16 + r16;
+    const int tok = token_of(ids[row], p.top_k);
+    op.a[mi] = (uint32_t)tok * K * ES + 16 * g;
+    if constexpr (KIND == KIND_FP8B) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int crow = wm * 64 + mi * 16 + 4 * g + i;
+        op.as[mi][i] = (uint32_t)token_of(ids[crow], p.top_k) * KS * 4;
+      }
+    }
+    if constexpr (KIND == KIND_MX) op.ax[mi] = (uint32_t)tok * (K / 32) + g;
+  }
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int n = (ni < 2 ? 0 : I) + s * kSlice + 32 * wn + 16 * (ni & 1) + r16;
+    op.b[ni] = (uint32_t)n * K * ES + 16 * g;
+    if constexpr (KIND == KIND_FP8B) {
+      const int nb = (ni < 2 ? 0 : S) + s;
+      op.bs[ni] = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + nb) * KS;
+    }
+    if constexpr (KIND == KIND_MX) op.bx[ni] = (uint32_t)n * (K / 32) + g;
+  }
+  f32x4 acc[MI][4];
+  gemm_steps<KIND, MI, 4, D>(op, KS, acc);
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[mi][j][i] = swiglu(acc[mi][j][i], acc[mi][2 + j][i]);
+}
+
+// Requantize the tile: codes[mi][j][i] (bf16 bits or e4m3 code) and the
+// per-row scale (FP8B: fp32 sf of the whole 128-wide slice; MX: e8m0 of this
+// wave's 32 columns).  FP8B reduces amax over the 4 waves through LDS.
+template <int KIND, int BM>
+__device__ __forceinline__ void requant_tile(const f32x4 (&h)[BlockShape<BM>::MI][2],
+                                             uint32_t (&codes)[BlockShape<BM>::MI][2][4],
+                                             float (&sf)[BlockShape<BM>::MI][4],
+                                             int (&sx)[BlockShape<BM>::MI][4],
+                                             float* lds_amax /* [4][BM] */) {
+  constexpr int MI = BlockShape<BM>::MI;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wn = wid & 3, wm = wid >> 2;
+  const int g = lane >> 4, r16 = lane & 15;
+  if constexpr (KIND == KIND_BF16) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) codes[mi][j][i] = f32_to_bf16(h[mi][j][i]);
+    return;
+  } else {
+    float am[MI][4];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        am[mi][i] = wave_max16(__builtin_fmaxf(__builtin_fabsf(h[mi][0][i]),
+                                               __builtin_fabsf(h[mi][1][i])));
+    if constexpr (KIND == KIND_FP8B) {
+      if (r16 == 0) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            lds_amax[wn * BM + wm * 64 + mi * 16 + 4 * g + i] = am[mi][i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = wm * 64 + mi * 16 + 4 * g + i;
+          float a = __builtin_fmaxf(__builtin_fmaxf(lds_amax[row], lds_amax[BM + row]),
+                                    __builtin_fmaxf(lds_amax[2 * BM + row], lds_amax[3 * BM + row]));
+          a = __builtin_fmaxf(a, 1e-10f);
+          const float f = a * (1.0f / 448.0f);
+          const float inv = 1.0f / f;
+          sf[mi][i] = f;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) codes[mi][j][i] = f32_to_e4m3(h[mi][j][i] * inv);
+        }
+    } else {  // MX: this wave's 32 columns form one group
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int se = mx_shared_exp(am[mi][i]);
+          sx[mi][i] = se + 127;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            codes[mi][j][i] = f32_to_e4m3(__builtin_amdgcn_ldexpf(h[mi][j][i], -se));
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// split mode
+// ---------------------------------------------------------------------------
+
+template <int KIND, int BM, int D>
+__global__ void __launch_bounds__(BlockShape<BM>::THREADS)
+k_up(MoeArgs p) {
+  constexpr int MI = BlockShape<BM>::MI;
+  constexpr int ES = KindTraits<KIND>::ES;
+  const int S = p.I / kSlice;
+  const int b = blockIdx.x / S, s = blockIdx.x % S;
+  if (b * BM >= *p.ntp) return;
+  const int e = p.expert_ids[b];
+  if ((unsigned)e >= (unsigned)p.E) return;
+  __shared__ int ids[BM];
+  __shared__ float lds_amax[4 * BM];
+  if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
+  __syncthreads();
+  f32x4 h[MI][2];
+  up_tile<KIND, BM, D>(p, e, s, ids, h);
+  uint32_t codes[MI][2][4];
+  float sf[MI][4];
+  int sx[MI][4];
+  requant_tile<KIND, BM>(h, codes, sf, sx, lds_amax);
+
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wn = wid & 3, wm = wid >> 2;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int I = p.I;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 64 + mi * 16 + 4 * g + i;
+      const size_t pos = (size_t)b * BM + row;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = s * kSlice + 32 * wn + 16 * j + r16;
+        if constexpr (ES == 2)
+          reinterpret_cast<uint16_t*>(p.hq)[pos * I + col] = (uint16_t)codes[mi][j][i];
+        else
+          p.hq[pos * I + col] = (uint8_t)codes[mi][j][i];
+      }
+      if (r16 == 0) {
+        if constexpr (KIND == KIND_FP8B) {
+          if (wn == 0) reinterpret_cast<float*>(p.hs)[pos * (I / 128) + s] = sf[mi][i];
+        }
+        if constexpr (KIND == KIND_MX) p.hs[pos * (I / 32) + s * 4 + wn] = (uint8_t)sx[mi][i];
+      }
+    }
+  if (s == 0 && threadIdx.x < BM) {
+    const int id = ids[threadIdx.x];
+    if (id >= 0) p.flags[id] = 1;
+  }
+}
+
+template <int KIND, int BM, int D>
+__global__ void __launch_bounds__(BlockShape<BM>::THREADS)
+k_down(MoeArgs p) {
+  constexpr int MI = BlockShape<BM>::MI;
+  constexpr int ES = KindTraits<KIND>::ES;
+  const int K = p.K, I = p.I;
+  const int NT = (K + 255) / 256;
+  const int b = blockIdx.x / NT, ct = blockIdx.x % NT;
+  if (b * BM >= *p.ntp) return;
+  const int e = p.expert_ids[b];
+  if ((unsigned)e >= (unsigned)p.E) return;
+  __shared__ int ids[BM];
+  if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wn = wid & 3, wm = wid >> 2;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int c0 = ct * 256 + 64 * wn;  // this wave's 64 output columns
+  if (c0 >= K) return;
+  const int IS = I / 128;
+  Operand<MI, 4> op;
+  op.ra = make_rsrc(p.hq, (uint32_t)((size_t)p.blocks_cap * BM * I * ES));
+  op.rb = make_rsrc(p.w2 + (size_t)e * K * I * ES, (uint32_t)((size_t)K * I * ES));
+  if constexpr (KIND == KIND_FP8B)
+    op.rsa = make_rsrc(p.hs, (uint32_t)((size_t)p.blocks_cap * BM * IS * 4));
+  if constexpr (KIND == KIND_MX) {
+    op.rxa = make_rsrc(p.hs, (uint32_t)((size_t)p.blocks_cap * BM * (I / 32)));
+    op.rxb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w2s) + (size_t)e * K * (I / 32),
+                       (uint32_t)((size_t)K * (I / 32)));
+  }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const uint32_t pos = (uint32_t)b * BM + wm * 64 + mi * 16 + r16;
+    op.a[mi] = pos * I * ES + 16 * g;
+    if constexpr (KIND == KIND_FP8B) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t cpos = (uint32_t)b * BM + wm * 64 + mi * 16 + 4 * g + i;
+        op.as[mi][i] = cpos * IS * 4;
+      }
+    }
+    if constexpr (KIND == KIND_MX) op.ax[mi] = pos * (I / 32) + g;
+  }
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int c = c0 + 16 * ni + r16;
+    op.b[ni] = (uint32_t)c * I * ES + 16 * g;
+    if constexpr (KIND == KIND_FP8B)
+      op.bs[ni] = reinterpret_cast<const float*>(p.w2s) + ((size_t)e * (K / 128) + c0 / 128) * IS;
+    if constexpr (KIND == KIND_MX) op.bx[ni] = (uint32_t)c * (I / 32) + g;
+  }
+  f32x4 acc[MI][4];
+  gemm_steps<KIND, MI, 4, D>(op, IS, acc);
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int id = ids[wm * 64 + mi * 16 + 4 * g + i];
+      if (id < 0) continue;
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) p.yr[(size_t)id * K + c0 + 16 * ni + r16] = acc[mi][ni][i];
+    }
+}
+
+// out[t, c:c+4] = bf16(sum_j w[t,j] * y[t*top_k+j, c:c+4]), j ascending.
+__global__ void __launch_bounds__(256) k_combine(MoeArgs p) {
+  const int K = p.K;
+  const int CT = (K + 1023) / 1024;
+  const int t = blockIdx.x / CT;
+  const int c = (blockIdx.x % CT) * 1024 + threadIdx.x * 4;
+  if (c >= K) return;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < p.top_k; ++j) {
+    const size_t id = (size_t)t * p.top_k + j;
+    if (!p.flags[id]) continue;
+    const float w = p.topk_w[id];
+    const float4 y = *reinterpret_cast<const float4*>(p.yr + id * K + c);
+    s.x += w * y.x;
+    s.y += w * y.y;
+    s.z += w * y.z;
+    s.w += w * y.w;
+  }
+  uint2 o;
+  o.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
+  o.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
+  *reinterpret_cast<uint2*>(p.out + (size_t)t * K + c) = o;
+}
+
+// ---------------------------------------------------------------------------
+// fused mode
+// ---------------------------------------------------------------------------
+
+template <int KIND, int BM, int D>
+__global__ void __launch_bounds__(BlockShape<BM>::THREADS)
+k_fused(MoeArgs p) {
+  constexpr int MI = BlockShape<BM>::MI;
+  constexpr int ES = KindTraits<KIND>::ES;
+  constexpr int QROW = 128 * ES + 16;  // LDS row stride of the slice (bytes)
+  const int S = p.I / kSlice;
+  const int b = blockIdx.x / S, s = blockIdx.x % S;
+  if (b * BM >= *p.ntp) return;
+  const int e = p.expert_ids[b];
+  if ((unsigned)e >= (unsigned)p.E) return;
+  __shared__ int ids[BM];
+  __shared__ float lds_amax[4 * BM];
+  __shared__ float lds_sf[BM];
+  __shared__ uint8_t lds_sx[BM * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_q[BM * QROW];
+  if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
+  __syncthreads();
+  f32x4 h[MI][2];
+  up_tile<KIND, BM, D>(p, e, s, ids, h);
+  uint32_t codes[MI][2][4];
+  float sf[MI][4];
+  int sx[MI][4];
+  requant_tile<KIND, BM>(h, codes, sf, sx, lds_amax);
+
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int wn = wid & 3, wm = wid >> 2;
+  const int g = lane >> 4, r16 = lane & 15;
+  const int K = p.K, I = p.I;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 64 + mi * 16 + 4 * g + i;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int col = 32 * wn + 16 * j + r16;
+        if constexpr (ES == 2)
+          *reinterpret_cast<uint16_t*>(lds_q + row * QROW + col * 2) = (uint16_t)codes[mi][j][i];
+        else
+          lds_q[row * QROW + col] = (uint8_t)codes[mi][j][i];
+      }
+      if (r16 == 0) {
+        if constexpr (KIND == KIND_FP8B) {
+          if (wn == 0) lds_sf[row] = sf[mi][i];
+        }
+        if constexpr (KIND == KIND_MX) lds_sx[row * 4 + wn] = (uint8_t)sx[mi][i];
+      }
+    }
+  __syncthreads();
+
+  // partial down GEMM of this slice: rows of this wave x all K columns
+  Frag<KIND> fa[MI];
+  int xa[MI];
+  float rsf[MI][4];
+  int ctok[MI][4];
+  float cw[MI][4];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int row = wm * 64 + mi * 16 + r16;
+#pragma unroll
+    for (int c = 0; c < KindTraits<KIND>::NCHUNK; ++c)
+      fa[mi].c[c] = *reinterpret_cast<const uint4*>(lds_q + row * QROW + c * 64 + 16 * g);
+    if constexpr (KIND == KIND_MX) xa[mi] = lds_sx[row * 4 + g];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int crow = wm * 64 + mi * 16 + 4 * g + i;
+      const int id = ids[crow];
+      ctok[mi][i] = id >= 0 ? id / p.top_k : -1;
+      cw[mi][i] = id >= 0 ? p.topk_w[id] : 0.f;
+      if constexpr (KIND == KIND_FP8B) rsf[mi][i] = lds_sf[crow];
+    }
+  }
+  const int IS = I / 128;
+  const int nchunks = K / 64;  // 64-column chunks, round-robin over the 4 wave columns
+  const __amdgpu_buffer_rsrc_t rw2 =
+      make_rsrc(p.w2 + (size_t)e * K * I * ES, (uint32_t)((size_t)K * I * ES));
+  const uint32_t soff = (uint32_t)s * kSlice * ES;
+  for (int q = wn; q < nchunks; q += 4) {
+    const int c0 = q * 64;
+    Frag<KIND> fb[4];
+    int xb[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int c = c0 + 16 * ni + r16;
+      load_frag<KIND>(fb[ni], rw2, (uint32_t)c * I * ES + 16 * g, soff);
+      if constexpr (KIND == KIND_MX)
+        xb[ni] = reinterpret_cast<const uint8_t*>(p.w2s)[((size_t)e * K + c) * (I / 32) + 4 * s + g];
+    }
+    float swb = 1.f;
+    if constexpr (KIND == KIND_FP8B)
+      swb = reinterpret_cast<const float*>(p.w2s)[((size_t)e * (K / 128) + c0 / 128) * IS + s];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (KIND == KIND_MX)
+          y = mfma_step_mx(fa[mi], fb[ni], y, xa[mi], xb[ni]);
+        else
+          y = mfma_step<KIND>(fa[mi], fb[ni], y);
+        const int c = c0 + 16 * ni + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (ctok[mi][i] < 0) continue;
+          float v = y[i];
+          if constexpr (KIND == KIND_FP8B) v *= rsf[mi][i] * swb;
+          atomicAdd(p.acc + (size_t)ctok[mi][i] * K + c, v * cw[mi][i]);
+        }
+      }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_finalize(MoeArgs p) {
+  const size_t n4 = (size_t)p.T * p.K / 4;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const float4 v = reinterpret_cast<const float4*>(p.acc)[i];
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    o.y = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    reinterpret_cast<uint2*>(p.out)[i] = o;
+  }
+}
+
+__global__ void __launch_bounds__(256) k_zero(uint4* ptr, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    ptr[i] = make_uint4(0, 0, 0, 0);
+}
+
+inline unsigned grid_for(size_t n, size_t per_block) {
+  size_t g = (n + per_block - 1) / per_block;
+  if (g > 65536) g = 65536;
+  if (g == 0) g = 1;
+  return (unsigned)g;
+}
+
+// Register-prefetch depth (K steps in flight per wave), sized so that the
+// operand ring, the accumulators and the scales fit the register file without
+// spills (a bf16 fragment is twice an e4m3 one).
+template <int KIND, int BM>
+constexpr int prefetch_depth() {
+  if constexpr (KIND == KIND_BF16) return BM <= 32 ? 2 : 1;
+  else return BM == 16 ? 4 : BM == 32 ? 3 : BM == 64 ? 2 : 1;
+}
+
+inline void mark(const TimingHook& h, int which, bool after, hipStream_t st) {
+  if (h.which == which && h.before && h.after) hipEventRecord(after ? h.after : h.before, st);
+}
+
+template <int KIND, int BM>
+hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const TimingHook& hk) {
+  constexpr int THREADS = BlockShape<BM>::THREADS;
+  constexpr int D = prefetch_depth<KIND, BM>();
+  const int S = a.I / kSlice;
+  const size_t R = (size_t)a.T * a.top_k;
+  if (split) {
+    const size_t fbytes = (R * 4 + 15) / 16;
+    hipLaunchKernelGGL(k_zero, dim3(grid_for(fbytes, 256)), dim3(256), 0, st,
+                       reinterpret_cast<uint4*>(a.flags), fbytes);
+    mark(hk, 1, false, st);
+    hipLaunchKernelGGL((k_up<KIND, BM, D>), dim3((unsigned)a.blocks_cap * S), dim3(THREADS), 0, st, a);
+    mark(hk, 1, true, st);
+    const int NT = (a.K + 255) / 256;
+    mark(hk, 2, false, st);
+    hipLaunchKernelGGL((k_down<KIND, BM, D>), dim3((unsigned)a.blocks_cap * NT), dim3(THREADS), 0,
+                       st, a);
+    mark(hk, 2, true, st);
+    const int CT = (a.K + 1023) / 1024;
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
+  } else {
+    const size_t n16 = (size_t)a.T * a.K * 4 / 16;
+    hipLaunchKernelGGL(k_zero, dim3(grid_for(n16, 256)), dim3(256), 0, st,
+                       reinterpret_cast<uint4*>(a.acc), n16);
+    mark(hk, 1, false, st);
+    hipLaunchKernelGGL((k_fused<KIND, BM, D>), dim3((unsigned)a.blocks_cap * S), dim3(THREADS), 0,
+                       st, a);
+    mark(hk, 1, true, st);
+    hipLaunchKernelGGL(k_finalize, dim3(grid_for((size_t)a.T * a.K / 4, 256)), dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_kind(int block_m, int split, const MoeArgs& a, hipStream_t st,
+                       const TimingHook& hk) {
+  switch (block_m) {
+    case 16: return launch_kind_bm<KIND, 16>(split, a, st, hk);
+    case 32: return launch_kind_bm<KIND, 32>(split, a, st, hk);
+    case 64: return launch_kind_bm<KIND, 64>(split, a, st, hk);
+    case 128: return launch_kind_bm<KIND, 128>(split, a, st, hk);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_moe(int kind, int block_m, int split, const MoeArgs& a, hipStream_t st,
+                      const TimingHook& hk) {
+  switch (kind) {
+    case KIND_BF16: return launch_kind<KIND_BF16>(block_m, split, a, st, hk);
+    case KIND_FP8B: return launch_kind<KIND_FP8B>(block_m, split, a, st, hk);
+    case KIND_MX: return launch_kind<KIND_MX>(block_m, split, a, st, hk);
+    default: return hipErrorInvalidValue;
+  }
+}

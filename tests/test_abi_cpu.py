@@ -1,0 +1,107 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/moe.h declares, and rejects bad arguments on the host before anything
+is enqueued (each call below returns before its first HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_moe_amd as moe
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "moe.h")
+FAKE = 1 << 20          # 16-byte aligned, never dereferenced (errors come first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    L = moe.lib()
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTED_SYMBOLS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_capacity_closed_form():
+    for T, k, E, bm in [(0, 2, 8, 16), (1, 6, 256, 16), (8192, 8, 288, 128), (37, 3, 5, 64)]:
+        rows, blocks = moe.moe_align_capacity(T, k, E, bm)
+        R = T * k
+        assert rows == R + min(E, R) * (bm - 1)
+        assert blocks == -(-rows // bm)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 2, 8, 16), -2), ((4, 0, 8, 16), -2), ((4, 2, 0, 16), -2),
+    ((4, 2, 8, 48), -3), ((1 << 29, 8, 8, 16), -2)])
+def test_capacity_errors(args, status):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_align_capacity(*args)
+    assert ei.value.status == status
+
+
+def test_align_errors_before_launch():
+    L = moe.lib()
+    P = ctypes.c_void_p
+    # E > 1024
+    assert L.moe_align(P(FAKE), 4, 2, 2000, 16, P(FAKE), P(FAKE), P(FAKE), None) == -3
+    # null outputs
+    assert L.moe_align(P(FAKE), 4, 2, 8, 16, None, P(FAKE), P(FAKE), None) == -1
+    # misaligned
+    assert L.moe_align(P(FAKE + 4), 4, 2, 8, 16, P(FAKE), P(FAKE), P(FAKE), None) == -4
+    assert b"aligned" in L.moe_last_error()
+
+
+def _ffn(L, fn, K=4096, N=4096, T=8, E=16, k=2, bm=16, split=-1, ws=FAKE, ws_bytes=1 << 40,
+         x=FAKE, sorted_ids=FAKE, scales=True):
+    P = ctypes.c_void_p
+    tail = [P(sorted_ids), P(FAKE), P(FAKE), P(FAKE), P(FAKE), T, K, N, E, k, bm, split,
+            P(ws) if ws else None, ws_bytes, None]
+    if fn == "fused_moe_bf16":
+        return getattr(L, fn)(P(x), P(FAKE), P(FAKE), *tail)
+    s = P(FAKE) if scales else None
+    return getattr(L, fn)(P(x), s, P(FAKE), s, P(FAKE), s, *tail)
+
+
+@pytest.mark.parametrize("fn", ["fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8"])
+def test_ffn_errors_before_launch(fn):
+    L = moe.lib()
+    assert _ffn(L, fn, K=4000) == -3                    # K % 128
+    assert _ffn(L, fn, N=4095) == -2                    # odd N
+    assert _ffn(L, fn, N=4096 + 128) == -3              # I % 128
+    assert _ffn(L, fn, bm=24) == -3                     # block_m
+    assert _ffn(L, fn, T=-1) == -2
+    assert _ffn(L, fn, k=0) == -2
+    assert _ffn(L, fn, split=2) == -3
+    assert _ffn(L, fn, x=0) == -1                       # null input
+    assert _ffn(L, fn, x=FAKE + 8) == -4                # misaligned
+    assert _ffn(L, fn, ws=0) == -5                      # no workspace
+    assert _ffn(L, fn, ws_bytes=100) == -5              # workspace too small
+    assert b"workspace" in L.moe_last_error()
+    if fn != "fused_moe_bf16":
+        assert _ffn(L, fn, scales=False) == -1
+    # T == 0 is a successful no-op (no launch)
+    assert _ffn(L, fn, T=0) == 0
+
+
+def test_workspace_sizes_grow_with_tokens():
+    small = moe.moe_workspace_size("fp8_blockwise", 64, 4096, 4096, 256, 6, 16, split=1)
+    big = moe.moe_workspace_size("fp8_blockwise", 4096, 4096, 4096, 256, 6, 64, split=1)
+    fused = moe.moe_workspace_size("fp8_blockwise", 64, 4096, 4096, 256, 6, 16, split=0)
+    assert 0 < small < big
+    assert fused == 64 * 4096 * 4
+    h, hs = moe.moe_workspace_layout("fp8_blockwise", 64, 4096, 4096, 256, 6, 16)
+    assert h % 256 == 0 and hs > h
+
+
+def test_heuristics():
+    assert moe.moe_select_block_m(8, 6, 256) == 16
+    assert moe.moe_select_block_m(8192, 8, 288) == 128
+    assert moe.moe_select_split("fp8_blockwise", 8, 4096, 4096, 256, 6, 16) == 0
+    assert moe.moe_select_split("fp8_blockwise", 8192, 4096, 4096, 288, 8, 128) == 1

@@ -1,0 +1,62 @@
+"""Planner parity on the GPU: moe_align through the C ABI must equal the
+oracle's alignment bit for bit (all three outputs, over the whole capacity)."""
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import mixture_experts_ffn_moe_amd as moe
+from oracle.align import align_ref
+
+from .gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _routing(kind, T, E, k, seed):
+    g = torch.Generator().manual_seed(seed)
+    if kind == "uniform":
+        ids, _ = datagen.make_routing(T, E, k, "uniform", tag=f"al{seed}")
+    elif kind == "zipf":
+        ids, _ = datagen.make_routing(T, E, k, "zipf", tag=f"al{seed}")
+    elif kind == "masked":
+        ids, _ = datagen.make_routing(T, E, k, "normal_masked", tag=f"al{seed}", n_masked=8)
+    elif kind == "one":
+        ids = torch.randint(0, E, (T, k), generator=g, dtype=torch.int32)
+        ids[:, 0] = 3
+    elif kind == "oor":
+        ids = torch.randint(-3, E + 3, (T, k), generator=g, dtype=torch.int32)
+    else:
+        raise ValueError(kind)
+    return ids.to(torch.int32)
+
+
+CASES = [
+    ("uniform", 0, 8, 2), ("uniform", 1, 8, 2), ("uniform", 37, 8, 2),
+    ("uniform", 8, 256, 6), ("uniform", 256, 256, 6), ("masked", 1024, 288, 8),
+    ("zipf", 4096, 384, 6), ("one", 300, 16, 4), ("oor", 500, 10, 3),
+    ("uniform", 8192, 288, 8), ("uniform", 512, 32, 8), ("uniform", 50, 1024, 4),
+]
+
+
+@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("kind,T,E,k", CASES)
+def test_align_bit_exact(kind, T, E, k, bm):
+    say(f"[gpu] align kind={kind} T={T} E={E} k={k} bm={bm}")
+    ids = _routing(kind, T, E, k, T * 7 + E)
+    s_ref, e_ref, n_ref = align_ref(ids.numpy(), E, bm)
+    s, e, n = moe.moe_align(ids.cuda(), E, bm)
+    torch.cuda.synchronize()
+    assert int(n.item()) == n_ref
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(e.cpu().numpy(), e_ref)
+
+
+def test_align_repeatable():
+    ids = _routing("uniform", 2048, 256, 6, 3).cuda()
+    a = moe.moe_align(ids, 256, 64)
+    b = moe.moe_align(ids, 256, 64)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
