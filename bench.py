@@ -157,6 +157,8 @@ def main():
     ap.add_argument("--split", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -166,6 +168,18 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        # a plain copy of known size: each launch reads and writes exactly
+        # MIB MiB, which calibrates the HBM byte counters of a profiler
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+        return
 
     import datagen
     import mixture_experts_ffn_moe_amd as moe
