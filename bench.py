@@ -156,7 +156,7 @@ def main():
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--split", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=4)
+    ap.add_argument("--cpu-tokens", type=int, default=20)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (counter calibration)")
     args = ap.parse_args()
