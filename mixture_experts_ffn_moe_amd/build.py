@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_mi355x.so")
-SOURCES = ["abi.hip", "align.hip", "moe_kernels.hip"]
+SOURCES = ["abi.hip", "align.hip", "moe_kernels.hip", "moe_tiled.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -39,3 +39,8 @@ struct TimingHook {
 
 hipError_t launch_moe(int kind, int block_m, int split, const MoeArgs& a,
                       hipStream_t stream, const TimingHook& hook);
+
+// LDS-tiled split-mode kernels (moe_tiled.hip) for many rows per expert.
+bool tiled_supported(int kind, int block_m, int K, int I);
+hipError_t launch_tiled(int kind, int block_m, const MoeArgs& a, hipStream_t stream,
+                        const TimingHook& hook);

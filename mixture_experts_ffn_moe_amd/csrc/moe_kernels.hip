@@ -606,6 +606,13 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
     const size_t fbytes = (R * 4 + 15) / 16;
     hipLaunchKernelGGL(k_zero, dim3(grid_for(fbytes, 256)), dim3(256), 0, st,
                        reinterpret_cast<uint4*>(a.flags), fbytes);
+    if (tiled_supported(KIND, BM, a.K, a.I)) {
+      hipError_t e = launch_tiled(KIND, BM, a, st, hk);
+      if (e != hipSuccess) return e;
+      const int CT = (a.K + 1023) / 1024;
+      hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
+      return hipGetLastError();
+    }
     mark(hk, 1, false, st);
     hipLaunchKernelGGL((k_up<KIND, BM, D>), dim3((unsigned)a.blocks_cap * S), dim3(THREADS), 0, st, a);
     mark(hk, 1, true, st);

@@ -180,3 +180,24 @@ def test_many_routes_fused_atomics():
     c = small_case("fp8_blockwise", T=600, E=8, k=4, routing="uniform")
     check(c, 64, 0, label="fused many routes")
     check(c, 64, 1, label="split many routes")
+
+
+@pytest.mark.parametrize("bm", [64, 128])
+@pytest.mark.parametrize("kind,K,I", [("fp8_blockwise", 768, 384), ("mxfp8", 512, 256),
+                                      ("fp8_blockwise", 256, 128)])
+def test_tiled_split_parity(kind, K, I, bm):
+    """The LDS-tiled split-mode kernels (block_m 64 / 128, K a multiple of
+    256): several blocks per expert, several K steps and slices, ragged last
+    blocks, skewed expert load."""
+    c = datagen.make_case(kind, 700, K, I, 6, 2, routing="zipf", tag="tiled")
+    c = to_gpu(c)
+    check(c, bm, 1, label="tiled")
+
+
+def test_tiled_deterministic():
+    c = to_gpu(datagen.make_case("fp8_blockwise", 500, 512, 256, 4, 2, routing="normal",
+                                 tag="tiled-det"))
+    a, _ = moe.run_case(c, block_m=128, split=1)
+    b, _ = moe.run_case(c, block_m=128, split=1)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
