@@ -70,7 +70,7 @@ const char* moe_last_error(void);
  *   *blocks_cap = ceil(*sorted_cap / block_m)
  * (each non-empty expert pads fewer than block_m rows).  Host out-params.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (T < 0, top_k < 1, E < 1,
- * T*top_k >= 2^31), MOE_ERR_UNSUPPORTED (block_m not 16, 32, 64 or 128).
+ * T*top_k >= 2^31), MOE_ERR_UNSUPPORTED (block_m not 16, 32, 64, 128 or 256).
  */
 int moe_align_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m,
                        int64_t* sorted_cap, int64_t* blocks_cap);
@@ -116,9 +116,11 @@ int moe_select_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E,
 /*
  * Suggested block_m for a call (small blocks for decode-sized batches, so
  * that padding does not dominate; larger blocks once experts hold many
- * rows).  *block_m is a host out-param.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE.
+ * rows; 256 only where the dtype and K allow it).  *block_m is a host
+ * out-param.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE.
  */
-int moe_select_block_m(int64_t T, int32_t top_k, int32_t E, int32_t* block_m);
+int moe_select_block_m(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32_t E,
+                       int32_t* block_m);
 
 /*
  * Workspace bytes a fused_moe_* call with these sizes needs (host out-param).
@@ -162,6 +164,8 @@ int moe_workspace_layout(int32_t dtype, int64_t T, int64_t K, int64_t N,
  *                    [0, I) of w1 are the gate, [I, N) the up projection),
  *                    experts, routes per token, planner block.
  *                    K % 128 == 0 and I % 128 == 0 are required.
+ *                    block_m is 16, 32, 64 or 128, or 256 for the e4m3
+ *                    dtypes when K % 256 == 0 (split mode only).
  *   split            -1: choose by size (moe_select_split); 0: fused mode
  *                    (the intermediate stays on chip, the down GEMM is
  *                    split-K over 128-wide slices of I accumulated in fp32);

@@ -75,7 +75,7 @@ def lib():
     L.moe_align.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]
     L.moe_select_split.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32,
                                    ctypes.POINTER(_I32)]
-    L.moe_select_block_m.argtypes = [_I64, _I32, _I32, ctypes.POINTER(_I32)]
+    L.moe_select_block_m.argtypes = [_I32, _I64, _I64, _I32, _I32, ctypes.POINTER(_I32)]
     L.moe_workspace_size.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
                                      ctypes.POINTER(_SZ)]
     L.moe_workspace_layout.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32,
@@ -150,9 +150,10 @@ def moe_select_split(dtype, T, K, N, num_experts, top_k, block_m):
     return out.value
 
 
-def moe_select_block_m(T, top_k, num_experts):
+def moe_select_block_m(T, top_k, num_experts, dtype="fp8_blockwise", K=4096):
     out = _I32()
-    _check(lib().moe_select_block_m(T, top_k, num_experts, ctypes.byref(out)))
+    _check(lib().moe_select_block_m(_DTYPE_CODE.get(dtype, dtype), T, K, top_k, num_experts,
+                                    ctypes.byref(out)))
     return out.value
 
 
@@ -221,7 +222,7 @@ def run_case(case, block_m=None, split=-1, stream=None, workspace=None, out=None
     Returns (out, (sorted_token_ids, expert_ids, num_tokens_post_padded))."""
     T = case.x.shape[0]
     if block_m is None:
-        block_m = moe_select_block_m(T, case.top_k, case.E)
+        block_m = moe_select_block_m(T, case.top_k, case.E, case.kind, case.x.shape[1])
     align = moe_align(case.topk_ids, case.E, block_m, stream=stream, out=align_out)
     args = dict(top_k=case.top_k, block_m=block_m, split=split, out=out, workspace=workspace,
                 stream=stream)

@@ -30,7 +30,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128; }
+bool valid_block_m(int32_t bm) {
+  return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256;
+}
 
 int check_routes(int64_t T, int32_t top_k, int32_t E) {
   if (T < 0) return fail(MOE_ERR_SHAPE, "T must be >= 0 (got %lld)", (long long)T);
@@ -59,7 +61,9 @@ int check_ffn(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
   if ((N / 2) % 128)
     return fail(MOE_ERR_UNSUPPORTED, "I = N/2 must be a multiple of 128 (got %lld)", (long long)(N / 2));
   if (!valid_block_m(block_m))
-    return fail(MOE_ERR_UNSUPPORTED, "block_m must be 16, 32, 64 or 128 (got %d)", block_m);
+    return fail(MOE_ERR_UNSUPPORTED, "block_m must be 16, 32, 64, 128 or 256 (got %d)", block_m);
+  if (block_m == 256 && (dtype == MOE_BF16 || K % 256))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m 256 needs an e4m3 dtype and K %% 256 == 0");
   // 32-bit offsets inside one expert's weights and element indices of out
   if (N * K >= (int64_t(1) << 31) || T * K >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "per-expert weight or output element count must be < 2^31");
@@ -72,7 +76,8 @@ int check_ffn(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
 
 int pick_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
                int32_t block_m) {
-  (void)dtype; (void)K; (void)N; (void)E; (void)block_m;
+  (void)dtype; (void)K; (void)N; (void)E;
+  if (block_m == 256) return 1;
   // The fused mode's split-K accumulation costs R*K*(I/128) fp32 atomic adds;
   // it stays cheap against the weight stream only for decode-sized calls.
   return (T * top_k <= 512) ? 0 : 1;
@@ -119,6 +124,8 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
   int rc = check_ffn(dtype, T, K, N, E, top_k, block_m);
   if (rc) return rc;
   if (split < -1 || split > 1) return fail(MOE_ERR_UNSUPPORTED, "split must be -1, 0 or 1");
+  if (block_m == 256 && split == 0)
+    return fail(MOE_ERR_UNSUPPORTED, "block_m 256 runs the split mode only");
   if (T == 0) return ok();
   if (!x || !w1 || !w2 || !sorted || !expert_ids || !ntp || !topk_w || !out)
     return fail(MOE_ERR_NULL, "a required pointer is NULL");
@@ -182,7 +189,7 @@ int moe_align_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m, int
   int rc = check_routes(T, top_k, E);
   if (rc) return rc;
   if (!valid_block_m(block_m))
-    return fail(MOE_ERR_UNSUPPORTED, "block_m must be 16, 32, 64 or 128 (got %d)", block_m);
+    return fail(MOE_ERR_UNSUPPORTED, "block_m must be 16, 32, 64, 128 or 256 (got %d)", block_m);
   capacity(T, top_k, E, block_m, sorted_cap, blocks_cap);
   return ok();
 }
@@ -224,7 +231,8 @@ int moe_select_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, 
   return ok();
 }
 
-int moe_select_block_m(int64_t T, int32_t top_k, int32_t E, int32_t* block_m) {
+int moe_select_block_m(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32_t E,
+                       int32_t* block_m) {
   if (!block_m) return fail(MOE_ERR_NULL, "block_m is NULL");
   int rc = check_routes(T, top_k, E);
   if (rc) return rc;
@@ -232,7 +240,10 @@ int moe_select_block_m(int64_t T, int32_t top_k, int32_t E, int32_t* block_m) {
   const int64_t R = T * top_k;
   const int64_t act = R < E ? (R > 0 ? R : 1) : E;
   const double per = (double)R / (double)act;
-  *block_m = per <= 16 ? 16 : per <= 48 ? 32 : per <= 160 ? 64 : 128;
+  // the 256-row tile pays off where the MFMA applies the scales itself; the
+  // blockwise path's per-step promotion does not fit its register budget
+  const bool big_ok = dtype == MOE_MXFP8 && K % 256 == 0;
+  *block_m = per <= 16 ? 16 : per <= 48 ? 32 : per <= 160 ? 64 : (per <= 200 || !big_ok) ? 128 : 256;
   return ok();
 }
 

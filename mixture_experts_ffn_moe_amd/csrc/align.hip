@@ -28,6 +28,7 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
+constexpr int kBatch = 8;
 
 __global__ void __launch_bounds__(kThreads)
 k_align(const int32_t* __restrict__ ids, int R, int E, int bm, int32_t* __restrict__ sorted,
@@ -45,9 +46,18 @@ k_align(const int32_t* __restrict__ ids, int R, int E, int bm, int32_t* __restri
 
   const int seg = (R + kWaves - 1) / kWaves;
   const int lo = min(R, w * seg), hi = min(R, lo + seg);
-  for (int i = lo + lane; i < hi; i += 64) {
-    const int e = ids[i];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[w * E + e], 1);
+  // ids are read kBatch chunks of 64 at a time so that the global loads
+  // overlap instead of costing one memory latency per chunk
+  for (int base = lo; base < hi; base += 64 * kBatch) {
+    int eb[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = base + u * 64 + lane;
+      eb[u] = i < hi ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if ((unsigned)eb[u] < (unsigned)E) atomicAdd(&cnt[w * E + eb[u]], 1);
   }
   __syncthreads();
 
@@ -100,26 +110,35 @@ k_align(const int32_t* __restrict__ ids, int R, int E, int bm, int32_t* __restri
   if (tid == 0) *ntp_out = ntp;
   __syncthreads();
 
-  // stable scatter
+  // stable scatter, chunks of 64 ids in order, kBatch chunks loaded at once
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const int e = (i < hi) ? ids[i] : -1;
-    const bool ok = (unsigned)e < (unsigned)E;
-    unsigned long long peers = __ballot(ok);
-    for (int bit = 0; (1 << bit) < E; ++bit) {
-      const bool set = (e >> bit) & 1;
-      const unsigned long long m = __ballot(ok && set);
-      peers &= set ? m : ~m;
+  for (int base0 = lo; base0 < hi; base0 += 64 * kBatch) {
+    int eb[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = base0 + u * 64 + lane;
+      eb[u] = i < hi ? ids[i] : -1;
     }
-    if (ok) {
-      const int rank = __popcll(peers & below);
-      const int slot = cnt[w * E + e] + rank;
-      sorted[slot] = i;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = base0 + u * 64 + lane;
+      const int e = eb[u];
+      const bool ok = (unsigned)e < (unsigned)E;
+      unsigned long long peers = __ballot(ok);
+      for (int bit = 0; (1 << bit) < E; ++bit) {
+        const bool set = (e >> bit) & 1;
+        const unsigned long long m = __ballot(ok && set);
+        peers &= set ? m : ~m;
+      }
+      if (ok) {
+        const int rank = __popcll(peers & below);
+        const int cur = cnt[w * E + e];
+        sorted[cur + rank] = i;
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 63 - __clzll(peers)) cnt[w * E + e] = cur + __popcll(peers);
+      }
       __builtin_amdgcn_wave_barrier();
-      if (lane == 63 - __clzll(peers)) cnt[w * E + e] = slot + 1 - rank + __popcll(peers) - 1;
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 

@@ -636,10 +636,26 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
   return hipGetLastError();
 }
 
+// block_m 256 exists only as the LDS-tiled split mode (e4m3, K % 256 == 0)
+template <int KIND>
+hipError_t launch_tiled_only(const MoeArgs& a, hipStream_t st, const TimingHook& hk) {
+  if (!tiled_supported(KIND, 256, a.K, a.I)) return hipErrorInvalidValue;
+  const size_t R = (size_t)a.T * a.top_k;
+  const size_t fbytes = (R * 4 + 15) / 16;
+  hipLaunchKernelGGL(k_zero, dim3(grid_for(fbytes, 256)), dim3(256), 0, st,
+                     reinterpret_cast<uint4*>(a.flags), fbytes);
+  hipError_t e = launch_tiled(KIND, 256, a, st, hk);
+  if (e != hipSuccess) return e;
+  const int CT = (a.K + 1023) / 1024;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int KIND>
 hipError_t launch_kind(int block_m, int split, const MoeArgs& a, hipStream_t st,
                        const TimingHook& hk) {
   switch (block_m) {
+    case 256: return launch_tiled_only<KIND>(a, st, hk);
     case 16: return launch_kind_bm<KIND, 16>(split, a, st, hk);
     case 32: return launch_kind_bm<KIND, 32>(split, a, st, hk);
     case 64: return launch_kind_bm<KIND, 64>(split, a, st, hk);

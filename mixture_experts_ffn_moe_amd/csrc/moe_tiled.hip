@@ -75,20 +75,24 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 
 template <int KIND, int BM, int BN, int NS>
 struct TileCfg {
-  static constexpr int WM = BM / 64;         // wave rows
-  static constexpr int WN = 4 / WM;          // wave columns
-  static constexpr int MI = 4;               // 16-row subtiles per wave
-  static constexpr int NI = BN / WN / 16;    // 16-column subtiles per wave
+  static constexpr int NW = BM == 256 ? 8 : 4;  // waves per workgroup
+  static constexpr int WM = BM / 64;            // wave rows (64 rows each)
+  static constexpr int WN = NW / WM;            // wave columns
+  static constexpr int MI = 4;                  // 16-row subtiles per wave
+  static constexpr int NI = BN / WN / 16;       // 16-column subtiles per wave
   static constexpr int A_BYTES = BM * kRowBytes;
   static constexpr int B_BYTES = BN * kRowBytes;
   static constexpr int SA_BYTES = BM * 4;                         // fp32 or 4 x e8m0 per row
   static constexpr int SB_BYTES = (KIND == KIND_MX) ? BN * 4 : 0;  // MX weight scales
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-  static constexpr int A_INSTR = A_BYTES / 1024 / 4;  // 16-byte DMA instructions per wave
-  static constexpr int B_INSTR = B_BYTES / 1024 / 4;
+  static constexpr int A_INSTR = A_BYTES / 1024 / NW;  // 16-byte DMA instructions per wave
+  static constexpr int B_INSTR = B_BYTES / 1024 / NW;
+  static constexpr int SA_ROWS = BM / NW;              // scale rows staged per wave
+  static constexpr int SB_ROWS = BN / NW;
   static constexpr int S_INSTR = 1 + ((KIND == KIND_MX) ? 1 : 0);
   static constexpr int LOADS = A_INSTR + B_INSTR + S_INSTR;  // per wave per stage
-  static constexpr int LDS = NS * STAGE;
+  static constexpr int THREADS = NW * 64;
+  static_assert(SA_ROWS <= 64 && SB_ROWS <= 64, "one scale instruction per wave");
 };
 
 // Operand sources of one tile GEMM.
@@ -113,29 +117,31 @@ __device__ __forceinline__ void tile_load(const TileSrc& src, uint8_t* lds, int 
   uint8_t* stage = lds + st * C::STAGE;
   const uint32_t soff = (uint32_t)ks * kRowBytes;
 #pragma unroll
-  for (int t = 0; t < C::A_INSTR; ++t) dma16(src.ra, stage + (w + 4 * t) * 1024, a_off[t], soff);
+  for (int t = 0; t < C::A_INSTR; ++t)
+    dma16(src.ra, stage + (w + C::NW * t) * 1024, a_off[t], soff);
 #pragma unroll
   for (int t = 0; t < C::B_INSTR; ++t)
-    dma16(src.rb, stage + C::A_BYTES + (w + 4 * t) * 1024, b_off[t], soff);
-  // row scales: wave w covers rows [w * BM / 4, (w + 1) * BM / 4)
-  if (lane < BM / 4)
-    dma4(src.rsa, stage + C::A_BYTES + C::B_BYTES + w * BM, sa_off, (uint32_t)ks * sa_step);
-  if constexpr (KIND == KIND_MX)
-    dma4(src.rsb, stage + C::A_BYTES + C::B_BYTES + C::SA_BYTES + w * (BN / 4) * 4, sb_off,
-         (uint32_t)ks * 4);
-  (void)lane;
+    dma16(src.rb, stage + C::A_BYTES + (w + C::NW * t) * 1024, b_off[t], soff);
+  // row scales: wave w covers rows [w * SA_ROWS, (w + 1) * SA_ROWS)
+  if (lane < C::SA_ROWS)
+    dma4(src.rsa, stage + C::A_BYTES + C::B_BYTES + w * C::SA_ROWS * 4, sa_off,
+         (uint32_t)ks * sa_step);
+  if constexpr (KIND == KIND_MX) {
+    if (lane < C::SB_ROWS)
+      dma4(src.rsb, stage + C::A_BYTES + C::B_BYTES + C::SA_BYTES + w * C::SB_ROWS * 4, sb_off,
+           (uint32_t)ks * 4);
+  }
 }
 
 // Per-lane DMA offsets of the A and B tiles: lane slot (w + 4t) * 64 + lane
 // holds row slot / 8, physical chunk slot % 8, which carries logical chunk
 // (slot % 8) ^ swz(row).
-template <int NT>
+template <int NW>
 __device__ __forceinline__ void dma_rows(int t_idx, int& row, int& qchunk) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int slot = (w + 4 * t_idx) * 64 + lane;
+  const int slot = (w + NW * t_idx) * 64 + lane;
   row = slot / kChunks;
   qchunk = (slot % kChunks) ^ swz(row);
-  (void)NT;
 }
 
 // Fragment of row `row` (tile-relative) from a staged tile at `base`.
@@ -180,17 +186,14 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) lds_frag(fa[mi], ta, wm * 64 + mi * 16 + r16, g);
   if constexpr (KIND == KIND_FP8B) {
-    float cs[MI][4], cs2[MI][4];
+    float sa[MI][4];
     const float s1 = sc1.at(ks);
     const float s2 = sc2.at(ks);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const float sa = reinterpret_cast<const float*>(tsa)[wm * 64 + mi * 16 + 4 * g + i4];
-        cs[mi][i4] = sa * s1;
-        cs2[mi][i4] = sa * s2;
-      }
+      for (int i4 = 0; i4 < 4; ++i4)
+        sa[mi][i4] = reinterpret_cast<const float*>(tsa)[wm * 64 + mi * 16 + 4 * g + i4];
     // MFMAs of subtile column ni go into their own temporaries and are
     // promoted one column later, so the MFMA pipe never waits on a
     // promotion (the tile products are independent of each other).
@@ -211,13 +214,23 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
       for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4)
-          acc[mi][ni][i4] += tt[mi][i4] * (ni < up_split ? cs[mi][i4] : cs2[mi][i4]);
+          acc[mi][ni][i4] += tt[mi][i4] * (sa[mi][i4] * (ni < up_split ? s1 : s2));
     };
-    issue(0, t[0]);
+    if constexpr (C::NW == 8) {
+      // two waves share each SIMD and fill each other's MFMA gaps; no
+      // lookahead, which keeps the wave within 256 registers
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      if (ni + 1 < NI) issue(ni + 1, t[(ni + 1) & 1]);
-      promote(ni, t[ni & 1]);
+      for (int ni = 0; ni < NI; ++ni) {
+        issue(ni, t[0]);
+        promote(ni, t[0]);
+      }
+    } else {
+      issue(0, t[0]);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        if (ni + 1 < NI) issue(ni + 1, t[(ni + 1) & 1]);
+        promote(ni, t[ni & 1]);
+      }
     }
   } else {  // MX
     int xa[MI];
@@ -244,18 +257,18 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
 }
 
 // One workgroup tile: acc[mi][ni] over all K steps, visiting the steps from
-// a staggered start, three stages in flight in three distinct LDS arrays (the
-// loop is unrolled by three so every LDS access names its array).
+// a staggered start, NS stages in flight in NS distinct LDS arrays (the loop
+// is unrolled by NS so every LDS access names its array and the compiler can
+// tell the stage being read from the stages being filled).
 template <int KIND, int BM, int BN, int NS>
-__device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* s0, uint8_t* s1,
-                                          uint8_t* s2, int ksteps,
+__device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* const (&stg)[NS], int ksteps,
                                           const uint32_t (&a_off)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
                                           uint32_t sa_off, uint32_t sa_step,
                                           const uint32_t (&b_off)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
                                           uint32_t sb_off, int up_split, int group,
                                           f32x4 (&acc)[4][TileCfg<KIND, BM, BN, NS>::NI]) {
   using C = TileCfg<KIND, BM, BN, NS>;
-  static_assert(NS == 3, "three pipeline stages");
+  static_assert(NS == 2 || NS == 3, "two or three pipeline stages");
   constexpr int MI = C::MI, NI = C::NI;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -266,30 +279,32 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* s0, uint8
     sc1.load(src.bsc, ksteps);
     sc2.load(src.bsc2 ? src.bsc2 : src.bsc, ksteps);
   }
-  // All tiles of one expert (its blocks x slices) start at the same step, so
-  // the tiles that share activation rows (slices of a block) or weight rows
-  // (blocks of an expert) walk K in step and share them in L2; different
-  // experts start at different steps, which spreads the rows being read over
-  // the HBM channels.
+  // Tiles that read the same weight rows (the blocks of one expert, for one
+  // slice or column tile) start at the same step and walk K in step, sharing
+  // those rows in L2.  Tiles reading other weight rows start elsewhere:
+  // thousands of rows 4 KiB apart read at one offset at once would
+  // concentrate the traffic on a few HBM channels.  The activation rows a
+  // block shares across its slices stay in L2 without lockstep (0.5 MiB per
+  // block).
   const int rot = (int)((((uint32_t)group * 2654435761u) >> 16) % (uint32_t)ksteps);
   auto step_at = [&](int i) { const int k = i + rot; return k >= ksteps ? k - ksteps : k; };
   auto load = [&](uint8_t* st, int i) {
     tile_load<KIND, BM, BN, NS>(src, st, 0, step_at(i), a_off, sa_off, sa_step, b_off, sb_off);
   };
-  load(s0, 0);
-  if (ksteps > 1) load(s1, 1);
-  for (int i0 = 0; i0 < ksteps; i0 += 3) {
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
+  for (int u = 0; u < NS - 1; ++u)
+    if (u < ksteps) load(stg[u], u);
+  for (int i0 = 0; i0 < ksteps; i0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
       const int i = i0 + u;
       if (i < ksteps) {
-        // stage i has landed once only stage i+1's loads may still be pending
-        if (i + 1 < ksteps) wait_vmcnt<C::LOADS>();
+        // stage i has landed once only the later stages' loads may be pending
+        if (i + NS - 2 < ksteps) wait_vmcnt<C::LOADS * (NS - 2)>();
         else wait_vmcnt<0>();
         lds_barrier();
-        if (i + 2 < ksteps) load(u == 0 ? s2 : u == 1 ? s0 : s1, i + 2);
-        tile_step<KIND, BM, BN, NS>(u == 0 ? s0 : u == 1 ? s1 : s2, step_at(i), sc1, sc2,
-                                    up_split, acc);
+        if (i + NS - 1 < ksteps) load(stg[(u + NS - 1) % NS], i + NS - 1);
+        tile_step<KIND, BM, BN, NS>(stg[u], step_at(i), sc1, sc2, up_split, acc);
       }
     }
   }
@@ -300,12 +315,12 @@ __device__ __forceinline__ int token_of(int id, int top_k) { return id >= 0 ? id
 
 // gate/up GEMM + SwiGLU + requantization, one (block, 128-wide slice) tile
 template <int KIND, int BM, int NS>
-__global__ void __launch_bounds__(256) k_up_t(MoeArgs p) {
+__global__ void __launch_bounds__(BM == 256 ? 512 : 256) k_up_t(MoeArgs p) {
   using C = TileCfg<KIND, BM, 256, NS>;
   constexpr int MI = C::MI, NI = C::NI, HALF = NI / 2;
   __shared__ __attribute__((aligned(1024))) uint8_t s0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t s1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t s2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[NS > 2 ? C::STAGE : 16];
   __shared__ int ids[BM];
   __shared__ float lds_amax[C::WN * BM];
   const int S = p.I / 128;
@@ -328,17 +343,17 @@ __global__ void __launch_bounds__(256) k_up_t(MoeArgs p) {
 #pragma unroll
   for (int t = 0; t < C::A_INSTR; ++t) {
     int row, q;
-    dma_rows<0>(t, row, q);
+    dma_rows<C::NW>(t, row, q);
     a_off[t] = (uint32_t)token_of(ids[row], p.top_k) * K + q * 16;
   }
 #pragma unroll
   for (int t = 0; t < C::B_INSTR; ++t) {
     int row, q;
-    dma_rows<0>(t, row, q);  // rows [0,128): gate slice rows; [128,256): up slice rows
+    dma_rows<C::NW>(t, row, q);  // rows [0,128): gate slice rows; [128,256): up slice rows
     const int n = (row < 128 ? s * 128 + row : I + s * 128 + row - 128);
     b_off[t] = (uint32_t)n * K + q * 16;
   }
-  const int srow = wid * (BM / 4) + lane;  // scale row this lane stages
+  const int srow = wid * C::SA_ROWS + lane;  // scale row this lane stages
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
   if constexpr (KIND == KIND_FP8B) {
     src.rsa = make_rsrc(p.xs, (uint32_t)((size_t)p.T * KS * 4));
@@ -350,15 +365,17 @@ __global__ void __launch_bounds__(256) k_up_t(MoeArgs p) {
     sa_off = (uint32_t)token_of(ids[srow < BM ? srow : 0], p.top_k) * (K / 32);
     src.rsb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w1s) + (size_t)e * N * (K / 32),
                         (uint32_t)((size_t)N * (K / 32)));
-    const int brow = wid * 64 + lane;  // B scale row this lane stages
+    const int brow = wid * C::SB_ROWS + lane;  // B scale row this lane stages
     const int n = (brow < 128 ? s * 128 + brow : I + s * 128 + brow - 128);
     sb_off = (uint32_t)n * (K / 32);
     src.bsc = nullptr;
     src.bsc2 = nullptr;
   }
   f32x4 acc[MI][NI];
-  tile_gemm<KIND, BM, 256, NS>(src, s0, s1, s2, KS, a_off, sa_off, sa_step, b_off, sb_off, HALF,
-                               e, acc);
+  uint8_t* const stg3[3] = {s0, s1, s2};
+  uint8_t* const (&stg)[NS] = *reinterpret_cast<uint8_t* const (*)[NS]>(&stg3);
+  tile_gemm<KIND, BM, 256, NS>(src, stg, KS, a_off, sa_off, sa_step, b_off, sb_off, HALF,
+                               e * 64 + s, acc);
 
   // SwiGLU: gate subtile j pairs with up subtile HALF + j (same columns)
   float h[MI][HALF][4];
@@ -426,7 +443,7 @@ __global__ void __launch_bounds__(256) k_up_t(MoeArgs p) {
   }
   __syncthreads();
   // coalesced store of the slice: each thread writes 16-byte row chunks
-  for (int c = threadIdx.x; c < BM * 8; c += 256) {
+  for (int c = threadIdx.x; c < BM * 8; c += C::THREADS) {
     const int row = c / 8, ch = c % 8;
     *reinterpret_cast<uint4*>(p.hq + (pos0 + row) * I + s * 128 + ch * 16) =
         *reinterpret_cast<const uint4*>(q + row * QROW + ch * 16);
@@ -439,12 +456,12 @@ __global__ void __launch_bounds__(256) k_up_t(MoeArgs p) {
 
 // down GEMM, one (block, 256 output columns) tile, fp32 per-route rows
 template <int KIND, int BM, int NS>
-__global__ void __launch_bounds__(256) k_down_t(MoeArgs p) {
+__global__ void __launch_bounds__(BM == 256 ? 512 : 256) k_down_t(MoeArgs p) {
   using C = TileCfg<KIND, BM, 256, NS>;
   constexpr int MI = C::MI, NI = C::NI;
   __shared__ __attribute__((aligned(1024))) uint8_t s0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t s1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t s2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t s2[NS > 2 ? C::STAGE : 16];
   __shared__ int ids[BM];
   const int K = p.K, I = p.I, IS = I / 128;
   const int NT = K / 256;
@@ -466,16 +483,16 @@ __global__ void __launch_bounds__(256) k_down_t(MoeArgs p) {
 #pragma unroll
   for (int t = 0; t < C::A_INSTR; ++t) {
     int row, q;
-    dma_rows<0>(t, row, q);
+    dma_rows<C::NW>(t, row, q);
     a_off[t] = (uint32_t)((size_t)b * BM + row) * I + q * 16;
   }
 #pragma unroll
   for (int t = 0; t < C::B_INSTR; ++t) {
     int row, q;
-    dma_rows<0>(t, row, q);
+    dma_rows<C::NW>(t, row, q);
     b_off[t] = (uint32_t)(ct * 256 + row) * I + q * 16;
   }
-  const int srow = wid * (BM / 4) + lane;
+  const int srow = wid * C::SA_ROWS + lane;
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
   const int c0 = ct * 256 + wn * (256 / C::WN);  // this wave's first output column
   if constexpr (KIND == KIND_FP8B) {
@@ -488,14 +505,16 @@ __global__ void __launch_bounds__(256) k_down_t(MoeArgs p) {
     sa_off = (uint32_t)((size_t)b * BM + (srow < BM ? srow : 0)) * (I / 32);
     src.rsb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w2s) + (size_t)e * K * (I / 32),
                         (uint32_t)((size_t)K * (I / 32)));
-    sb_off = (uint32_t)(ct * 256 + wid * 64 + lane) * (I / 32);
+    sb_off = (uint32_t)(ct * 256 + (wid * C::SB_ROWS + lane) % 256) * (I / 32);
     src.bsc = nullptr;
     src.bsc2 = nullptr;
   }
   f32x4 acc[MI][NI];
   // all NI subtiles of a wave are contiguous output columns (no gate/up split)
-  tile_gemm<KIND, BM, 256, NS>(src, s0, s1, s2, IS, a_off, sa_off, sa_step, b_off, sb_off, NI, e,
-                               acc);
+  uint8_t* const stg3[3] = {s0, s1, s2};
+  uint8_t* const (&stg)[NS] = *reinterpret_cast<uint8_t* const (*)[NS]>(&stg3);
+  tile_gemm<KIND, BM, 256, NS>(src, stg, IS, a_off, sa_off, sa_step, b_off, sb_off, NI,
+                               e * 64 + ct, acc);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -509,15 +528,16 @@ __global__ void __launch_bounds__(256) k_down_t(MoeArgs p) {
 
 template <int KIND, int BM>
 hipError_t launch_tiled_kind(const MoeArgs& a, hipStream_t st, const TimingHook& hk) {
-  constexpr int NS = 3;
+  constexpr int NS = BM == 256 ? 2 : 3;
+  constexpr int TH = TileCfg<KIND, BM, 256, NS>::THREADS;
   const int S = a.I / 128;
   const unsigned g_up = (unsigned)(((size_t)a.blocks_cap * S + 7) / 8 * 8);
   const unsigned g_dn = (unsigned)(((size_t)a.blocks_cap * (a.K / 256) + 7) / 8 * 8);
   if (hk.which == 1 && hk.before) hipEventRecord(hk.before, st);
-  hipLaunchKernelGGL((k_up_t<KIND, BM, NS>), dim3(g_up), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_up_t<KIND, BM, NS>), dim3(g_up), dim3(TH), 0, st, a);
   if (hk.which == 1 && hk.after) hipEventRecord(hk.after, st);
   if (hk.which == 2 && hk.before) hipEventRecord(hk.before, st);
-  hipLaunchKernelGGL((k_down_t<KIND, BM, NS>), dim3(g_dn), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_down_t<KIND, BM, NS>), dim3(g_dn), dim3(TH), 0, st, a);
   if (hk.which == 2 && hk.after) hipEventRecord(hk.after, st);
   return hipGetLastError();
 }
@@ -525,16 +545,18 @@ hipError_t launch_tiled_kind(const MoeArgs& a, hipStream_t st, const TimingHook&
 }  // namespace
 
 bool tiled_supported(int kind, int block_m, int K, int I) {
-  return (kind == KIND_FP8B || kind == KIND_MX) && (block_m == 64 || block_m == 128) &&
-         K % 256 == 0 && I % 128 == 0;
+  return (kind == KIND_FP8B || kind == KIND_MX) &&
+         (block_m == 64 || block_m == 128 || block_m == 256) && K % 256 == 0 && I % 128 == 0;
 }
 
 hipError_t launch_tiled(int kind, int block_m, const MoeArgs& a, hipStream_t st,
                         const TimingHook& hk) {
   if (kind == KIND_FP8B) {
+    if (block_m == 256) return launch_tiled_kind<KIND_FP8B, 256>(a, st, hk);
     if (block_m == 128) return launch_tiled_kind<KIND_FP8B, 128>(a, st, hk);
     return launch_tiled_kind<KIND_FP8B, 64>(a, st, hk);
   }
+  if (block_m == 256) return launch_tiled_kind<KIND_MX, 256>(a, st, hk);
   if (block_m == 128) return launch_tiled_kind<KIND_MX, 128>(a, st, hk);
   return launch_tiled_kind<KIND_MX, 64>(a, st, hk);
 }

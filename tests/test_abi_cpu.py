@@ -39,7 +39,7 @@ def test_capacity_closed_form():
 
 @pytest.mark.parametrize("args,status", [
     ((-1, 2, 8, 16), -2), ((4, 0, 8, 16), -2), ((4, 2, 0, 16), -2),
-    ((4, 2, 8, 48), -3), ((1 << 29, 8, 8, 16), -2)])
+    ((4, 2, 8, 48), -3), ((4, 2, 8, 512), -3), ((1 << 29, 8, 8, 16), -2)])
 def test_capacity_errors(args, status):
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_align_capacity(*args)
@@ -76,6 +76,11 @@ def test_ffn_errors_before_launch(fn):
     assert _ffn(L, fn, N=4095) == -2                    # odd N
     assert _ffn(L, fn, N=4096 + 128) == -3              # I % 128
     assert _ffn(L, fn, bm=24) == -3                     # block_m
+    if fn == "fused_moe_bf16":
+        assert _ffn(L, fn, bm=256) == -3                # 256 is e4m3-only
+    else:
+        assert _ffn(L, fn, bm=256, K=384 * 2 + 128) == -3   # 256 needs K % 256 == 0
+        assert _ffn(L, fn, bm=256, split=0) == -3       # 256 runs the split mode only
     assert _ffn(L, fn, T=-1) == -2
     assert _ffn(L, fn, k=0) == -2
     assert _ffn(L, fn, split=2) == -3
@@ -102,6 +107,10 @@ def test_workspace_sizes_grow_with_tokens():
 
 def test_heuristics():
     assert moe.moe_select_block_m(8, 6, 256) == 16
-    assert moe.moe_select_block_m(8192, 8, 288) == 128
+    assert moe.moe_select_block_m(8192, 8, 288, "fp8_blockwise", 4096) == 128
+    assert moe.moe_select_block_m(8192, 8, 288, "mxfp8", 4096) == 256
+    assert moe.moe_select_block_m(8192, 8, 288, "mxfp8", 4096 + 128) == 128
+    assert moe.moe_select_block_m(8192, 8, 288, "bf16", 4096) == 128
+    assert moe.moe_select_block_m(4096, 8, 288, "fp8_blockwise", 4096) == 64
     assert moe.moe_select_split("fp8_blockwise", 8, 4096, 4096, 256, 6, 16) == 0
     assert moe.moe_select_split("fp8_blockwise", 8192, 4096, 4096, 288, 8, 128) == 1

@@ -40,7 +40,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("kind,T,E,k", CASES)
 def test_align_bit_exact(kind, T, E, k, bm):
     say(f"[gpu] align kind={kind} T={T} E={E} k={k} bm={bm}")

@@ -182,7 +182,7 @@ def test_many_routes_fused_atomics():
     check(c, 64, 1, label="split many routes")
 
 
-@pytest.mark.parametrize("bm", [64, 128])
+@pytest.mark.parametrize("bm", [64, 128, 256])
 @pytest.mark.parametrize("kind,K,I", [("fp8_blockwise", 768, 384), ("mxfp8", 512, 256),
                                       ("fp8_blockwise", 256, 128)])
 def test_tiled_split_parity(kind, K, I, bm):
@@ -197,7 +197,8 @@ def test_tiled_split_parity(kind, K, I, bm):
 def test_tiled_deterministic():
     c = to_gpu(datagen.make_case("fp8_blockwise", 500, 512, 256, 4, 2, routing="normal",
                                  tag="tiled-det"))
-    a, _ = moe.run_case(c, block_m=128, split=1)
-    b, _ = moe.run_case(c, block_m=128, split=1)
-    torch.cuda.synchronize()
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for bm in (128, 256):
+        a, _ = moe.run_case(c, block_m=bm, split=1)
+        b, _ = moe.run_case(c, block_m=bm, split=1)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))

@@ -39,7 +39,7 @@ def test_golden():
         assert n == case["num_tokens_post_padded"]
 
 
-@pytest.mark.parametrize("bm", [16, 32, 64, 128])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("T,E,k,mode", [
     (0, 8, 2, "uniform"), (1, 8, 2, "uniform"), (37, 8, 2, "uniform"),
     (64, 256, 6, "uniform"), (200, 16, 4, "one"), (128, 4, 1, "multiple"),
