@@ -35,16 +35,49 @@ constexpr int kChunks = 8;      // 16-byte chunks per row
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-typedef __attribute__((address_space(3))) void lds_void;
+typedef int desc_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void* lds_wave_base,
-                                      uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 16, (int)voff, (int)soff, 0, 0);
+// Raw buffer descriptor: base address, no stride, `bytes` records (loads past
+// them return zeros), 32-bit data format.
+__device__ __forceinline__ desc_t make_desc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return desc_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
+                __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
 
-__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, const void* lds_wave_base,
-                                     uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_wave_base, 4, (int)voff, (int)soff, 0, 0);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p);
+}
+
+// Direct-to-LDS buffer loads: lane L's bytes land at M0 + L * size.  They are
+// issued from asm so that the only waits on them are the explicit vmcnt waits
+// of the pipeline: the compiler cannot always tell which LDS stage such a
+// load writes and would otherwise wait for every load in flight before an LDS
+// read.  They have no destination register; VMEM loads complete in order, so
+// the compiler's own vmcnt waits stay correct (at worst stricter).  M0 is set
+// in the same statement; the compiler sets it right before each of its own
+// uses.
+// The scalar operands pass through readfirstlane: the compiler may hold a
+// wave-uniform value in a vector register, which an "s" operand cannot take
+// (the read folds away for values already in scalar registers).
+__device__ __forceinline__ void dma16(desc_t r, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
+}
+
+__device__ __forceinline__ void dma4(desc_t r, uint32_t m0, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r),
+                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
+}
+
+// Wave index as a wave-uniform (scalar) value, so that addresses derived from
+// it (LDS stage offsets for M0, row bases) stay in scalar registers.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
 // s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt in bits 3:0 and 15:14), other counters untouched
@@ -82,8 +115,10 @@ struct TileCfg {
   static constexpr int NI = BN / WN / 16;       // 16-column subtiles per wave
   static constexpr int A_BYTES = BM * kRowBytes;
   static constexpr int B_BYTES = BN * kRowBytes;
-  static constexpr int SA_BYTES = BM * 4;                         // fp32 or 4 x e8m0 per row
-  static constexpr int SB_BYTES = (KIND == KIND_MX) ? BN * 4 : 0;  // MX weight scales
+  // Row scales (fp32, or 4 x e8m0 per row): each wave stages SA_ROWS rows in
+  // 64 four-byte slots (every lane loads; the slots past SA_ROWS are padding).
+  static constexpr int SA_BYTES = NW * 256;
+  static constexpr int SB_BYTES = (KIND == KIND_MX) ? NW * 256 : 0;  // MX weight scales
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
   static constexpr int A_INSTR = A_BYTES / 1024 / NW;  // 16-byte DMA instructions per wave
   static constexpr int B_INSTR = B_BYTES / 1024 / NW;
@@ -97,40 +132,37 @@ struct TileCfg {
 
 // Operand sources of one tile GEMM.
 struct TileSrc {
-  __amdgpu_buffer_rsrc_t ra, rb, rsa, rsb;
+  desc_t ra, rb, rsa, rsb;
   const float* bsc;  // FP8B: weight block-scale row of the wave's n-block (index: step)
   const float* bsc2; // FP8B k_up_t: the up half's block-scale row
 };
 
-// Issue the DMA loads of K step `ks` into stage slot `st`.
-//  a_off[t]: byte offset of A row (w + 4t) * 8 + lane / 8 (t < A_INSTR)
-//  sa_off : byte offset of this lane's scale row (lane < BM / 4 active)
-//  b_row0 : B row index base; B rows are b_base + row * b_stride
+// Issue the DMA loads of K step `ks` into stage slot `st` of the pipeline
+// area at LDS address `lds` (a wave-uniform byte address).
+//  a_off[t] / b_off[t]: this lane's byte offsets of its A / B chunks (t-th load)
+//  sa_off / sb_off    : this lane's scale row offsets; sa_step bytes per step
 template <int KIND, int BM, int BN, int NS>
-__device__ __forceinline__ void tile_load(const TileSrc& src, uint8_t* lds, int st, int ks,
+__device__ __forceinline__ void tile_load(const TileSrc& src, uint32_t lds, int st, int ks,
                                           const uint32_t (&a_off)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
                                           uint32_t sa_off, uint32_t sa_step,
                                           const uint32_t (&b_off)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
                                           uint32_t sb_off) {
   using C = TileCfg<KIND, BM, BN, NS>;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint8_t* stage = lds + st * C::STAGE;
+  const uint32_t w = (uint32_t)wave_id();
+  const uint32_t stage = lds + (uint32_t)(st * C::STAGE);
   const uint32_t soff = (uint32_t)ks * kRowBytes;
 #pragma unroll
-  for (int t = 0; t < C::A_INSTR; ++t)
-    dma16(src.ra, stage + (w + C::NW * t) * 1024, a_off[t], soff);
+  for (int t = 0; t < C::A_INSTR; ++t) dma16(src.ra, stage + (w + C::NW * t) * 1024, a_off[t], soff);
 #pragma unroll
   for (int t = 0; t < C::B_INSTR; ++t)
     dma16(src.rb, stage + C::A_BYTES + (w + C::NW * t) * 1024, b_off[t], soff);
-  // row scales: wave w covers rows [w * SA_ROWS, (w + 1) * SA_ROWS)
-  if (lane < C::SA_ROWS)
-    dma4(src.rsa, stage + C::A_BYTES + C::B_BYTES + w * C::SA_ROWS * 4, sa_off,
-         (uint32_t)ks * sa_step);
-  if constexpr (KIND == KIND_MX) {
-    if (lane < C::SB_ROWS)
-      dma4(src.rsb, stage + C::A_BYTES + C::B_BYTES + C::SA_BYTES + w * C::SB_ROWS * 4, sb_off,
-           (uint32_t)ks * 4);
-  }
+  // row scales: wave w stages rows [w * SA_ROWS, (w + 1) * SA_ROWS) in its 64
+  // slots.  All lanes load (lanes past SA_ROWS fill padding from an in-bounds
+  // row): a lane-dependent branch around the asm would put its scalar
+  // operands in vector registers.
+  dma4(src.rsa, stage + C::A_BYTES + C::B_BYTES + w * 256, sa_off, (uint32_t)ks * sa_step);
+  if constexpr (KIND == KIND_MX)
+    dma4(src.rsb, stage + C::A_BYTES + C::B_BYTES + C::SA_BYTES + w * 256, sb_off, (uint32_t)ks * 4);
 }
 
 // Per-lane DMA offsets of the A and B tiles: lane slot (w + 4t) * 64 + lane
@@ -138,7 +170,7 @@ __device__ __forceinline__ void tile_load(const TileSrc& src, uint8_t* lds, int 
 // (slot % 8) ^ swz(row).
 template <int NW>
 __device__ __forceinline__ void dma_rows(int t_idx, int& row, int& qchunk) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int slot = (w + NW * t_idx) * 64 + lane;
   row = slot / kChunks;
   qchunk = (slot % kChunks) ^ swz(row);
@@ -168,6 +200,10 @@ struct StepScales {
   }
 };
 
+// LDS slot of a row's staged scale: wave row / ROWS, lane row % ROWS.
+template <int ROWS>
+__device__ __forceinline__ int scale_slot(int row) { return (row / ROWS) * 64 + row % ROWS; }
+
 // Compute one staged K step (stage at `stage`, logical step ks).
 template <int KIND, int BM, int BN, int NS>
 __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const StepScales& sc1,
@@ -175,16 +211,39 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
                                           f32x4 (&acc)[4][TileCfg<KIND, BM, BN, NS>::NI]) {
   using C = TileCfg<KIND, BM, BN, NS>;
   constexpr int MI = C::MI, NI = C::NI;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int wn = wid % C::WN, wm = wid / C::WN;
   const int g = lane >> 4, r16 = lane & 15;
   const uint8_t* ta = stage;
   const uint8_t* tb = stage + C::A_BYTES;
   const uint8_t* tsa = stage + C::A_BYTES + C::B_BYTES;
   const uint8_t* tsb = tsa + C::SA_BYTES;
+  // With one wave per SIMD nothing else hides LDS latency, so every fragment
+  // of the step is requested before the first MFMA (reads complete in order
+  // and each MFMA waits only for its own operands).  With two waves per SIMD
+  // the register budget is halved; B fragments are then read per column
+  // and the other wave covers the wait.
+  constexpr bool B_AHEAD = C::NW == 4;
+  auto brow_of = [&](int ni) {
+    return (ni < up_split ? 0 : BN / 2 - up_split * 16) + wn * (up_split * 16) + ni * 16 + r16;
+  };
   Frag<KIND_FP8B> fa[MI];
+  Frag<KIND_FP8B> fbs[B_AHEAD ? NI : 1];
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) lds_frag(fa[mi], ta, wm * 64 + mi * 16 + r16, g);
+  if constexpr (B_AHEAD) {
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) lds_frag(fbs[ni], tb, brow_of(ni), g);
+  }
+  auto frag_b = [&](int ni) -> Frag<KIND_FP8B> {
+    if constexpr (B_AHEAD) {
+      return fbs[ni];
+    } else {
+      Frag<KIND_FP8B> fb;
+      lds_frag(fb, tb, brow_of(ni), g);
+      return fb;
+    }
+  };
   if constexpr (KIND == KIND_FP8B) {
     float sa[MI][4];
     const float s1 = sc1.at(ks);
@@ -193,16 +252,13 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4)
-        sa[mi][i4] = reinterpret_cast<const float*>(tsa)[wm * 64 + mi * 16 + 4 * g + i4];
+        sa[mi][i4] = reinterpret_cast<const float*>(tsa)[scale_slot<C::SA_ROWS>(wm * 64 + mi * 16 + 4 * g + i4)];
     // MFMAs of subtile column ni go into their own temporaries and are
     // promoted one column later, so the MFMA pipe never waits on a
     // promotion (the tile products are independent of each other).
     f32x4 t[2][MI];
     auto issue = [&](int ni, f32x4 (&tt)[MI]) {
-      Frag<KIND_FP8B> fb;
-      const int brow = (ni < up_split ? 0 : BN / 2 - up_split * 16) + wn * (up_split * 16) +
-                       ni * 16 + r16;
-      lds_frag(fb, tb, brow, g);
+      const Frag<KIND_FP8B> fb = frag_b(ni);
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -235,14 +291,14 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
   } else {  // MX
     int xa[MI];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) xa[mi] = tsa[(wm * 64 + mi * 16 + r16) * 4 + g];
+    for (int mi = 0; mi < MI; ++mi)
+      xa[mi] = (reinterpret_cast<const uint32_t*>(tsa)[scale_slot<C::SA_ROWS>(wm * 64 + mi * 16 + r16)] >>
+                (8 * g)) & 0xff;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      Frag<KIND_FP8B> fb;
-      const int brow = (ni < up_split ? 0 : BN / 2 - up_split * 16) + wn * (up_split * 16) +
-                       ni * 16 + r16;
-      lds_frag(fb, tb, brow, g);
-      const int xb = tsb[brow * 4 + g];
+      const Frag<KIND_FP8B> fb = frag_b(ni);
+      const int xb =
+          (reinterpret_cast<const uint32_t*>(tsb)[scale_slot<C::SB_ROWS>(brow_of(ni))] >> (8 * g)) & 0xff;
       Frag<KIND_MX> fbm, fam;
       fbm.c[0] = fb.c[0];
       fbm.c[1] = fb.c[1];
@@ -257,18 +313,15 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
 }
 
 // One workgroup tile: acc[mi][ni] over all K steps, visiting the steps from
-// a staggered start, NS stages in flight in NS distinct LDS arrays (the loop
-// is unrolled by NS so every LDS access names its array and the compiler can
-// tell the stage being read from the stages being filled).
+// a staggered start, NS stages in flight (stage slots in one LDS array).
 template <int KIND, int BM, int BN, int NS>
-__device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* const (&stg)[NS], int ksteps,
+__device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, int ksteps,
                                           const uint32_t (&a_off)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
                                           uint32_t sa_off, uint32_t sa_step,
                                           const uint32_t (&b_off)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
                                           uint32_t sb_off, int up_split, int group,
                                           f32x4 (&acc)[4][TileCfg<KIND, BM, BN, NS>::NI]) {
   using C = TileCfg<KIND, BM, BN, NS>;
-  static_assert(NS == 2 || NS == 3, "two or three pipeline stages");
   constexpr int MI = C::MI, NI = C::NI;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -278,35 +331,34 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* const (&s
   if constexpr (KIND == KIND_FP8B) {
     sc1.load(src.bsc, ksteps);
     sc2.load(src.bsc2 ? src.bsc2 : src.bsc, ksteps);
+    // wait here: the compiler would place this wait at the first use, inside
+    // the K loop, where it would also drain the pipeline's loads every pass
+    wait_vmcnt<0>();
   }
   // Tiles that read the same weight rows (the blocks of one expert, for one
   // slice or column tile) start at the same step and walk K in step, sharing
   // those rows in L2.  Tiles reading other weight rows start elsewhere:
   // thousands of rows 4 KiB apart read at one offset at once would
-  // concentrate the traffic on a few HBM channels.  The activation rows a
-  // block shares across its slices stay in L2 without lockstep (0.5 MiB per
-  // block).
+  // concentrate the traffic on a few HBM channels.
   const int rot = (int)((((uint32_t)group * 2654435761u) >> 16) % (uint32_t)ksteps);
   auto step_at = [&](int i) { const int k = i + rot; return k >= ksteps ? k - ksteps : k; };
-  auto load = [&](uint8_t* st, int i) {
-    tile_load<KIND, BM, BN, NS>(src, st, 0, step_at(i), a_off, sa_off, sa_step, b_off, sb_off);
+  const uint32_t lbase = lds_addr(smem);
+  auto load = [&](int slot, int i) {
+    tile_load<KIND, BM, BN, NS>(src, lbase, slot, step_at(i), a_off, sa_off, sa_step, b_off, sb_off);
   };
 #pragma unroll
   for (int u = 0; u < NS - 1; ++u)
-    if (u < ksteps) load(stg[u], u);
-  for (int i0 = 0; i0 < ksteps; i0 += NS) {
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const int i = i0 + u;
-      if (i < ksteps) {
-        // stage i has landed once only the later stages' loads may be pending
-        if (i + NS - 2 < ksteps) wait_vmcnt<C::LOADS * (NS - 2)>();
-        else wait_vmcnt<0>();
-        lds_barrier();
-        if (i + NS - 1 < ksteps) load(stg[(u + NS - 1) % NS], i + NS - 1);
-        tile_step<KIND, BM, BN, NS>(stg[u], step_at(i), sc1, sc2, up_split, acc);
-      }
-    }
+    if (u < ksteps) load(u, u);
+  int slot = 0;
+  for (int i = 0; i < ksteps; ++i) {
+    // step i has landed once only the later steps' loads may be pending
+    if (i + NS - 2 < ksteps) wait_vmcnt<C::LOADS * (NS - 2)>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    const int ahead = slot + NS - 1;
+    if (i + NS - 1 < ksteps) load(ahead >= NS ? ahead - NS : ahead, i + NS - 1);
+    tile_step<KIND, BM, BN, NS>(smem + slot * C::STAGE, step_at(i), sc1, sc2, up_split, acc);
+    slot = slot + 1 == NS ? 0 : slot + 1;
   }
   __syncthreads();  // the caller reuses the LDS
 }
@@ -315,21 +367,19 @@ __device__ __forceinline__ int token_of(int id, int top_k) { return id >= 0 ? id
 
 // gate/up GEMM + SwiGLU + requantization, one (block, 128-wide slice) tile
 template <int KIND, int BM, int NS>
-__global__ void __launch_bounds__(BM == 256 ? 512 : 256) k_up_t(MoeArgs p) {
+__global__ void __launch_bounds__(BM == 256 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(1, BM == 256 ? 2 : 1))) k_up_t(MoeArgs p) {
   using C = TileCfg<KIND, BM, 256, NS>;
   constexpr int MI = C::MI, NI = C::NI, HALF = NI / 2;
-  __shared__ __attribute__((aligned(1024))) uint8_t s0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t s1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t s2[NS > 2 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE];
   __shared__ int ids[BM];
   __shared__ float lds_amax[C::WN * BM];
   const int S = p.I / 128;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int b = logical / S, s = logical % S;
   if (b >= p.blocks_cap || b * BM >= *p.ntp) return;
-  const int e = p.expert_ids[b];
+  const int e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);  // uniform: descriptors in SGPRs
   if ((unsigned)e >= (unsigned)p.E) return;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int wn = wid % C::WN, wm = wid / C::WN;
   const int g = lane >> 4, r16 = lane & 15;
   if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
@@ -337,8 +387,8 @@ __global__ void __launch_bounds__(BM == 256 ? 512 : 256) k_up_t(MoeArgs p) {
   const int K = p.K, I = p.I, N = 2 * I, KS = K / 128;
 
   TileSrc src;
-  src.ra = make_rsrc(p.x, (uint32_t)((size_t)p.T * K));
-  src.rb = make_rsrc(p.w1 + (size_t)e * N * K, (uint32_t)((size_t)N * K));
+  src.ra = make_desc(p.x, (uint32_t)((size_t)p.T * K));
+  src.rb = make_desc(p.w1 + (size_t)e * N * K, (uint32_t)((size_t)N * K));
   uint32_t a_off[C::A_INSTR], b_off[C::B_INSTR];
 #pragma unroll
   for (int t = 0; t < C::A_INSTR; ++t) {
@@ -356,25 +406,23 @@ __global__ void __launch_bounds__(BM == 256 ? 512 : 256) k_up_t(MoeArgs p) {
   const int srow = wid * C::SA_ROWS + lane;  // scale row this lane stages
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
   if constexpr (KIND == KIND_FP8B) {
-    src.rsa = make_rsrc(p.xs, (uint32_t)((size_t)p.T * KS * 4));
+    src.rsa = make_desc(p.xs, (uint32_t)((size_t)p.T * KS * 4));
     sa_off = (uint32_t)token_of(ids[srow < BM ? srow : 0], p.top_k) * KS * 4;
     src.bsc = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + s) * KS;
     src.bsc2 = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + S + s) * KS;
   } else {
-    src.rsa = make_rsrc(p.xs, (uint32_t)((size_t)p.T * (K / 32)));
+    src.rsa = make_desc(p.xs, (uint32_t)((size_t)p.T * (K / 32)));
     sa_off = (uint32_t)token_of(ids[srow < BM ? srow : 0], p.top_k) * (K / 32);
-    src.rsb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w1s) + (size_t)e * N * (K / 32),
+    src.rsb = make_desc(reinterpret_cast<const uint8_t*>(p.w1s) + (size_t)e * N * (K / 32),
                         (uint32_t)((size_t)N * (K / 32)));
-    const int brow = wid * C::SB_ROWS + lane;  // B scale row this lane stages
+    const int brow = min(wid * C::SB_ROWS + lane, 255);  // B scale row this lane stages
     const int n = (brow < 128 ? s * 128 + brow : I + s * 128 + brow - 128);
     sb_off = (uint32_t)n * (K / 32);
     src.bsc = nullptr;
     src.bsc2 = nullptr;
   }
   f32x4 acc[MI][NI];
-  uint8_t* const stg3[3] = {s0, s1, s2};
-  uint8_t* const (&stg)[NS] = *reinterpret_cast<uint8_t* const (*)[NS]>(&stg3);
-  tile_gemm<KIND, BM, 256, NS>(src, stg, KS, a_off, sa_off, sa_step, b_off, sb_off, HALF,
+  tile_gemm<KIND, BM, 256, NS>(src, smem, KS, a_off, sa_off, sa_step, b_off, sb_off, HALF,
                                e * 64 + s, acc);
 
   // SwiGLU: gate subtile j pairs with up subtile HALF + j (same columns)
@@ -387,7 +435,7 @@ __global__ void __launch_bounds__(BM == 256 ? 512 : 256) k_up_t(MoeArgs p) {
       for (int i4 = 0; i4 < 4; ++i4) h[mi][j][i4] = swiglu(acc[mi][j][i4], acc[mi][HALF + j][i4]);
 
   // requantize; stage codes in LDS as (BM x 128) bytes, then store rows
-  uint8_t* q = s0;  // reuse the pipeline LDS
+  uint8_t* q = smem;  // reuse the pipeline LDS
   constexpr int QROW = 128 + 16;
   const size_t pos0 = (size_t)b * BM;
   if constexpr (KIND == KIND_FP8B) {
@@ -456,29 +504,27 @@ __global__ void __launch_bounds__(BM == 256 ? 512 : 256) k_up_t(MoeArgs p) {
 
 // down GEMM, one (block, 256 output columns) tile, fp32 per-route rows
 template <int KIND, int BM, int NS>
-__global__ void __launch_bounds__(BM == 256 ? 512 : 256) k_down_t(MoeArgs p) {
+__global__ void __launch_bounds__(BM == 256 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(1, BM == 256 ? 2 : 1))) k_down_t(MoeArgs p) {
   using C = TileCfg<KIND, BM, 256, NS>;
   constexpr int MI = C::MI, NI = C::NI;
-  __shared__ __attribute__((aligned(1024))) uint8_t s0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t s1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t s2[NS > 2 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE];
   __shared__ int ids[BM];
   const int K = p.K, I = p.I, IS = I / 128;
   const int NT = K / 256;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int b = logical / NT, ct = logical % NT;
   if (b >= p.blocks_cap || b * BM >= *p.ntp) return;
-  const int e = p.expert_ids[b];
+  const int e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);  // uniform: descriptors in SGPRs
   if ((unsigned)e >= (unsigned)p.E) return;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wid = wave_id();
   const int wn = wid % C::WN, wm = wid / C::WN;
   const int g = lane >> 4, r16 = lane & 15;
   if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
   __syncthreads();
   const size_t rows_cap = (size_t)p.blocks_cap * BM;
   TileSrc src;
-  src.ra = make_rsrc(p.hq, (uint32_t)(rows_cap * I));
-  src.rb = make_rsrc(p.w2 + (size_t)e * K * I, (uint32_t)((size_t)K * I));
+  src.ra = make_desc(p.hq, (uint32_t)(rows_cap * I));
+  src.rb = make_desc(p.w2 + (size_t)e * K * I, (uint32_t)((size_t)K * I));
   uint32_t a_off[C::A_INSTR], b_off[C::B_INSTR];
 #pragma unroll
   for (int t = 0; t < C::A_INSTR; ++t) {
@@ -496,14 +542,14 @@ __global__ void __launch_bounds__(BM == 256 ? 512 : 256) k_down_t(MoeArgs p) {
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
   const int c0 = ct * 256 + wn * (256 / C::WN);  // this wave's first output column
   if constexpr (KIND == KIND_FP8B) {
-    src.rsa = make_rsrc(p.hs, (uint32_t)(rows_cap * IS * 4));
+    src.rsa = make_desc(p.hs, (uint32_t)(rows_cap * IS * 4));
     sa_off = (uint32_t)((size_t)b * BM + (srow < BM ? srow : 0)) * IS * 4;
     src.bsc = reinterpret_cast<const float*>(p.w2s) + ((size_t)e * (K / 128) + c0 / 128) * IS;
     src.bsc2 = nullptr;
   } else {
-    src.rsa = make_rsrc(p.hs, (uint32_t)(rows_cap * (I / 32)));
+    src.rsa = make_desc(p.hs, (uint32_t)(rows_cap * (I / 32)));
     sa_off = (uint32_t)((size_t)b * BM + (srow < BM ? srow : 0)) * (I / 32);
-    src.rsb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w2s) + (size_t)e * K * (I / 32),
+    src.rsb = make_desc(reinterpret_cast<const uint8_t*>(p.w2s) + (size_t)e * K * (I / 32),
                         (uint32_t)((size_t)K * (I / 32)));
     sb_off = (uint32_t)(ct * 256 + (wid * C::SB_ROWS + lane) % 256) * (I / 32);
     src.bsc = nullptr;
@@ -511,9 +557,7 @@ __global__ void __launch_bounds__(BM == 256 ? 512 : 256) k_down_t(MoeArgs p) {
   }
   f32x4 acc[MI][NI];
   // all NI subtiles of a wave are contiguous output columns (no gate/up split)
-  uint8_t* const stg3[3] = {s0, s1, s2};
-  uint8_t* const (&stg)[NS] = *reinterpret_cast<uint8_t* const (*)[NS]>(&stg3);
-  tile_gemm<KIND, BM, 256, NS>(src, stg, IS, a_off, sa_off, sa_step, b_off, sb_off, NI,
+  tile_gemm<KIND, BM, 256, NS>(src, smem, IS, a_off, sa_off, sa_step, b_off, sb_off, NI,
                                e * 64 + ct, acc);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
