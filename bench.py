@@ -118,6 +118,55 @@ def load_traffic(workload, T, kernel_name):
     return None if e is None else e.get("bytes_per_launch")
 
 
+def summarize_counters(root, workload):
+    """Turn the rocprofv3 counter runs of the traffic measurement into
+    profiles/hbm_traffic.json.  `root` holds one directory per run, named
+    pmc_{copy,up,fused}_{FETCH_SIZE,WRITE_SIZE} (see the command list in
+    profiles/hbm_traffic_*.md), each with the profiler's *_counter_collection.csv."""
+    import csv
+    import glob
+
+    def values(run, counter, kernel_sub=None):
+        out = []
+        for f in glob.glob(os.path.join(root, f"pmc_{run}_{counter}", "*counter_collection.csv")):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] != counter:
+                    continue
+                if kernel_sub and kernel_sub not in r["Kernel_Name"]:
+                    continue
+                out.append(float(r["Counter_Value"]))
+        if not out:
+            raise SystemExit(f"no {counter} values for {run} {kernel_sub or ''} under {root}")
+        return out
+
+    # the copy kernel moves exactly n bytes each way per launch; the largest
+    # dispatches are the copies (torch's fill of the source is a write only)
+    n = 1024 << 20
+    fetch_copy = max(values("copy", "FETCH_SIZE"))
+    write_copy = max(values("copy", "WRITE_SIZE"))
+    fetch_factor = n / (fetch_copy * 1024)
+    write_factor = n / (write_copy * 1024)
+    entries = {}
+    for run, T, kname, sub in (("up", 256, "k_up", "::k_up<"), ("up", 256, "k_down", "::k_down<"),
+                               ("fused", 8, "k_fused", "::k_fused<")):
+        fk = values(run, "FETCH_SIZE", sub)
+        wk = values(run, "WRITE_SIZE", sub)
+        f_raw, w_raw = sum(fk) / len(fk), sum(wk) / len(wk)
+        fb, wb = f_raw * 1024 * fetch_factor, w_raw * 1024 * write_factor
+        entries[f"{workload}/T={T}/{kname}"] = {
+            "fetch_kib_raw": f_raw, "write_kib_raw": w_raw, "fetch_bytes": fb,
+            "write_bytes": wb, "bytes_per_launch": fb + wb, "dispatches": len(fk)}
+    d = {"kernel_source_hash": kernel_source_hash(),
+         "calibration": {"copy_bytes_read": n, "copy_bytes_written": n,
+                         "fetch_kib_per_copy": fetch_copy, "write_kib_per_copy": write_copy,
+                         "fetch_factor": fetch_factor, "write_factor": write_factor},
+         "entries": entries}
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(d, f, indent=1)
+    print(json.dumps(d, indent=1))
+
+
 def cpu_baseline(case, n_tokens, K, I):
     import numpy as np
 
@@ -159,7 +208,13 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=20)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-counters", default=None, metavar="DIR",
+                    help="only write profiles/hbm_traffic.json from the counter runs under DIR")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
