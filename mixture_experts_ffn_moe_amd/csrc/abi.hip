@@ -76,11 +76,14 @@ int check_ffn(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
 
 int pick_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
                int32_t block_m) {
-  (void)dtype; (void)K; (void)N; (void)E;
+  (void)dtype; (void)K; (void)E;
   if (block_m == 256) return 1;
   // The fused mode's split-K accumulation costs R*K*(I/128) fp32 atomic adds;
   // it stays cheap against the weight stream only for decode-sized calls.
-  return (T * top_k <= 512) ? 0 : 1;
+  // Its grid is (blocks x I/128 slices): with few slices (a narrow
+  // intermediate) it cannot fill the GPU, and the split mode's down GEMM,
+  // tiled over the K output columns, streams the weights faster.
+  return (T * top_k <= 512 && N / 2 / 128 >= 8) ? 0 : 1;
 }
 
 struct Layout {
@@ -243,7 +246,10 @@ int moe_select_block_m(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32
   // the 256-row tile pays off where the MFMA applies the scales itself; the
   // blockwise path's per-step promotion does not fit its register budget
   const bool big_ok = dtype == MOE_MXFP8 && K % 256 == 0;
-  *block_m = per <= 16 ? 16 : per <= 48 ? 32 : per <= 160 ? 64 : (per <= 200 || !big_ok) ? 128 : 256;
+  // measured: 16 rows stream the weights best while experts hold about a
+  // block; past that the 64-row LDS-tiled kernels win (32 measured slower
+  // than 64 at 28 rows per expert)
+  *block_m = per <= 16 ? 16 : per <= 160 ? 64 : (per <= 200 || !big_ok) ? 128 : 256;
   return ok();
 }
 

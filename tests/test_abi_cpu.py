@@ -112,5 +112,8 @@ def test_heuristics():
     assert moe.moe_select_block_m(8192, 8, 288, "mxfp8", 4096 + 128) == 128
     assert moe.moe_select_block_m(8192, 8, 288, "bf16", 4096) == 128
     assert moe.moe_select_block_m(4096, 8, 288, "fp8_blockwise", 4096) == 64
+    assert moe.moe_select_block_m(1024, 8, 288, "fp8_blockwise", 4096) == 64   # 28 rows/expert
+    assert moe.moe_select_block_m(1024, 6, 384, "fp8_blockwise", 7168) == 16   # 16 rows/expert
     assert moe.moe_select_split("fp8_blockwise", 8, 4096, 4096, 256, 6, 16) == 0
+    assert moe.moe_select_split("mxfp8", 8, 4096, 512, 32, 8, 16) == 1         # I = 256: 2 slices
     assert moe.moe_select_split("fp8_blockwise", 8192, 4096, 4096, 288, 8, 128) == 1
