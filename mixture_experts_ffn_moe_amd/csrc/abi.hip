@@ -60,6 +60,9 @@ int check_ffn(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
   if (K % 128) return fail(MOE_ERR_UNSUPPORTED, "K must be a multiple of 128 (got %lld)", (long long)K);
   if ((N / 2) % 128)
     return fail(MOE_ERR_UNSUPPORTED, "I = N/2 must be a multiple of 128 (got %lld)", (long long)(N / 2));
+  // blockwise weight scales of one row of 128-blocks sit in two registers per lane
+  if (dtype == MOE_FP8_BLOCKWISE && (K > 16384 || N / 2 > 16384))
+    return fail(MOE_ERR_UNSUPPORTED, "blockwise FP8 needs K and I = N/2 <= 16384");
   if (!valid_block_m(block_m))
     return fail(MOE_ERR_UNSUPPORTED, "block_m must be 16, 32, 64, 128 or 256 (got %d)", block_m);
   if (block_m == 256 && (dtype == MOE_BF16 || K % 256))

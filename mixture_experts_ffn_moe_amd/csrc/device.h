@@ -151,3 +151,27 @@ __device__ __forceinline__ float wave_max16(float v) {
   v = __builtin_fmaxf(v, __shfl_xor(v, 8));
   return v;
 }
+
+// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt in bits 3:0 and 15:14), other counters untouched
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Weight block scales of one n-block for every K step, held lane-indexed in
+// registers (lane j holds step j, and step 64 + j in the second register), so
+// the K loop reads them with readlane instead of memory loads (at most 128
+// steps: K <= 16384).
+struct StepScales {
+  float lo, hi;
+  __device__ __forceinline__ void load(const float* row, int nsteps) {
+    const int lane = threadIdx.x & 63;
+    lo = lane < nsteps ? row[lane] : 0.f;
+    hi = 64 + lane < nsteps ? row[64 + lane] : 0.f;
+  }
+  __device__ __forceinline__ float at(int ks) const {
+    const float v = ks < 64 ? lo : hi;
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), ks & 63));
+  }
+};

@@ -46,10 +46,12 @@ struct Operand {
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t a[MI], b[NI];
   // FP8B: fp32 scale of each of the lane's C rows (byte offsets, step stride
-  // 4 bytes) and the weight block scale row of each n-subtile (uniform)
+  // 4 bytes); the weight block-scale rows (at most two distinct 128-column
+  // blocks per wave) and which of them each n-subtile uses
   __amdgpu_buffer_rsrc_t rsa;
   uint32_t as[MI][4];
-  const float* bs[NI];
+  const float* bsrow[2];
+  int bsel[NI];
   // MX: e8m0 rows of the lane's A row and B row (+ lane group), 4 bytes per step
   __amdgpu_buffer_rsrc_t rxa, rxb;
   uint32_t ax[MI], bx[NI];
@@ -60,7 +62,6 @@ struct Ring {
   Frag<KIND> fa[D][MI];
   Frag<KIND> fb[D][NI];
   float sa[D][MI][4];
-  float sb[D][NI];
   int xa[D][MI];
   int xb[D][NI];
 };
@@ -78,8 +79,6 @@ __device__ __forceinline__ void ring_load(Ring<KIND, MI, NI, D>& r, int slot, in
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int i = 0; i < 4; ++i) r.sa[slot][mi][i] = buf_loadf(op.rsa, op.as[mi][i], ks * 4);
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) r.sb[slot][ni] = op.bs[ni][ks];
   }
   if constexpr (KIND == KIND_MX) {
 #pragma unroll
@@ -90,18 +89,22 @@ __device__ __forceinline__ void ring_load(Ring<KIND, MI, NI, D>& r, int slot, in
 }
 
 template <int KIND, int MI, int NI, int D>
-__device__ __forceinline__ void ring_compute(const Ring<KIND, MI, NI, D>& r, int slot,
-                                             f32x4 (&acc)[MI][NI]) {
+__device__ __forceinline__ void ring_compute(const Ring<KIND, MI, NI, D>& r, int slot, int ks,
+                                             const Operand<MI, NI>& op,
+                                             const StepScales (&sc)[2], f32x4 (&acc)[MI][NI]) {
   if constexpr (KIND == KIND_FP8B) {
+    float sb[2];
+    sb[0] = sc[0].at(ks);
+    sb[1] = sc[1].at(ks);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 t = mfma_step<KIND>(r.fa[slot][mi], r.fb[slot][ni], z);
+        const float w = op.bsel[ni] ? sb[1] : sb[0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[mi][ni][i] += t[i] * (r.sa[slot][mi][i] * r.sb[slot][ni]);
+        for (int i = 0; i < 4; ++i) acc[mi][ni][i] += t[i] * (r.sa[slot][mi][i] * w);
       }
   } else if constexpr (KIND == KIND_MX) {
 #pragma unroll
@@ -135,39 +138,62 @@ __device__ __forceinline__ int stagger_wg(int nsteps) {
   return (int)(((blockIdx.x * 2654435761u) >> 16) % (uint32_t)nsteps);
 }
 
-// acc[mi][ni] = sum over ksteps 128-wide steps of A rows . B rows (with the
-// dtype's scales), D steps of operands prefetched into registers, visiting
-// the steps from a staggered start.
+// acc[mi][ni] = sum over the 128-wide K steps [k_first, k_first + ksteps) of
+// A rows . B rows (with the dtype's scales), D steps of operands prefetched
+// into registers, visiting the steps from a staggered start.
 template <int KIND, int MI, int NI, int D>
-__device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int ksteps,
+__device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_first, int ksteps,
                                            f32x4 (&acc)[MI][NI]) {
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+  StepScales sc[2] = {{0.f, 0.f}, {0.f, 0.f}};
+  if constexpr (KIND == KIND_FP8B) {
+    sc[0].load(op.bsrow[0] + k_first, ksteps);
+    sc[1].load(op.bsrow[1] + k_first, ksteps);
+    // wait here, not at the first use inside the loop, where it would also
+    // drain the operand ring every pass
+    wait_vmcnt<0>();
+  }
   const int rot = stagger_wg(ksteps);
-  auto step_at = [&](int i) { const int k = i + rot; return k >= ksteps ? k - ksteps : k; };
+  auto rel = [&](int i) { const int k = i + rot; return k >= ksteps ? k - ksteps : k; };
   Ring<KIND, MI, NI, D> r;
+  // The steady-state loop loads unconditionally, so the count of loads in
+  // flight is the same at every step and the compiler's waits stay precise
+  // (a conditional load inside the loop makes it wait for every load at the
+  // join).  The last steps, fewer than 2D, run in an unrolled tail.
+  // the prologue fills every slot unconditionally too (with fewer steps than
+  // slots the spare slots re-load a wrapped, in-bounds step nobody uses):
+  // a skipped load here would leave the loop's first waits conservative
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (d < ksteps) ring_load<KIND>(r, d, step_at(d), op);
-  for (int k0 = 0; k0 < ksteps; k0 += D) {
+  for (int d = 0; d < D; ++d) ring_load<KIND>(r, d, k_first + rel(d < ksteps ? d : d % ksteps), op);
+  int ks = 0;
+  for (; ks + 2 * D <= ksteps; ks += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int ks = k0 + d;
-      if (ks < ksteps) {
-        ring_compute<KIND>(r, d, acc);
-        if (ks + D < ksteps) ring_load<KIND>(r, d, step_at(ks + D), op);
-      }
+      ring_compute<KIND>(r, d, rel(ks + d), op, sc, acc);
+      ring_load<KIND>(r, d, k_first + rel(ks + d + D), op);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < 2 * D; ++d) {
+    const int k = ks + d;
+    if (k < ksteps) {
+      ring_compute<KIND>(r, d % D, rel(k), op, sc, acc);
+      if (k + D < ksteps) ring_load<KIND>(r, d % D, k_first + rel(k + D), op);
     }
   }
 }
 
-template <int BM>
+template <int BM, int KSPLIT = 1>
 struct BlockShape {
   static constexpr int MI = (BM < 64 ? BM : 64) / 16;  // 16-row subtiles per wave
   static constexpr int WM = (BM + 63) / 64;            // wave rows
-  static constexpr int THREADS = 256 * WM;
+  static constexpr int WG = 4 * WM;                    // waves per K group
+  static constexpr int THREADS = 64 * WG * KSPLIT;
+  // LDS floats for the partial sums of groups 1..KSPLIT-1 (4 gate/up subtile columns)
+  static constexpr int RED = KSPLIT > 1 ? (KSPLIT - 1) * WG * MI * 4 * 4 * 64 : 1;
 };
 
 __device__ __forceinline__ int token_of(int id, int top_k) {
@@ -177,13 +203,17 @@ __device__ __forceinline__ int token_of(int id, int top_k) {
 // Gate/up GEMM + SwiGLU for one (block, slice) tile: h[mi][j] holds the
 // lane's C elements of gate/up column pair j (columns 32*wn + 16*j + l%16 of
 // the slice), rows 64*wm + 16*mi + 4*(l/16) + i.
-template <int KIND, int BM, int D>
+template <int KIND, int BM, int D, int KSPLIT>
 __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const int* ids,
-                                        f32x4 (&h)[BlockShape<BM>::MI][2]) {
-  constexpr int MI = BlockShape<BM>::MI;
+                                        f32x4 (&h)[BlockShape<BM>::MI][2], float* red) {
+  using B = BlockShape<BM, KSPLIT>;
+  constexpr int MI = B::MI;
   constexpr int ES = KindTraits<KIND>::ES;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wn = wid & 3, wm = wid >> 2;
+  // wave-uniform wave index: the K range (hence every load's soffset) derives
+  // from it and must stay in scalar registers
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int kg = KSPLIT > 1 ? wid / B::WG : 0, wig = KSPLIT > 1 ? wid % B::WG : wid;
+  const int wn = wig & 3, wm = wig >> 2;
   const int g = lane >> 4, r16 = lane & 15;
   const int K = p.K, I = p.I, N = 2 * p.I;
   const int KS = K / 128, S = I / kSlice;
@@ -214,14 +244,43 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const in
   for (int ni = 0; ni < 4; ++ni) {
     const int n = (ni < 2 ? 0 : I) + s * kSlice + 32 * wn + 16 * (ni & 1) + r16;
     op.b[ni] = (uint32_t)n * K * ES + 16 * g;
-    if constexpr (KIND == KIND_FP8B) {
-      const int nb = (ni < 2 ? 0 : S) + s;
-      op.bs[ni] = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + nb) * KS;
-    }
+    if constexpr (KIND == KIND_FP8B) op.bsel[ni] = ni < 2 ? 0 : 1;  // gate block, up block
     if constexpr (KIND == KIND_MX) op.bx[ni] = (uint32_t)n * (K / 32) + g;
   }
+  if constexpr (KIND == KIND_FP8B) {
+    op.bsrow[0] = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + s) * KS;
+    op.bsrow[1] = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + S + s) * KS;
+  }
   f32x4 acc[MI][4];
-  gemm_steps<KIND, MI, 4, D>(op, KS, acc);
+  const int k_lo = kg * KS / KSPLIT, k_hi = (kg + 1) * KS / KSPLIT;
+  gemm_steps<KIND, MI, 4, D>(op, k_lo, k_hi - k_lo, acc);
+  if constexpr (KSPLIT > 1) {
+    // partial sums of groups 1.. go through LDS (lane-contiguous floats);
+    // group 0 adds them in group order
+    constexpr int PER = MI * 4 * 4;  // floats per lane
+    if (kg > 0) {
+      float* dst = red + ((size_t)((kg - 1) * B::WG + wig) * PER) * 64 + lane;
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[((mi * 4 + ni) * 4 + i) * 64] = acc[mi][ni][i];
+    }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int gk = 1; gk < KSPLIT; ++gk) {
+        const float* src = red + ((size_t)((gk - 1) * B::WG + wig) * PER) * 64 + lane;
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[mi][ni][i] += src[((mi * 4 + ni) * 4 + i) * 64];
+      }
+    }
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -240,8 +299,10 @@ __device__ __forceinline__ void requant_tile(const f32x4 (&h)[BlockShape<BM>::MI
                                              int (&sx)[BlockShape<BM>::MI][4],
                                              float* lds_amax /* [4][BM] */) {
   constexpr int MI = BlockShape<BM>::MI;
+  constexpr int WG = BlockShape<BM>::WG;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wn = wid & 3, wm = wid >> 2;
+  const int wig = wid % WG;  // waves past the first K group hold no result
+  const int wn = wig & 3, wm = wig >> 2;
   const int g = lane >> 4, r16 = lane & 15;
   if constexpr (KIND == KIND_BF16) {
 #pragma unroll
@@ -260,7 +321,7 @@ __device__ __forceinline__ void requant_tile(const f32x4 (&h)[BlockShape<BM>::MI
         am[mi][i] = wave_max16(__builtin_fmaxf(__builtin_fabsf(h[mi][0][i]),
                                                __builtin_fabsf(h[mi][1][i])));
     if constexpr (KIND == KIND_FP8B) {
-      if (r16 == 0) {
+      if (r16 == 0 && wid < WG) {
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -301,10 +362,11 @@ __device__ __forceinline__ void requant_tile(const f32x4 (&h)[BlockShape<BM>::MI
 // split mode
 // ---------------------------------------------------------------------------
 
-template <int KIND, int BM, int D>
-__global__ void __launch_bounds__(BlockShape<BM>::THREADS)
+template <int KIND, int BM, int D, int KSPLIT>
+__global__ void __launch_bounds__((BlockShape<BM, KSPLIT>::THREADS))
 k_up(MoeArgs p) {
-  constexpr int MI = BlockShape<BM>::MI;
+  using B = BlockShape<BM, KSPLIT>;
+  constexpr int MI = B::MI;
   constexpr int ES = KindTraits<KIND>::ES;
   const int S = p.I / kSlice;
   const int b = blockIdx.x / S, s = blockIdx.x % S;
@@ -313,16 +375,18 @@ k_up(MoeArgs p) {
   if ((unsigned)e >= (unsigned)p.E) return;
   __shared__ int ids[BM];
   __shared__ float lds_amax[4 * BM];
+  __shared__ float red[B::RED];
   if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
   __syncthreads();
   f32x4 h[MI][2];
-  up_tile<KIND, BM, D>(p, e, s, ids, h);
+  up_tile<KIND, BM, D, KSPLIT>(p, e, s, ids, h, red);
   uint32_t codes[MI][2][4];
   float sf[MI][4];
   int sx[MI][4];
   requant_tile<KIND, BM>(h, codes, sf, sx, lds_amax);
 
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (wid >= B::WG) return;  // the other K groups hold no result (no barrier follows)
   const int wn = wid & 3, wm = wid >> 2;
   const int g = lane >> 4, r16 = lane & 15;
   const int I = p.I;
@@ -400,12 +464,15 @@ k_down(MoeArgs p) {
   for (int ni = 0; ni < 4; ++ni) {
     const int c = c0 + 16 * ni + r16;
     op.b[ni] = (uint32_t)c * I * ES + 16 * g;
-    if constexpr (KIND == KIND_FP8B)
-      op.bs[ni] = reinterpret_cast<const float*>(p.w2s) + ((size_t)e * (K / 128) + c0 / 128) * IS;
+    if constexpr (KIND == KIND_FP8B) op.bsel[ni] = 0;
     if constexpr (KIND == KIND_MX) op.bx[ni] = (uint32_t)c * (I / 32) + g;
   }
+  if constexpr (KIND == KIND_FP8B) {
+    op.bsrow[0] = reinterpret_cast<const float*>(p.w2s) + ((size_t)e * (K / 128) + c0 / 128) * IS;
+    op.bsrow[1] = op.bsrow[0];
+  }
   f32x4 acc[MI][4];
-  gemm_steps<KIND, MI, 4, D>(op, IS, acc);
+  gemm_steps<KIND, MI, 4, D>(op, 0, IS, acc);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -445,10 +512,11 @@ __global__ void __launch_bounds__(256) k_combine(MoeArgs p) {
 // fused mode
 // ---------------------------------------------------------------------------
 
-template <int KIND, int BM, int D>
-__global__ void __launch_bounds__(BlockShape<BM>::THREADS)
+template <int KIND, int BM, int D, int KSPLIT>
+__global__ void __launch_bounds__((BlockShape<BM, KSPLIT>::THREADS))
 k_fused(MoeArgs p) {
-  constexpr int MI = BlockShape<BM>::MI;
+  using B = BlockShape<BM, KSPLIT>;
+  constexpr int MI = B::MI;
   constexpr int ES = KindTraits<KIND>::ES;
   constexpr int QROW = 128 * ES + 16;  // LDS row stride of the slice (bytes)
   const int S = p.I / kSlice;
@@ -461,39 +529,43 @@ k_fused(MoeArgs p) {
   __shared__ float lds_sf[BM];
   __shared__ uint8_t lds_sx[BM * 4];
   __shared__ __attribute__((aligned(16))) uint8_t lds_q[BM * QROW];
+  __shared__ float red[B::RED];
   if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
   __syncthreads();
   f32x4 h[MI][2];
-  up_tile<KIND, BM, D>(p, e, s, ids, h);
+  up_tile<KIND, BM, D, KSPLIT>(p, e, s, ids, h, red);
   uint32_t codes[MI][2][4];
   float sf[MI][4];
   int sx[MI][4];
   requant_tile<KIND, BM>(h, codes, sf, sx, lds_amax);
 
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int wn = wid & 3, wm = wid >> 2;
+  const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int kg = KSPLIT > 1 ? wid / B::WG : 0, wig = KSPLIT > 1 ? wid % B::WG : wid;
+  const int wn = wig & 3, wm = wig >> 2;
   const int g = lane >> 4, r16 = lane & 15;
   const int K = p.K, I = p.I;
-#pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 64 + mi * 16 + 4 * g + i;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = 32 * wn + 16 * j + r16;
-        if constexpr (ES == 2)
-          *reinterpret_cast<uint16_t*>(lds_q + row * QROW + col * 2) = (uint16_t)codes[mi][j][i];
-        else
-          lds_q[row * QROW + col] = (uint8_t)codes[mi][j][i];
-      }
-      if (r16 == 0) {
-        if constexpr (KIND == KIND_FP8B) {
-          if (wn == 0) lds_sf[row] = sf[mi][i];
+  if (kg == 0) {  // the first K group holds the slice
+  #pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 64 + mi * 16 + 4 * g + i;
+  #pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = 32 * wn + 16 * j + r16;
+          if constexpr (ES == 2)
+            *reinterpret_cast<uint16_t*>(lds_q + row * QROW + col * 2) = (uint16_t)codes[mi][j][i];
+          else
+            lds_q[row * QROW + col] = (uint8_t)codes[mi][j][i];
         }
-        if constexpr (KIND == KIND_MX) lds_sx[row * 4 + wn] = (uint8_t)sx[mi][i];
+        if (r16 == 0) {
+          if constexpr (KIND == KIND_FP8B) {
+            if (wn == 0) lds_sf[row] = sf[mi][i];
+          }
+          if constexpr (KIND == KIND_MX) lds_sx[row * 4 + wn] = (uint8_t)sx[mi][i];
+        }
       }
-    }
+  }
   __syncthreads();
 
   // partial down GEMM of this slice: rows of this wave x all K columns
@@ -519,12 +591,12 @@ k_fused(MoeArgs p) {
     }
   }
   const int IS = I / 128;
-  const int nchunks = K / 64;  // 64-column chunks, round-robin over the 4 wave columns
+  const int nchunks = K / 64;  // 64-column chunks, round-robin over the wave columns
   const __amdgpu_buffer_rsrc_t rw2 =
       make_rsrc(p.w2 + (size_t)e * K * I * ES, (uint32_t)((size_t)K * I * ES));
   const uint32_t soff = (uint32_t)s * kSlice * ES;
   const int qrot = stagger_wg(nchunks);
-  for (int qi = wn; qi < nchunks; qi += 4) {
+  for (int qi = wn + 4 * kg; qi < nchunks; qi += 4 * KSPLIT) {
     const int q = (qi + qrot) % nchunks;  // staggered start, see stagger_wg()
     const int c0 = q * 64;
     Frag<KIND> fb[4];
@@ -586,14 +658,50 @@ inline unsigned grid_for(size_t n, size_t per_block) {
 // Register-prefetch depth (K steps in flight per wave), sized so that the
 // operand ring, the accumulators and the scales fit the register file without
 // spills (a bf16 fragment is twice an e4m3 one).
-template <int KIND, int BM>
+template <int KIND, int BM, int KSPLIT = 1>
 constexpr int prefetch_depth() {
-  if constexpr (KIND == KIND_BF16) return BM <= 32 ? 2 : 1;
+  // two K groups put two waves on each SIMD, which halves each wave's
+  // registers (four groups would leave too few for any prefetch)
+  if constexpr (KIND == KIND_BF16) return BM <= 32 && KSPLIT == 1 ? 2 : 1;
+  else if constexpr (KSPLIT == 2) return BM == 16 ? 3 : 2;
   else return BM == 16 ? 4 : BM == 32 ? 3 : BM == 64 ? 2 : 1;
 }
 
 inline void mark(const TimingHook& h, int which, bool after, hipStream_t st) {
   if (h.which == which && h.before && h.after) hipEventRecord(after ? h.after : h.before, st);
+}
+
+// Launch of the up-GEMM kernel (k_up or k_fused) with KSPLIT K groups.
+template <int KIND, int BM, int KSPLIT>
+void launch_up(int split, const MoeArgs& a, unsigned grid, hipStream_t st) {
+  constexpr int TH = BlockShape<BM, KSPLIT>::THREADS;
+  constexpr int D = prefetch_depth<KIND, BM, KSPLIT>();
+  if (split) hipLaunchKernelGGL((k_up<KIND, BM, D, KSPLIT>), dim3(grid), dim3(TH), 0, st, a);
+  else hipLaunchKernelGGL((k_fused<KIND, BM, D, KSPLIT>), dim3(grid), dim3(TH), 0, st, a);
+}
+
+// K groups for the up GEMM: with few (block, slice) tiles (a narrow
+// intermediate, or few routes) one workgroup per tile leaves most CUs idle
+// and each CU streams from few waves.  Tiles are estimated as one block per
+// routed expert (decode sizes) times the slices.
+template <int BM>
+int pick_ksplit(const MoeArgs& a) {
+  if constexpr (BM > 32) {
+    return 1;
+  } else {
+    const size_t R = (size_t)a.T * a.top_k;
+    const size_t tiles = (R < (size_t)a.E ? R : (size_t)a.E) * (size_t)(a.I / kSlice);
+    if (a.K / 128 < 8) return 1;  // too few K steps to share out
+    return tiles <= 256 ? 2 : 1;
+  }
+}
+
+template <int KIND, int BM>
+void launch_up_any(int split, const MoeArgs& a, unsigned grid, hipStream_t st) {
+  if constexpr (BM <= 32) {
+    if (pick_ksplit<BM>(a) == 2) return launch_up<KIND, BM, 2>(split, a, grid, st);
+  }
+  launch_up<KIND, BM, 1>(split, a, grid, st);
 }
 
 template <int KIND, int BM>
@@ -614,7 +722,7 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
       return hipGetLastError();
     }
     mark(hk, 1, false, st);
-    hipLaunchKernelGGL((k_up<KIND, BM, D>), dim3((unsigned)a.blocks_cap * S), dim3(THREADS), 0, st, a);
+    launch_up_any<KIND, BM>(1, a, (unsigned)a.blocks_cap * S, st);
     mark(hk, 1, true, st);
     const int NT = (a.K + 255) / 256;
     mark(hk, 2, false, st);
@@ -628,8 +736,7 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
     hipLaunchKernelGGL(k_zero, dim3(grid_for(n16, 256)), dim3(256), 0, st,
                        reinterpret_cast<uint4*>(a.acc), n16);
     mark(hk, 1, false, st);
-    hipLaunchKernelGGL((k_fused<KIND, BM, D>), dim3((unsigned)a.blocks_cap * S), dim3(THREADS), 0,
-                       st, a);
+    launch_up_any<KIND, BM>(0, a, (unsigned)a.blocks_cap * S, st);
     mark(hk, 1, true, st);
     hipLaunchKernelGGL(k_finalize, dim3(grid_for((size_t)a.T * a.K / 4, 256)), dim3(256), 0, st, a);
   }

@@ -80,13 +80,6 @@ __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
-// s_waitcnt vmcnt(n) (gfx9 encoding: vmcnt in bits 3:0 and 15:14), other counters untouched
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
 // Workgroup barrier without the release fence __syncthreads() carries: that
 // fence waits for every outstanding vector load, including the direct-to-LDS
 // loads of later pipeline stages.  Stage completion is tracked with explicit
@@ -183,22 +176,6 @@ __device__ __forceinline__ void lds_frag(Frag<KIND_FP8B>& f, const uint8_t* base
   f.c[0] = *reinterpret_cast<const uint4*>(r + ((g ^ s) << 4));
   f.c[1] = *reinterpret_cast<const uint4*>(r + (((4 + g) ^ s) << 4));
 }
-
-// Weight block scales of one n-block for every K step, held lane-indexed in
-// registers (lane j holds step j, and step 64 + j in the second register), so
-// the K loop reads them with readlane instead of memory loads.
-struct StepScales {
-  float lo, hi;
-  __device__ __forceinline__ void load(const float* row, int nsteps) {
-    const int lane = threadIdx.x & 63;
-    lo = lane < nsteps ? row[lane] : 0.f;
-    hi = 64 + lane < nsteps ? row[64 + lane] : 0.f;
-  }
-  __device__ __forceinline__ float at(int ks) const {
-    const float v = ks < 64 ? lo : hi;
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), ks & 63));
-  }
-};
 
 // LDS slot of a row's staged scale: wave row / ROWS, lane row % ROWS.
 template <int ROWS>

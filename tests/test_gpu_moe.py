@@ -182,6 +182,24 @@ def test_many_routes_fused_atomics():
     check(c, 64, 1, label="split many routes")
 
 
+@pytest.mark.parametrize("split", [1, 0])
+@pytest.mark.parametrize("bm", [16, 32])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8"])
+def test_ksplit_parity(kind, bm, split):
+    """Few (block, slice) tiles and at least 8 K steps: the up GEMM runs with
+    two K groups per workgroup; 9 K steps give the groups an uneven share."""
+    c = small_case(kind, T=20, E=8, k=2, K=1152, I=256)
+    check(c, bm, split, label="ksplit")
+
+
+def test_ksplit_deterministic():
+    c = small_case("mxfp8", T=20, E=8, k=2, K=1152, I=256)
+    a, _ = moe.run_case(c, block_m=16, split=1)
+    b, _ = moe.run_case(c, block_m=16, split=1)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 @pytest.mark.parametrize("bm", [64, 128, 256])
 @pytest.mark.parametrize("kind,K,I", [("fp8_blockwise", 768, 384), ("mxfp8", 512, 256),
                                       ("fp8_blockwise", 256, 128)])
