@@ -106,9 +106,10 @@ int moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
  * output; split=True writes the H-wide activation once and runs the down
  * projection with no split-K, trading one HBM round trip for a reduction
  * cost that grows with token count; [hpc-ops RFC] "Results so far": the
- * fused kernel helps small-token workloads).  The fused mode is picked for
- * T*top_k <= 512 when the intermediate has at least 8 slices of 128
- * columns (its grid is blocks x slices; fewer slices cannot fill the GPU).
+ * fused kernel helps small-token workloads).  On MI355X the split mode
+ * streams the weights faster wherever they set the time; the fused mode is
+ * picked only for T*top_k <= 512 with at most 32 MB of expert weights, where
+ * its one launch fewer matters.
  *   *split (host out) = 1 for split mode, 0 for the fused mode.
  * Errors: MOE_ERR_NULL.
  */

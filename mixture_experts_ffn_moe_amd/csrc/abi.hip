@@ -79,14 +79,17 @@ int check_ffn(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
 
 int pick_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
                int32_t block_m) {
-  (void)dtype; (void)K; (void)E;
   if (block_m == 256) return 1;
-  // The fused mode's split-K accumulation costs R*K*(I/128) fp32 atomic adds;
-  // it stays cheap against the weight stream only for decode-sized calls.
-  // Its grid is (blocks x I/128 slices): with few slices (a narrow
-  // intermediate) it cannot fill the GPU, and the split mode's down GEMM,
-  // tiled over the K output columns, streams the weights faster.
-  return (T * top_k <= 512 && N / 2 / 128 >= 8) ? 0 : 1;
+  // Measured on MI355X: wherever the weight stream sets the time the split
+  // mode is faster (its down GEMM streams W2 through the register ring,
+  // while the fused mode reads its W2 slice column chunk by chunk and adds
+  // R*K*(I/128) fp32 atomics); e.g. K=4096, I=2048, E=256, top-6: 219 vs
+  // 240 us at T=8, 833 vs 949 us at T=64.  The fused mode's one launch fewer
+  // wins only when the whole call is tiny (bf16 K=512, I=256, E=8, T=32:
+  // 37.5 vs 41.3 us).
+  const double weight_bytes =
+      (double)E * 3.0 * (double)K * (double)(N / 2) * (dtype == MOE_BF16 ? 2.0 : 1.0);
+  return (T * top_k <= 512 && weight_bytes <= 32e6) ? 0 : 1;
 }
 
 struct Layout {

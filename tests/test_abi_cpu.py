@@ -114,6 +114,7 @@ def test_heuristics():
     assert moe.moe_select_block_m(4096, 8, 288, "fp8_blockwise", 4096) == 64
     assert moe.moe_select_block_m(1024, 8, 288, "fp8_blockwise", 4096) == 64   # 28 rows/expert
     assert moe.moe_select_block_m(1024, 6, 384, "fp8_blockwise", 7168) == 16   # 16 rows/expert
-    assert moe.moe_select_split("fp8_blockwise", 8, 4096, 4096, 256, 6, 16) == 0
-    assert moe.moe_select_split("mxfp8", 8, 4096, 512, 32, 8, 16) == 1         # I = 256: 2 slices
+    assert moe.moe_select_split("fp8_blockwise", 8, 4096, 4096, 256, 6, 16) == 1  # 6.4 GB of weights
+    assert moe.moe_select_split("mxfp8", 8, 4096, 512, 32, 8, 16) == 1         # 100 MB
+    assert moe.moe_select_split("bf16", 32, 512, 512, 8, 2, 16) == 0            # 6.3 MB: fused
     assert moe.moe_select_split("fp8_blockwise", 8192, 4096, 4096, 288, 8, 128) == 1
