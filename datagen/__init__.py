@@ -16,6 +16,11 @@ the way an upstream caller would:
   - MX: one e8m0 exponent per 32 elements along the contraction dimension,
     exponent = floor(log2 amax) - 8 (OCP MX rule for e4m3), values saturated to
     +-448 and cast to e4m3.
+  - MXFP4 weights ([DeepGEMM #411] "Summary": packed E2M1 with a UE8M0
+    exponent per 32 along K): exponent = floor(log2 amax) - 2 (OCP MX rule
+    for E2M1, whose largest magnitude is 1.5 * 2^2), values rounded to the
+    nearest E2M1 magnitude with ties to the even code, saturated to +-6, two
+    codes per byte (element 2j in the low nibble).  Activations stay MX FP8.
   All done with torch tensor ops, on the CPU or on the GPU.
 
 Randomness: ``torch.Generator`` seeded from a CRC of (workload, tensor name,
@@ -55,6 +60,11 @@ WORKLOADS = {
     "mx-k4096-i256-e32-top8": dict(
         kind="mxfp8", K=4096, I=256, E=32, top_k=8,
         tokens=(8, 32, 128, 512), routing="uniform"),
+    # the DeepSeek-V4-Flash decode shape with MXFP4 weights and MX FP8
+    # activations (the weight format of the [DeepGEMM #411] page)
+    "mxfp4-k4096-i2048-e256-top6": dict(
+        kind="mxfp4", K=4096, I=2048, E=256, top_k=6,
+        tokens=(8, 64, 256), routing="uniform"),
 }
 
 
@@ -103,6 +113,30 @@ def quant_mx(w):
     scaled = torch.ldexp(wb, (-s).to(wb.dtype)[..., None])
     q = scaled.clamp(-448.0, 448.0).reshape(shp).to(torch.float8_e4m3fn)
     return q, (s + 127).to(torch.uint8)
+
+
+# E2M1 magnitudes by code and the midpoints between neighbouring codes
+_E2M1_MIDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def quant_mxfp4(w):
+    """(..., C) float32 -> (packed e2m1 uint8 (..., C/2), e8m0 uint8 (..., C/32))."""
+    shp = w.shape
+    wb = w.reshape(*shp[:-1], shp[-1] // 32, 32)
+    amax = wb.abs().amax(dim=-1)
+    _, ex = torch.frexp(amax)                 # amax = m * 2^ex, m in [0.5, 1)
+    s = (ex.to(torch.int32) - 1) - 2
+    s = torch.where(amax > 0, s.clamp(-127, 127), torch.full_like(s, -127))
+    a = torch.ldexp(wb.abs(), (-s).to(wb.dtype)[..., None])   # exact: power-of-two scale
+    mids = torch.tensor(_E2M1_MIDS, dtype=a.dtype, device=a.device)
+    code = torch.bucketize(a, mids)           # ties go to the lower code ...
+    lower = code.clamp(max=6)
+    tie = (code < 7) & (a == mids[lower]) & (code % 2 == 1)
+    code = code + tie.to(code.dtype)          # ... and to the upper one when it is even
+    code = code | torch.where(wb < 0, 8, 0).to(code.dtype)
+    code = code.to(torch.uint8).reshape(*shp[:-1], shp[-1] // 2, 2)
+    packed = code[..., 0] | (code[..., 1] << 4)
+    return packed, (s + 127).to(torch.uint8)
 
 
 # ---------------------------------------------------------------------------
@@ -163,7 +197,8 @@ def make_weights(kind, K, I, E, device="cpu", tag="w", w_std=None, chunk=8):
 
     bf16: w1 (E, 2I, K), w2 (E, K, I) bf16.  Blockwise: e4m3 values plus fp32
     scales (E, 2I/128, K/128) and (E, K/128, I/128).  MX: e4m3 values plus e8m0
-    scales (E, 2I, K/32) and (E, K, I/32).
+    scales (E, 2I, K/32) and (E, K, I/32).  MXFP4: packed e2m1 pairs
+    (E, 2I, K/2) and (E, K, I/2) plus the same e8m0 scale shapes as MX.
     """
     N = 2 * I
     if kind == "bf16":
@@ -174,8 +209,12 @@ def make_weights(kind, K, I, E, device="cpu", tag="w", w_std=None, chunk=8):
         w2 = (torch.randn(E, K, I, generator=g, device=device) * std).to(torch.bfloat16)
         return w1, None, w2, None
     std = (1.0 / K) ** 0.5 if w_std is None else w_std
-    w1 = torch.empty(E, N, K, dtype=torch.float8_e4m3fn, device=device)
-    w2 = torch.empty(E, K, I, dtype=torch.float8_e4m3fn, device=device)
+    if kind == "mxfp4":
+        w1 = torch.empty(E, N, K // 2, dtype=torch.uint8, device=device)
+        w2 = torch.empty(E, K, I // 2, dtype=torch.uint8, device=device)
+    else:
+        w1 = torch.empty(E, N, K, dtype=torch.float8_e4m3fn, device=device)
+        w2 = torch.empty(E, K, I, dtype=torch.float8_e4m3fn, device=device)
     if kind == "fp8_blockwise":
         s1 = torch.empty(E, N // 128, K // 128, dtype=torch.float32, device=device)
         s2 = torch.empty(E, K // 128, I // 128, dtype=torch.float32, device=device)
@@ -192,6 +231,9 @@ def make_weights(kind, K, I, E, device="cpu", tag="w", w_std=None, chunk=8):
             if kind == "fp8_blockwise":
                 w1[e], s1[e] = quant_blockwise_mat(a[e - e0])
                 w2[e], s2[e] = quant_blockwise_mat(b[e - e0])
+            elif kind == "mxfp4":
+                w1[e], s1[e] = quant_mxfp4(a[e - e0])
+                w2[e], s2[e] = quant_mxfp4(b[e - e0])
             else:
                 w1[e], s1[e] = quant_mx(a[e - e0])
                 w2[e], s2[e] = quant_mx(b[e - e0])

@@ -20,6 +20,13 @@ Formats
   [prime-flash] "Shapes" table: out is bf16; "Two data types" table: the bf16
   path.
 
+* e2m1 -- OCP MX FP4 element "E2M1": 1 sign bit, 2 exponent bits with bias 1,
+  1 mantissa bit; exponent field 0 holds the subnormal m * 0.5; no infinity
+  and no NaN, so the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  The
+  [DeepGEMM #411] page ("Summary") keeps routed weights as packed MXFP4:
+  E2M1 elements with one UE8M0 (= e8m0) exponent per 32 along K.  Packing:
+  two elements per byte, the one with the lower index in the low nibble.
+
 Rounding: every encoder rounds to nearest, ties to even, once, from the exact
 fp64 input.  e4m3 saturates to +-448 (the reading that an out-of-range
 product after scaling by 1/amax*448 must land on the largest code, since the
@@ -87,6 +94,35 @@ def e4m3_encode(values):
     code = np.where(sign, code | 0x80, code)
     code = np.where(nan, 0x7F, code)
     return code.astype(np.uint8)
+
+
+def _e2m1_decode_one(code):
+    """Value of one e2m1 code (0..15) from the bit fields."""
+    s = -1.0 if (code >> 3) & 1 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return s * m * 0.5                        # subnormal: m * 2^(1-1) * 0.5
+    return s * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+# 16-entry decode table built from the bit-field definition above.
+E2M1_TABLE = np.array([_e2m1_decode_one(c) for c in range(16)], dtype=np.float64)
+
+
+def fp4_unpack(packed):
+    """uint8 (..., C/2) packed e2m1 pairs -> uint8 codes (..., C): element 2j
+    from the low nibble of byte j, element 2j+1 from its high nibble."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = p & 0x0F
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def e2m1_decode(codes):
+    """uint8 e2m1 codes (0..15) -> fp64 values (exact)."""
+    return E2M1_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def e8m0_decode(codes):

@@ -87,7 +87,7 @@ def dequant_x(kind, x, x_scale, rows):
     v = codecs.e4m3_decode(x[rows])
     if kind == "fp8_blockwise":
         return v * np.repeat(x_scale[rows].astype(np.float64), 128, axis=1)
-    if kind == "mxfp8":
+    if kind in ("mxfp8", "mxfp4"):   # MXFP4 weights take MX FP8 activations
         return v * np.repeat(codecs.e8m0_decode(x_scale[rows]), 32, axis=1)
     raise ValueError(kind)
 
@@ -96,6 +96,9 @@ def dequant_w(kind, w, w_scale, e):
     """fp64 weight matrix of expert e (rows = output features)."""
     if kind == "bf16":
         return codecs.bf16_decode(w[e])
+    if kind == "mxfp4":
+        v = codecs.e2m1_decode(codecs.fp4_unpack(w[e]))
+        return v * np.repeat(codecs.e8m0_decode(w_scale[e]), 32, axis=1)
     v = codecs.e4m3_decode(w[e])
     if kind == "fp8_blockwise":
         s = w_scale[e].astype(np.float64)
@@ -200,7 +203,9 @@ def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
     Arrays are numpy: bf16 data as uint16 bit patterns, e4m3 data as uint8
     codes, blockwise scales as float32, MX scales as uint8 e8m0 codes.
     Shapes: x (T, K); w1 (E, N, K); w2 (E, K, N/2); topk_ids, topk_weights
-    (T, top_k).
+    (T, top_k).  ``mxfp4``: w1 (E, N, K/2) and w2 (E, K, N/4) packed e2m1
+    pairs with e8m0 scales (E, N, K/32) and (E, K, N/64); x is MX FP8 and the
+    intermediate is requantized to MX FP8, as on the mxfp8 path.
 
     ``tokens``: optional sorted array of token indices; only those outputs are
     computed (rows of the result follow that order).
@@ -220,7 +225,7 @@ def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
     wts = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
     T, k = ids.shape
     E = w1.shape[0]
-    K = w1.shape[2]
+    K = w1.shape[2] * (2 if kind == "mxfp4" else 1)
     I = w1.shape[1] // 2
     if tokens is None:
         tokens = np.arange(T)
@@ -234,7 +239,7 @@ def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
         requant = requant_bf16
     elif kind == "fp8_blockwise":
         requant = requant_blockwise
-    elif kind == "mxfp8":
+    elif kind in ("mxfp8", "mxfp4"):
         requant = requant_mx
     else:
         raise ValueError(kind)

@@ -150,3 +150,24 @@ def test_bf16_round_fp64_brute_force():
         assert d[1] <= d[0] and d[1] <= d[2]
         if d[1] == d[0] or d[1] == d[2]:
             assert b % 2 == 0
+
+
+def test_e2m1_decode_golden(gold):
+    for code, val in gold["e2m1_decode"].items():
+        got = codecs.e2m1_decode(np.array([_int(code)], np.uint8))[0]
+        want = _num(val)
+        assert got == want and math.copysign(1.0, got) == math.copysign(1.0, want), (code, got)
+
+
+def test_e2m1_table_shape():
+    t = codecs.E2M1_TABLE
+    assert np.all(np.isfinite(t))
+    assert np.array_equal(t[8:], -t[:8])                # sign bit
+    assert np.all(np.diff(t[:8]) > 0)                   # codes 0..7 ascend
+    assert t[:8].max() == 6.0 and t[1] == 0.5           # largest, smallest subnormal
+
+
+def test_fp4_unpack_nibble_order():
+    # element 2j in the low nibble of byte j, element 2j+1 in its high nibble
+    got = codecs.fp4_unpack(np.array([[0x5A, 0x0F]], np.uint8))
+    assert got.tolist() == [[0xA, 0x5, 0xF, 0x0]]

@@ -142,11 +142,20 @@ def brute_force(kind, d, t):
     x, xs, w1, s1, w2, s2 = d["x"], d["x_scale"], d["w1"], d["w1_scale"], d["w2"], d["w2_scale"]
     ids, wts = d["topk_ids"], d["topk_weights"]
     E, N, K = w1.shape
+    if kind == "mxfp4":
+        K *= 2
     I = N // 2
+
+    def fp4(byte, c):  # element c of a packed row: low nibble holds the even index
+        code = (byte >> 4) if c % 2 else (byte & 15)
+        mag = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0][code & 7]
+        return -mag if code & 8 else mag
 
     def deq(arr, scale, e, r, c, rowwise):
         if kind == "bf16":
             return float(codecs.bf16_decode(np.array([arr[e][r, c] if e is not None else arr[r, c]]))[0])
+        if kind == "mxfp4" and e is not None:
+            return fp4(int(arr[e][r, c // 2]), c) * 2.0 ** (int(scale[e][r, c // 32]) - 127)
         v = TABLE[arr[e][r, c] if e is not None else arr[r, c]]
         if kind == "fp8_blockwise":
             if rowwise:
@@ -182,7 +191,7 @@ def run(d, **kw):
 
 
 @pytest.mark.parametrize("kind,K,I", [("bf16", 64, 32), ("fp8_blockwise", 256, 128),
-                                      ("mxfp8", 64, 64)])
+                                      ("mxfp8", 64, 64), ("mxfp4", 64, 64)])
 def test_brute_force_per_token(kind, K, I):
     d = small_case(kind, 4, K, I, 4, 2)
     ref = run(d)["out64"]
@@ -217,7 +226,7 @@ def test_dense_ffn_special_case():
 
 
 @pytest.mark.parametrize("kind,K,I", [("bf16", 128, 64), ("fp8_blockwise", 256, 256),
-                                      ("mxfp8", 128, 64)])
+                                      ("mxfp8", 128, 64), ("mxfp4", 128, 64)])
 def test_linearity_in_routing_weights(kind, K, I):
     d = small_case(kind, 8, K, I, 6, 3)
     full = run(d)["out64"]
@@ -231,7 +240,7 @@ def test_linearity_in_routing_weights(kind, K, I):
     np.testing.assert_allclose(full, acc, rtol=1e-12, atol=1e-14 * np.abs(full).max())
 
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
 def test_empty_experts_contribute_nothing(kind):
     d = small_case(kind, 4, 256, 128, 16, 2)
     base = run(d)["out64"]
@@ -363,3 +372,21 @@ def test_flip_bound_covers_fp32_deviation(kind, K, I, T):
     if kind == "fp8_blockwise":
         _, strict = tolerance_check(got, base["out64"], tol, None)
         assert strict["n_over_bound"] > 0
+
+
+def test_mxfp4_equals_mxfp8_on_exact_reencoding():
+    """Every E2M1 value is exact in e4m3: MXFP4 weights re-encoded as MX FP8
+    codes with the same e8m0 exponents describe the same numbers, so both
+    paths must give bit-identical results (pins the MXFP4 weight decode to the
+    pinned MX FP8 path)."""
+    d = small_case("mxfp4", 5, 128, 64, 3, 2)
+    out4 = run(d)
+    d8 = dict(d)
+    d8["kind"] = "mxfp8"
+    for wk in ("w1", "w2"):
+        d8[wk] = codecs.e4m3_encode(codecs.e2m1_decode(codecs.fp4_unpack(d[wk])))
+    assert np.array_equal(codecs.e4m3_decode(d8["w1"]),
+                          codecs.e2m1_decode(codecs.fp4_unpack(d["w1"])))
+    out8 = run(d8)
+    assert np.array_equal(out4["out64"], out8["out64"])
+    assert np.array_equal(out4["out_bf16"], out8["out_bf16"])

@@ -27,6 +27,9 @@ def _pins():
         tm.test_dense_ffn_special_case,
         lambda: tm.test_brute_force_per_token("fp8_blockwise", 128, 128),
         lambda: tm.test_brute_force_per_token("mxfp8", 64, 32),
+        lambda: tm.test_brute_force_per_token("mxfp4", 64, 64),
+        lambda: tc.test_e2m1_decode_golden(tc.gold.__wrapped__()),
+        tc.test_fp4_unpack_nibble_order,
         _square_brute,
     ]
     failed = 0
@@ -79,9 +82,29 @@ def _decode_bias8(codes):
     return ORIG["e4m3_decode"](codes) * 0.5
 
 
+def _fp4_nibbles_swapped(packed):
+    out = ORIG["fp4_unpack"](packed)
+    return out.reshape(out.shape[:-1] + (-1, 2))[..., ::-1].reshape(out.shape)
+
+
+def _e2m1_bias2(codes):
+    # exponent bias 2 instead of 1: every normal value halves
+    v = ORIG["e2m1_decode"](codes)
+    return np.where(np.abs(v) >= 1.0, v * 0.5, v)
+
+
+def _mxfp4_scale_per_16(kind, w, w_scale, e):
+    if kind != "mxfp4":
+        return ORIG["dequant_w"](kind, w, w_scale, e)
+    v = codecs.e2m1_decode(codecs.fp4_unpack(w[e]))
+    sc = np.repeat(codecs.e8m0_decode(w_scale[e]), 16, axis=1)
+    return v * np.concatenate([sc, sc], axis=1)[:, :v.shape[1]]
+
+
 ORIG = {"requant_blockwise": moe.requant_blockwise, "requant_mx": moe.requant_mx,
         "dequant_w": moe.dequant_w, "dequant_x": moe.dequant_x,
-        "e4m3_decode": codecs.e4m3_decode}
+        "e4m3_decode": codecs.e4m3_decode, "fp4_unpack": codecs.fp4_unpack,
+        "e2m1_decode": codecs.e2m1_decode}
 
 MUTATIONS = {
     "gate_up_swapped": (moe, "_swiglu", _swap_gate_up),
@@ -91,6 +114,9 @@ MUTATIONS = {
     "w2_transposed": (moe, "dequant_w", _dequant_w_T),
     "x_columns_permuted": (moe, "dequant_x", _dequant_x_wrong_block),
     "e4m3_bias_8": (codecs, "e4m3_decode", _decode_bias8),
+    "fp4_nibbles_swapped": (codecs, "fp4_unpack", _fp4_nibbles_swapped),
+    "e2m1_bias_2": (codecs, "e2m1_decode", _e2m1_bias2),
+    "mxfp4_scale_block_16": (moe, "dequant_w", _mxfp4_scale_per_16),
 }
 
 
