@@ -32,8 +32,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_blockwise": 5000.0, "mxfp8": 5000.0}
-DTYPE_NAME = {"bf16": "bf16", "fp8_blockwise": "e4m3/fp32-blockwise", "mxfp8": "e4m3/e8m0-mx"}
+# dense MFMA peaks; an e4m3 x e2m1 product issues at the e4m3 rate
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_blockwise": 5000.0, "mxfp8": 5000.0, "mxfp4": 5000.0}
+DTYPE_NAME = {"bf16": "bf16", "fp8_blockwise": "e4m3/fp32-blockwise", "mxfp8": "e4m3/e8m0-mx",
+              "mxfp4": "e2m1/e8m0-mx weights x e4m3/e8m0-mx activations"}
 METRIC = ("fused MoE fwd µs and TFLOP/s (% FP8 MFMA / % HBM roofline) vs tokens T")
 KERNEL_SOURCES = ["mixture_experts_ffn_moe_amd/csrc/moe_kernels.hip",
                   "mixture_experts_ffn_moe_amd/csrc/device.h"]
@@ -82,6 +84,9 @@ def byte_model(kind, K, I, E_act, T, R, split):
     es = 2 if kind == "bf16" else 1
     if kind == "bf16":
         w1e, w2e = N * K * 2, K * I * 2
+    elif kind == "mxfp4":
+        w1e = N * K // 2 + N * (K // 32)
+        w2e = K * I // 2 + K * (I // 32)
     elif kind == "fp8_blockwise":
         w1e = N * K + (N // 128) * (K // 128) * 4
         w2e = K * I + (K // 128) * (I // 128) * 4

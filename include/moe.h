@@ -57,7 +57,8 @@ typedef enum {
 typedef enum {
   MOE_BF16 = 0,          /* bf16 x, w1, w2; fp32 accumulate */
   MOE_FP8_BLOCKWISE = 1, /* e4m3 with fp32 scales per 1x128 (x) and 128x128 (w) */
-  MOE_MXFP8 = 2          /* e4m3 with e8m0 scales per 32 along the contraction */
+  MOE_MXFP8 = 2,         /* e4m3 with e8m0 scales per 32 along the contraction */
+  MOE_MXFP4 = 3          /* weights e2m1 + e8m0 per 32; activations as MOE_MXFP8 */
 } moe_dtype;
 
 /* Message describing the last error of the calling thread ("" if none). */
@@ -223,6 +224,27 @@ int fused_moe_fp8_blockwise(const void* x, const float* x_scale,
  *   w1 (E, N, K) e4m3, w1_scale (E, N, K/32) e8m0;
  *   w2 (E, K, N/2) e4m3, w2_scale (E, K, (N/2)/32) e8m0. */
 int fused_moe_mxfp8(const void* x, const uint8_t* x_scale, const void* w1,
+                    const uint8_t* w1_scale, const void* w2,
+                    const uint8_t* w2_scale, const int32_t* sorted_token_ids,
+                    const int32_t* expert_ids,
+                    const int32_t* num_tokens_post_padded,
+                    const float* topk_weights, void* out, int64_t T, int64_t K,
+                    int64_t N, int32_t E, int32_t top_k, int32_t block_m,
+                    int32_t split, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* MXFP4 weights x MX FP8 activations ([DeepGEMM #411] "Summary": routed
+ * weights stay packed MXFP4 in memory, E2M1 elements with one UE8M0 exponent
+ * per 32 along K; activations FP8).  The e2m1 elements (OCP MX FP4: 1 sign,
+ * 2 exponent bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2,
+ * 3, 4, 6) are packed two per byte, element 2j in the low nibble of byte j,
+ * along the contraction dimension.  Activations and the on-chip intermediate
+ * are MX FP8 exactly as in fused_moe_mxfp8 (workspace as for MOE_MXFP8).
+ *   x (T, K) e4m3, x_scale (T, K/32) e8m0;
+ *   w1 (E, N, K/2) bytes, w1_scale (E, N, K/32) e8m0;
+ *   w2 (E, K, (N/2)/2) bytes, w2_scale (E, K, (N/2)/32) e8m0.
+ * block_m 256 is not available for this dtype (MOE_ERR_UNSUPPORTED). */
+int fused_moe_mxfp4(const void* x, const uint8_t* x_scale, const void* w1,
                     const uint8_t* w1_scale, const void* w2,
                     const uint8_t* w2_scale, const int32_t* sorted_token_ids,
                     const int32_t* expert_ids,

@@ -14,6 +14,7 @@ Entry points (same names as the C ABI):
                  num_tokens_post_padded, topk_weights, top_k, block_m, ...)
   fused_moe_fp8_blockwise(x, x_scale, w1, w1_scale, w2, w2_scale, ...)
   fused_moe_mxfp8(x, x_scale, w1, w1_scale, w2, w2_scale, ...)
+  fused_moe_mxfp4(x, x_scale, w1, w1_scale, w2, w2_scale, ...)   (packed e2m1 weights)
 plus the host helpers moe_align_capacity, moe_workspace_size,
 moe_workspace_layout, moe_select_split and moe_select_block_m.
 """
@@ -24,21 +25,23 @@ import os
 import torch
 
 __all__ = [
-    "MoeError", "lib", "LIB_PATH", "MOE_BF16", "MOE_FP8_BLOCKWISE", "MOE_MXFP8",
+    "MoeError", "lib", "LIB_PATH", "MOE_BF16", "MOE_FP8_BLOCKWISE", "MOE_MXFP8", "MOE_MXFP4",
     "moe_align_capacity", "moe_align", "moe_select_split", "moe_select_block_m",
     "moe_workspace_size", "moe_workspace_layout", "fused_moe_bf16",
-    "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "EXPORTED_SYMBOLS",
+    "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
-MOE_BF16, MOE_FP8_BLOCKWISE, MOE_MXFP8 = 0, 1, 2
-_DTYPE_CODE = {"bf16": MOE_BF16, "fp8_blockwise": MOE_FP8_BLOCKWISE, "mxfp8": MOE_MXFP8}
+MOE_BF16, MOE_FP8_BLOCKWISE, MOE_MXFP8, MOE_MXFP4 = 0, 1, 2, 3
+_DTYPE_CODE = {"bf16": MOE_BF16, "fp8_blockwise": MOE_FP8_BLOCKWISE, "mxfp8": MOE_MXFP8,
+               "mxfp4": MOE_MXFP4}
 
 EXPORTED_SYMBOLS = (
     "moe_last_error", "moe_align_capacity", "moe_align", "moe_select_split",
     "moe_select_block_m", "moe_workspace_size", "moe_workspace_layout",
-    "fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "moe_set_timing_events",
+    "fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4",
+    "moe_set_timing_events",
 )
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
@@ -84,6 +87,7 @@ def lib():
     L.fused_moe_bf16.argtypes = [_P, _P, _P] + tail
     L.fused_moe_fp8_blockwise.argtypes = [_P, _P, _P, _P, _P, _P] + tail
     L.fused_moe_mxfp8.argtypes = [_P, _P, _P, _P, _P, _P] + tail
+    L.fused_moe_mxfp4.argtypes = [_P, _P, _P, _P, _P, _P] + tail
     L.moe_set_timing_events.argtypes = [_P, _P, _I32]
     for name in EXPORTED_SYMBOLS:
         if name != "moe_last_error":
@@ -215,6 +219,16 @@ def fused_moe_mxfp8(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, ex
                 block_m, split, out, workspace, stream, T, K)
 
 
+def fused_moe_mxfp4(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
+                    num_tokens_post_padded, topk_weights, top_k, block_m, split=-1, out=None,
+                    workspace=None, stream=None):
+    """w1 (E, N, K/2) and w2 (E, K, N/4) uint8: packed e2m1 pairs."""
+    T, K = x.shape
+    return _run(lib().fused_moe_mxfp4, MOE_MXFP4, [x, x_scale, w1, w1_scale, w2, w2_scale], w1,
+                sorted_token_ids, expert_ids, num_tokens_post_padded, topk_weights, top_k,
+                block_m, split, out, workspace, stream, T, K)
+
+
 def run_case(case, block_m=None, split=-1, stream=None, workspace=None, out=None,
              align_out=None):
     """Planner + forward for a ``datagen.Case``-like object (attributes kind,
@@ -231,7 +245,10 @@ def run_case(case, block_m=None, split=-1, stream=None, workspace=None, out=None
     elif case.kind == "fp8_blockwise":
         o = fused_moe_fp8_blockwise(case.x, case.x_scale, case.w1, case.w1_scale, case.w2,
                                     case.w2_scale, *align, case.topk_weights, **args)
-    else:
+    elif case.kind == "mxfp8":
         o = fused_moe_mxfp8(case.x, case.x_scale, case.w1, case.w1_scale, case.w2,
+                            case.w2_scale, *align, case.topk_weights, **args)
+    else:
+        o = fused_moe_mxfp4(case.x, case.x_scale, case.w1, case.w1_scale, case.w2,
                             case.w2_scale, *align, case.topk_weights, **args)
     return o, align

@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "../../include/moe.h"
+#include "device.h"
 #include "launch.h"
 
 namespace {
@@ -54,7 +55,7 @@ int check_ffn(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
               int32_t block_m) {
   int rc = check_routes(T, top_k, E);
   if (rc) return rc;
-  if (dtype < MOE_BF16 || dtype > MOE_MXFP8) return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (dtype < MOE_BF16 || dtype > MOE_MXFP4) return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   if (K <= 0 || N <= 0) return fail(MOE_ERR_SHAPE, "K and N must be > 0");
   if (N % 2) return fail(MOE_ERR_SHAPE, "N (fused gate+up width) must be even");
   if (K % 128) return fail(MOE_ERR_UNSUPPORTED, "K must be a multiple of 128 (got %lld)", (long long)K);
@@ -65,8 +66,8 @@ int check_ffn(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
     return fail(MOE_ERR_UNSUPPORTED, "blockwise FP8 needs K and I = N/2 <= 16384");
   if (!valid_block_m(block_m))
     return fail(MOE_ERR_UNSUPPORTED, "block_m must be 16, 32, 64, 128 or 256 (got %d)", block_m);
-  if (block_m == 256 && (dtype == MOE_BF16 || K % 256))
-    return fail(MOE_ERR_UNSUPPORTED, "block_m 256 needs an e4m3 dtype and K %% 256 == 0");
+  if (block_m == 256 && (dtype == MOE_BF16 || dtype == MOE_MXFP4 || K % 256))
+    return fail(MOE_ERR_UNSUPPORTED, "block_m 256 needs e4m3 weights and K %% 256 == 0");
   // 32-bit offsets inside one expert's weights and element indices of out
   if (N * K >= (int64_t(1) << 31) || T * K >= (int64_t(1) << 31))
     return fail(MOE_ERR_UNSUPPORTED, "per-expert weight or output element count must be < 2^31");
@@ -88,7 +89,8 @@ int pick_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_
   // wins only when the whole call is tiny (bf16 K=512, I=256, E=8, T=32:
   // 37.5 vs 41.3 us).
   const double weight_bytes =
-      (double)E * 3.0 * (double)K * (double)(N / 2) * (dtype == MOE_BF16 ? 2.0 : 1.0);
+      (double)E * 3.0 * (double)K * (double)(N / 2) *
+      (dtype == MOE_BF16 ? 2.0 : dtype == MOE_MXFP4 ? 0.5 : 1.0);
   return (T * top_k <= 512 && weight_bytes <= 32e6) ? 0 : 1;
 }
 
@@ -113,7 +115,7 @@ Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
     off = round_up(off + (size_t)rows * I * es, 256);
     L.hs = off;
     if (dtype == MOE_FP8_BLOCKWISE) off = round_up(off + (size_t)rows * (I / 128) * 4, 256);
-    if (dtype == MOE_MXFP8) off = round_up(off + (size_t)rows * (I / 32), 256);
+    if (dtype == MOE_MXFP8 || dtype == MOE_MXFP4) off = round_up(off + (size_t)rows * (I / 32), 256);
     if (dtype == MOE_BF16) L.hs = L.hq;
     L.yr = off;
     off = round_up(off + R * (size_t)K * 4, 256);
@@ -180,7 +182,10 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
   a.E = E;
   a.top_k = top_k;
   a.blocks_cap = (int)blocks;
-  const int kind = dtype;  // MOE_BF16 / MOE_FP8_BLOCKWISE / MOE_MXFP8 match the kernel kinds
+  static_assert(MOE_BF16 == KIND_BF16 && MOE_FP8_BLOCKWISE == KIND_FP8B && MOE_MXFP8 == KIND_MX &&
+                    MOE_MXFP4 == KIND_MX4,
+                "the moe_dtype values are the kernel kinds");
+  const int kind = dtype;
   hipError_t e = launch_moe(kind, block_m, sp, a, static_cast<hipStream_t>(stream), g_hook);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -310,6 +315,17 @@ int fused_moe_mxfp8(const void* x, const uint8_t* x_scale, const void* w1, const
                     int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* workspace,
                     size_t workspace_bytes, void* stream) {
   return run_ffn(MOE_MXFP8, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
+                 num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m, split,
+                 workspace, workspace_bytes, stream);
+}
+
+int fused_moe_mxfp4(const void* x, const uint8_t* x_scale, const void* w1, const uint8_t* w1_scale,
+                    const void* w2, const uint8_t* w2_scale, const int32_t* sorted_token_ids,
+                    const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                    const float* topk_weights, void* out, int64_t T, int64_t K, int64_t N,
+                    int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return run_ffn(MOE_MXFP4, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
                  num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m, split,
                  workspace, workspace_bytes, stream);
 }

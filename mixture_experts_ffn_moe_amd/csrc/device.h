@@ -20,8 +20,19 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-enum : int { KIND_BF16 = 0, KIND_FP8B = 1, KIND_MX = 2 };
+// KIND_MX4: MXFP4 weights (packed e2m1, two per byte, element 2j in the low
+// nibble, e8m0 per 32 along K) against MX FP8 activations.  Measured on
+// gfx950 with a one-wave in-bounds probe: with B in format e2m1 (blgp = 4)
+// the instruction reads four registers per lane; lane (column l % 16, group
+// g = l / 16) holds K [32g, 32g + 32) of the step, lower index in the low
+// nibble, and its e8m0 scale covers exactly that K block.  A keeps the e4m3
+// layout above.  So a weight row's step is one 64-byte chunk at 16 * g.
+enum : int { KIND_BF16 = 0, KIND_FP8B = 1, KIND_MX = 2, KIND_MX4 = 3 };
 
+// e8m0 block scales go into the MFMA (MX activations)
+constexpr bool is_mx(int kind) { return kind == KIND_MX || kind == KIND_MX4; }
+
+// A operand (activations, intermediate): bf16 or e4m3
 template <int KIND>
 struct KindTraits {
   static constexpr int ES = (KIND == KIND_BF16) ? 2 : 1;  // bytes per element
@@ -29,10 +40,26 @@ struct KindTraits {
   static constexpr int STEP_BYTES = 128 * ES;                 // bytes of one row per K step
 };
 
+// B operand (weights): as A except for MXFP4
+template <int KIND>
+struct BTraits {
+  static constexpr int NCHUNK = KIND == KIND_MX4 ? 1 : KindTraits<KIND>::NCHUNK;
+  static constexpr int STEP_BYTES = KIND == KIND_MX4 ? 64 : KindTraits<KIND>::STEP_BYTES;
+  // bytes of a weight row of `len` elements
+  static constexpr size_t row_bytes(size_t len) {
+    return KIND == KIND_MX4 ? len / 2 : len * KindTraits<KIND>::ES;
+  }
+};
+
 // One lane's share of a 16-row (or 16-column) operand for one 128-wide K step.
 template <int KIND>
 struct Frag {
   uint4 c[KindTraits<KIND>::NCHUNK];
+};
+
+template <int KIND>
+struct FragB {
+  uint4 c[BTraits<KIND>::NCHUNK];
 };
 
 // Buffer resource over [base, base + bytes): loads past the end return 0.
@@ -63,6 +90,13 @@ __device__ __forceinline__ void load_frag(Frag<KIND>& f, __amdgpu_buffer_rsrc_t 
 }
 
 template <int KIND>
+__device__ __forceinline__ void load_frag_b(FragB<KIND>& f, __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                            uint32_t soff) {
+#pragma unroll
+  for (int c = 0; c < BTraits<KIND>::NCHUNK; ++c) f.c[c] = buf_load16(r, voff + c * 64, soff);
+}
+
+template <int KIND>
 __device__ __forceinline__ void load_frag_ptr(Frag<KIND>& f, const uint8_t* row_step_ptr, int g) {
 #pragma unroll
   for (int c = 0; c < KindTraits<KIND>::NCHUNK; ++c)
@@ -87,8 +121,8 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
 }
 
 // acc += A . B over one 128-wide K step, no scales (bf16 and e4m3).
-template <int KIND>
-__device__ __forceinline__ f32x4 mfma_step(const Frag<KIND>& a, const Frag<KIND>& b, f32x4 acc) {
+template <int KIND, class FB>
+__device__ __forceinline__ f32x4 mfma_step(const Frag<KIND>& a, const FB& b, f32x4 acc) {
   if constexpr (KIND == KIND_BF16) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -108,6 +142,25 @@ __device__ __forceinline__ f32x4 mfma_step_mx(const Frag<KIND_MX>& a, const Frag
                                               f32x4 acc, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
       as_i32x8(a.c[0], a.c[1]), as_i32x8(b.c[0], b.c[1]), acc, 0, 0, 0, sa, 0, sb);
+}
+
+// The same with B in e2m1 (format 4: only the first four registers are read).
+__device__ __forceinline__ f32x4 mfma_step_mx4(const Frag<KIND_MX4>& a, const FragB<KIND_MX4>& b,
+                                               f32x4 acc, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+      as_i32x8(a.c[0], a.c[1]), as_i32x8(b.c[0], make_uint4(0, 0, 0, 0)), acc, 0, 4, 0, sa, 0, sb);
+}
+
+// MX-scaled step for either MX kind (the B fragment type follows the kind).
+template <int KIND>
+__device__ __forceinline__ f32x4 mfma_step_scaled(const Frag<KIND>& a, const FragB<KIND>& b,
+                                                  f32x4 acc, int sa, int sb) {
+  if constexpr (KIND == KIND_MX4) {
+    return mfma_step_mx4(a, b, acc, sa, sb);
+  } else {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+        as_i32x8(a.c[0], a.c[1]), as_i32x8(b.c[0], b.c[1]), acc, 0, 0, 0, sa, 0, sb);
+  }
 }
 
 // silu(g) * u in fp32: g / (1 + 2^(-g*log2 e)) with the hardware exp2 and an

@@ -60,7 +60,7 @@ struct Operand {
 template <int KIND, int MI, int NI, int D>
 struct Ring {
   Frag<KIND> fa[D][MI];
-  Frag<KIND> fb[D][NI];
+  FragB<KIND> fb[D][NI];
   float sa[D][MI][4];
   int xa[D][MI];
   int xb[D][NI];
@@ -73,14 +73,15 @@ __device__ __forceinline__ void ring_load(Ring<KIND, MI, NI, D>& r, int slot, in
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) load_frag<KIND>(r.fa[slot][mi], op.ra, op.a[mi], soff);
 #pragma unroll
-  for (int ni = 0; ni < NI; ++ni) load_frag<KIND>(r.fb[slot][ni], op.rb, op.b[ni], soff);
+  for (int ni = 0; ni < NI; ++ni)
+    load_frag_b<KIND>(r.fb[slot][ni], op.rb, op.b[ni], (uint32_t)ks * BTraits<KIND>::STEP_BYTES);
   if constexpr (KIND == KIND_FP8B) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int i = 0; i < 4; ++i) r.sa[slot][mi][i] = buf_loadf(op.rsa, op.as[mi][i], ks * 4);
   }
-  if constexpr (KIND == KIND_MX) {
+  if constexpr (is_mx(KIND)) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) r.xa[slot][mi] = buf_loadu8(op.rxa, op.ax[mi], ks * 4);
 #pragma unroll
@@ -106,13 +107,13 @@ __device__ __forceinline__ void ring_compute(const Ring<KIND, MI, NI, D>& r, int
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[mi][ni][i] += t[i] * (r.sa[slot][mi][i] * w);
       }
-  } else if constexpr (KIND == KIND_MX) {
+  } else if constexpr (is_mx(KIND)) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = mfma_step_mx(r.fa[slot][mi], r.fb[slot][ni], acc[mi][ni], r.xa[slot][mi],
-                                   r.xb[slot][ni]);
+        acc[mi][ni] = mfma_step_scaled<KIND>(r.fa[slot][mi], r.fb[slot][ni], acc[mi][ni],
+                                             r.xa[slot][mi], r.xb[slot][ni]);
   } else {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -219,9 +220,10 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const in
   const int KS = K / 128, S = I / kSlice;
   Operand<MI, 4> op;
   op.ra = make_rsrc(p.x, (uint32_t)((size_t)p.T * K * ES));
-  op.rb = make_rsrc(p.w1 + (size_t)e * N * K * ES, (uint32_t)((size_t)N * K * ES));
+  op.rb = make_rsrc(p.w1 + (size_t)e * N * BTraits<KIND>::row_bytes(K),
+                    (uint32_t)(N * BTraits<KIND>::row_bytes(K)));
   if constexpr (KIND == KIND_FP8B) op.rsa = make_rsrc(p.xs, (uint32_t)((size_t)p.T * KS * 4));
-  if constexpr (KIND == KIND_MX) {
+  if constexpr (is_mx(KIND)) {
     op.rxa = make_rsrc(p.xs, (uint32_t)((size_t)p.T * (K / 32)));
     op.rxb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w1s) + (size_t)e * N * (K / 32),
                        (uint32_t)((size_t)N * (K / 32)));
@@ -238,14 +240,14 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const in
         op.as[mi][i] = (uint32_t)token_of(ids[crow], p.top_k) * KS * 4;
       }
     }
-    if constexpr (KIND == KIND_MX) op.ax[mi] = (uint32_t)tok * (K / 32) + g;
+    if constexpr (is_mx(KIND)) op.ax[mi] = (uint32_t)tok * (K / 32) + g;
   }
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int n = (ni < 2 ? 0 : I) + s * kSlice + 32 * wn + 16 * (ni & 1) + r16;
-    op.b[ni] = (uint32_t)n * K * ES + 16 * g;
+    op.b[ni] = (uint32_t)(n * BTraits<KIND>::row_bytes(K)) + 16 * g;
     if constexpr (KIND == KIND_FP8B) op.bsel[ni] = ni < 2 ? 0 : 1;  // gate block, up block
-    if constexpr (KIND == KIND_MX) op.bx[ni] = (uint32_t)n * (K / 32) + g;
+    if constexpr (is_mx(KIND)) op.bx[ni] = (uint32_t)n * (K / 32) + g;
   }
   if constexpr (KIND == KIND_FP8B) {
     op.bsrow[0] = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + s) * KS;
@@ -408,7 +410,7 @@ k_up(MoeArgs p) {
         if constexpr (KIND == KIND_FP8B) {
           if (wn == 0) reinterpret_cast<float*>(p.hs)[pos * (I / 128) + s] = sf[mi][i];
         }
-        if constexpr (KIND == KIND_MX) p.hs[pos * (I / 32) + s * 4 + wn] = (uint8_t)sx[mi][i];
+        if constexpr (is_mx(KIND)) p.hs[pos * (I / 32) + s * 4 + wn] = (uint8_t)sx[mi][i];
       }
     }
   if (s == 0 && threadIdx.x < BM) {
@@ -439,10 +441,11 @@ k_down(MoeArgs p) {
   const int IS = I / 128;
   Operand<MI, 4> op;
   op.ra = make_rsrc(p.hq, (uint32_t)((size_t)p.blocks_cap * BM * I * ES));
-  op.rb = make_rsrc(p.w2 + (size_t)e * K * I * ES, (uint32_t)((size_t)K * I * ES));
+  op.rb = make_rsrc(p.w2 + (size_t)e * K * BTraits<KIND>::row_bytes(I),
+                    (uint32_t)(K * BTraits<KIND>::row_bytes(I)));
   if constexpr (KIND == KIND_FP8B)
     op.rsa = make_rsrc(p.hs, (uint32_t)((size_t)p.blocks_cap * BM * IS * 4));
-  if constexpr (KIND == KIND_MX) {
+  if constexpr (is_mx(KIND)) {
     op.rxa = make_rsrc(p.hs, (uint32_t)((size_t)p.blocks_cap * BM * (I / 32)));
     op.rxb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w2s) + (size_t)e * K * (I / 32),
                        (uint32_t)((size_t)K * (I / 32)));
@@ -458,14 +461,14 @@ k_down(MoeArgs p) {
         op.as[mi][i] = cpos * IS * 4;
       }
     }
-    if constexpr (KIND == KIND_MX) op.ax[mi] = pos * (I / 32) + g;
+    if constexpr (is_mx(KIND)) op.ax[mi] = pos * (I / 32) + g;
   }
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int c = c0 + 16 * ni + r16;
-    op.b[ni] = (uint32_t)c * I * ES + 16 * g;
+    op.b[ni] = (uint32_t)(c * BTraits<KIND>::row_bytes(I)) + 16 * g;
     if constexpr (KIND == KIND_FP8B) op.bsel[ni] = 0;
-    if constexpr (KIND == KIND_MX) op.bx[ni] = (uint32_t)c * (I / 32) + g;
+    if constexpr (is_mx(KIND)) op.bx[ni] = (uint32_t)c * (I / 32) + g;
   }
   if constexpr (KIND == KIND_FP8B) {
     op.bsrow[0] = reinterpret_cast<const float*>(p.w2s) + ((size_t)e * (K / 128) + c0 / 128) * IS;
@@ -562,7 +565,7 @@ k_fused(MoeArgs p) {
           if constexpr (KIND == KIND_FP8B) {
             if (wn == 0) lds_sf[row] = sf[mi][i];
           }
-          if constexpr (KIND == KIND_MX) lds_sx[row * 4 + wn] = (uint8_t)sx[mi][i];
+          if constexpr (is_mx(KIND)) lds_sx[row * 4 + wn] = (uint8_t)sx[mi][i];
         }
       }
   }
@@ -580,7 +583,7 @@ k_fused(MoeArgs p) {
 #pragma unroll
     for (int c = 0; c < KindTraits<KIND>::NCHUNK; ++c)
       fa[mi].c[c] = *reinterpret_cast<const uint4*>(lds_q + row * QROW + c * 64 + 16 * g);
-    if constexpr (KIND == KIND_MX) xa[mi] = lds_sx[row * 4 + g];
+    if constexpr (is_mx(KIND)) xa[mi] = lds_sx[row * 4 + g];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int crow = wm * 64 + mi * 16 + 4 * g + i;
@@ -593,19 +596,20 @@ k_fused(MoeArgs p) {
   const int IS = I / 128;
   const int nchunks = K / 64;  // 64-column chunks, round-robin over the wave columns
   const __amdgpu_buffer_rsrc_t rw2 =
-      make_rsrc(p.w2 + (size_t)e * K * I * ES, (uint32_t)((size_t)K * I * ES));
-  const uint32_t soff = (uint32_t)s * kSlice * ES;
+      make_rsrc(p.w2 + (size_t)e * K * BTraits<KIND>::row_bytes(I),
+                (uint32_t)(K * BTraits<KIND>::row_bytes(I)));
+  const uint32_t soff = (uint32_t)s * BTraits<KIND>::STEP_BYTES;  // this slice's K step of w2 rows
   const int qrot = stagger_wg(nchunks);
   for (int qi = wn + 4 * kg; qi < nchunks; qi += 4 * KSPLIT) {
     const int q = (qi + qrot) % nchunks;  // staggered start, see stagger_wg()
     const int c0 = q * 64;
-    Frag<KIND> fb[4];
+    FragB<KIND> fb[4];
     int xb[4];
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
       const int c = c0 + 16 * ni + r16;
-      load_frag<KIND>(fb[ni], rw2, (uint32_t)c * I * ES + 16 * g, soff);
-      if constexpr (KIND == KIND_MX)
+      load_frag_b<KIND>(fb[ni], rw2, (uint32_t)(c * BTraits<KIND>::row_bytes(I)) + 16 * g, soff);
+      if constexpr (is_mx(KIND))
         xb[ni] = reinterpret_cast<const uint8_t*>(p.w2s)[((size_t)e * K + c) * (I / 32) + 4 * s + g];
     }
     float swb = 1.f;
@@ -616,8 +620,8 @@ k_fused(MoeArgs p) {
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (KIND == KIND_MX)
-          y = mfma_step_mx(fa[mi], fb[ni], y, xa[mi], xb[ni]);
+        if constexpr (is_mx(KIND))
+          y = mfma_step_scaled<KIND>(fa[mi], fb[ni], y, xa[mi], xb[ni]);
         else
           y = mfma_step<KIND>(fa[mi], fb[ni], y);
         const int c = c0 + 16 * ni + r16;
@@ -662,7 +666,11 @@ template <int KIND, int BM, int KSPLIT = 1>
 constexpr int prefetch_depth() {
   // two K groups put two waves on each SIMD, which halves each wave's
   // registers (four groups would leave too few for any prefetch)
+  // An MXFP4 step moves half the weight bytes in half the registers, so its
+  // ring holds more steps to keep the same bytes in flight.
   if constexpr (KIND == KIND_BF16) return BM <= 32 && KSPLIT == 1 ? 2 : 1;
+  else if constexpr (KIND == KIND_MX4 && KSPLIT == 2) return BM == 16 ? 4 : 3;
+  else if constexpr (KIND == KIND_MX4) return BM == 16 ? 6 : BM == 32 ? 4 : BM == 64 ? 3 : 2;
   else if constexpr (KSPLIT == 2) return BM == 16 ? 3 : 2;
   else return BM == 16 ? 4 : BM == 32 ? 3 : BM == 64 ? 2 : 1;
 }
@@ -779,6 +787,7 @@ hipError_t launch_moe(int kind, int block_m, int split, const MoeArgs& a, hipStr
     case KIND_BF16: return launch_kind<KIND_BF16>(block_m, split, a, st, hk);
     case KIND_FP8B: return launch_kind<KIND_FP8B>(block_m, split, a, st, hk);
     case KIND_MX: return launch_kind<KIND_MX>(block_m, split, a, st, hk);
+    case KIND_MX4: return launch_kind<KIND_MX4>(block_m, split, a, st, hk);
     default: return hipErrorInvalidValue;
   }
 }

@@ -12,7 +12,7 @@ from oracle.moe import moe_ref, tolerance_check
 
 # max |err| <= TOL * rms(out_oracle) (+ half a bf16 ulp), mean relative error
 # <= 5e-3: the bounds of the fused-MoE parity requirement for FP8 and bf16.
-TOL = {"bf16": 5e-3, "fp8_blockwise": 2e-2, "mxfp8": 2e-2}
+TOL = {"bf16": 5e-3, "fp8_blockwise": 2e-2, "mxfp8": 2e-2, "mxfp4": 2e-2}
 
 
 def say(*a):

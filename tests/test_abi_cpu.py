@@ -69,15 +69,16 @@ def _ffn(L, fn, K=4096, N=4096, T=8, E=16, k=2, bm=16, split=-1, ws=FAKE, ws_byt
     return getattr(L, fn)(P(x), s, P(FAKE), s, P(FAKE), s, *tail)
 
 
-@pytest.mark.parametrize("fn", ["fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8"])
+@pytest.mark.parametrize("fn", ["fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8",
+                                "fused_moe_mxfp4"])
 def test_ffn_errors_before_launch(fn):
     L = moe.lib()
     assert _ffn(L, fn, K=4000) == -3                    # K % 128
     assert _ffn(L, fn, N=4095) == -2                    # odd N
     assert _ffn(L, fn, N=4096 + 128) == -3              # I % 128
     assert _ffn(L, fn, bm=24) == -3                     # block_m
-    if fn == "fused_moe_bf16":
-        assert _ffn(L, fn, bm=256) == -3                # 256 is e4m3-only
+    if fn in ("fused_moe_bf16", "fused_moe_mxfp4"):
+        assert _ffn(L, fn, bm=256) == -3                # 256 needs e4m3 weights
     else:
         assert _ffn(L, fn, bm=256, K=384 * 2 + 128) == -3   # 256 needs K % 256 == 0
         assert _ffn(L, fn, bm=256, split=0) == -3       # 256 runs the split mode only

@@ -32,7 +32,8 @@ def weights(name):
 
 
 CASES = [(name, T) for name in ("fp8-k4096-i2048-e256-top6", "fp8-k4096-i2048-e288-top8",
-                                "fp8-k7168-i3072-e384-top6", "mx-k4096-i256-e32-top8")
+                                "fp8-k7168-i3072-e384-top6", "mx-k4096-i256-e32-top8",
+                                "mxfp4-k4096-i2048-e256-top6")
          for T in datagen.WORKLOADS[name]["tokens"]]
 
 
@@ -67,7 +68,8 @@ def test_full_size_sampled(name, T):
 
 
 @pytest.mark.parametrize("name,T", [("fp8-k4096-i2048-e256-top6", 256),
-                                    ("mx-k4096-i256-e32-top8", 512)])
+                                    ("mx-k4096-i256-e32-top8", 512),
+                                    ("mxfp4-k4096-i2048-e256-top6", 64)])
 def test_full_size_modes_agree(name, T):
     """Both modes at full size on the same inputs agree on sampled tokens
     within the oracle gate."""

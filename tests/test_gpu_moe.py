@@ -20,6 +20,7 @@ SHAPES = {
     "bf16": dict(K=512, I=256),
     "fp8_blockwise": dict(K=512, I=384),
     "mxfp8": dict(K=384, I=256),
+    "mxfp4": dict(K=384, I=256),
 }
 
 
@@ -40,7 +41,7 @@ def to_gpu(c):
 
 @pytest.mark.parametrize("split", [1, 0])
 @pytest.mark.parametrize("bm", [16, 32, 64, 128])
-@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
 def test_small_parity(kind, bm, split):
     c = small_case(kind)
     check(c, bm, split, label="small")
@@ -52,7 +53,7 @@ def test_bf16_tiny_workload():
         check(c, 16, split, label="bf16 workload")
 
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
 def test_split_mode_deterministic(kind):
     c = small_case(kind, T=200, E=16, k=4)
     a, _ = moe.run_case(c, block_m=32, split=1)
@@ -61,7 +62,7 @@ def test_split_mode_deterministic(kind):
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
 def test_fused_matches_split(kind):
     c = small_case(kind, T=100, E=8, k=2)
     a, _ = moe.run_case(c, block_m=16, split=1)
@@ -82,7 +83,7 @@ def _adjacent(a, b, sign):
     return (a == b) | (same_sign & (step == 1)) | ((a & (sign - 1)) + (b & (sign - 1)) <= 1)
 
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
 def test_split_intermediate_matches_oracle(kind):
     """The requantized intermediate the split mode writes (values and scales)
     against the oracle's: scales equal up to fp32 summation noise, every code
@@ -117,7 +118,7 @@ def test_split_intermediate_matches_oracle(kind):
         if kind == "fp8_blockwise":
             srow = wsn[hs_off + pos * (I // 128) * 4: hs_off + (pos + 1) * (I // 128) * 4]
             np.testing.assert_allclose(srow.view(np.float32), s_ref, rtol=1e-4)
-        if kind == "mxfp8":
+        if kind in ("mxfp8", "mxfp4"):
             srow = wsn[hs_off + pos * (I // 32): hs_off + (pos + 1) * (I // 32)]
             moved = srow != s_ref          # power-of-two scale decided the other way
             assert np.all(np.abs(srow.astype(int) - s_ref.astype(int)) <= 1)
@@ -131,7 +132,7 @@ def test_split_intermediate_matches_oracle(kind):
     assert scale_flips <= max(1, n * (I // 32) // 100)
 
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
 def test_empty_experts_never_read(kind):
     c = small_case(kind, T=6, E=32, k=2)
     base, _ = moe.run_case(c, block_m=16, split=1)
@@ -139,16 +140,24 @@ def test_empty_experts_never_read(kind):
     empty = [e for e in range(c.E) if e not in used]
     assert empty
     idx = torch.tensor(empty, device="cuda")
-    w1 = c.w1.view(torch.uint8).clone()
-    w2 = c.w2.view(torch.uint8).clone()
-    if kind == "bf16":
-        w1.view(torch.int16)[idx] = 0x7FC0
-        w2.view(torch.int16)[idx] = 0x7FC0
+    if kind == "mxfp4":
+        # every e2m1 code is finite: poison the e8m0 scales (0xFF is NaN)
+        s1 = c.w1_scale.clone()
+        s2 = c.w2_scale.clone()
+        s1[idx] = 0xFF
+        s2[idx] = 0xFF
+        c.w1_scale, c.w2_scale = s1, s2
     else:
-        w1[idx] = 0x7F
-        w2[idx] = 0x7F
-    c.w1 = w1.view(c.w1.dtype)
-    c.w2 = w2.view(c.w2.dtype)
+        w1 = c.w1.view(torch.uint8).clone()
+        w2 = c.w2.view(torch.uint8).clone()
+        if kind == "bf16":
+            w1.view(torch.int16)[idx] = 0x7FC0
+            w2.view(torch.int16)[idx] = 0x7FC0
+        else:
+            w1[idx] = 0x7F
+            w2[idx] = 0x7F
+        c.w1 = w1.view(c.w1.dtype)
+        c.w2 = w2.view(c.w2.dtype)
     for split in (1, 0):
         got, _ = moe.run_case(c, block_m=16, split=split)
         torch.cuda.synchronize()
@@ -169,7 +178,7 @@ def test_routes_outside_local_experts(split):
     assert torch.all(out[5].float() == 0)
 
 
-@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
 def test_single_token(kind):
     c = small_case(kind, T=1, E=8, k=2)
     for split in (1, 0):
@@ -184,7 +193,7 @@ def test_many_routes_fused_atomics():
 
 @pytest.mark.parametrize("split", [1, 0])
 @pytest.mark.parametrize("bm", [16, 32])
-@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
 def test_ksplit_parity(kind, bm, split):
     """Few (block, slice) tiles and at least 8 K steps: the up GEMM runs with
     two K groups per workgroup; 9 K steps give the groups an uneven share."""
