@@ -52,21 +52,100 @@ struct Operand {
   uint32_t as[MI][4];
   const float* bsrow[2];
   int bsel[NI];
-  // MX: e8m0 rows of the lane's A row and B row (+ lane group), 4 bytes per step
+  // MX: e8m0 rows of the lane's A row and B row, 4 bytes (one per 32-wide
+  // block) per step; the same buffers as descriptors for direct-to-LDS loads
   __amdgpu_buffer_rsrc_t rxa, rxb;
   uint32_t ax[MI], bx[NI];
+  desc_t dxa, dxb;
 };
+
+// MX scales staged in LDS.  Each wave copies, before its K walk, the e8m0
+// bytes of its K range for every row it multiplies (NI*16 weight rows, then
+// MI*16 activation rows) into a private LDS region, with direct-to-LDS loads
+// that move whole 128-byte lines; a scale run (4 steps, 16 bytes of a row) is
+// then one LDS read.  Fetched from memory instead, every run is a load that
+// touches 16 rows' lines for 16 bytes each, which measured at 14% of the
+// MXFP4 up GEMM.  Rows are `4 * ksteps` bytes, in 16-byte chunks; chunk q of
+// row i sits in slot (q + (i % 16)) mod (chunks per row), so a run's 16 rows
+// fall on different banks.
+constexpr int kStageMax = 65536;  // dynamic LDS per workgroup for the regions
+
+// Bytes of one wave's region for a K walk of `ksteps` steps (0: not staged,
+// the runs come from memory).  Staging needs whole runs (ksteps % 4 == 0).
+__host__ __device__ constexpr int stage_bytes(int ksteps, int mi, int waves) {
+  const int cpr = ksteps / 4;
+  const int bytes = 4 * 16 * cpr * 16 + (mi * 16 * cpr + 63) / 64 * 1024;
+  return (ksteps % 4 == 0 && ksteps > 0 && bytes * waves <= kStageMax) ? bytes : 0;
+}
+
+struct Stage {
+  const uint8_t* lds;  // the wave's region
+  int rbs;             // bytes per row (4 per step)
+  int cpr;             // 16-byte chunks per row
+  int rm;              // this lane's slot rotation, (l % 16) % cpr
+  int a_off;           // offset of the activation rows in the region
+  uint32_t lane_row;   // (l % 16) * rbs
+};
+
+// MX scales travel in runs: one Q-dword load brings Q consecutive K steps of a
+// row's e8m0 bytes, where Q (4, 2 or 1) divides the ring depth.  One byte per
+// lane per step would cost a load instruction per operand row and step, each
+// touching 16 rows' cache lines, and those requests (not bytes) measured as
+// the streaming kernels' limit.
+template <int D>
+constexpr int scale_run() { return D % 4 == 0 ? 4 : D % 2 == 0 ? 2 : 1; }
 
 template <int KIND, int MI, int NI, int D>
 struct Ring {
+  static constexpr int Q = scale_run<D>();
   Frag<KIND> fa[D][MI];
   FragB<KIND> fb[D][NI];
   float sa[D][MI][4];
-  int xa[D][MI];
-  int xb[D][NI];
+  // MX: the rows' scale runs in flight, and the lane's byte of each step of
+  // the run being computed (copied out when the run starts, so that its slot
+  // can be refilled at once)
+  uint32_t qa[D / Q][MI][Q];
+  uint32_t qb[D / Q][NI][Q];
+  int xa[MI][Q];
+  int xb[NI][Q];
 };
 
+template <int Q>
+__device__ __forceinline__ void load_run(uint32_t (&q)[Q], __amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                         uint32_t soff) {
+  if constexpr (Q == 4) {
+    const uint4 v = buf_load16(r, voff, soff);
+    q[0] = v.x, q[1] = v.y, q[2] = v.z, q[3] = v.w;
+  } else if constexpr (Q == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    q[0] = v[0], q[1] = v[1];
+  } else {
+    q[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+  }
+}
+
+// MX scale run of the walk's steps [4q, 4q + 4) from the staged rows
 template <int KIND, int MI, int NI, int D>
+__device__ __forceinline__ void stage_read(Ring<KIND, MI, NI, D>& r, int slot, int q,
+                                           const Stage& st) {
+  int sl = q + st.rm;
+  sl = sl >= st.cpr ? sl - st.cpr : sl;
+  const uint8_t* base = st.lds + st.lane_row + 16 * sl;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni) {
+    const uint4 v = *reinterpret_cast<const uint4*>(base + ni * 16 * st.rbs);
+    r.qb[slot / 4][ni][0] = v.x, r.qb[slot / 4][ni][1] = v.y;
+    r.qb[slot / 4][ni][2] = v.z, r.qb[slot / 4][ni][3] = v.w;
+  }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const uint4 v = *reinterpret_cast<const uint4*>(base + st.a_off + mi * 16 * st.rbs);
+    r.qa[slot / 4][mi][0] = v.x, r.qa[slot / 4][mi][1] = v.y;
+    r.qa[slot / 4][mi][2] = v.z, r.qa[slot / 4][mi][3] = v.w;
+  }
+}
+
+template <int KIND, int MI, int NI, int D, bool STAGED = false>
 __device__ __forceinline__ void ring_load(Ring<KIND, MI, NI, D>& r, int slot, int ks,
                                           const Operand<MI, NI>& op) {
   const uint32_t soff = (uint32_t)ks * KindTraits<KIND>::STEP_BYTES;
@@ -81,16 +160,21 @@ __device__ __forceinline__ void ring_load(Ring<KIND, MI, NI, D>& r, int slot, in
 #pragma unroll
       for (int i = 0; i < 4; ++i) r.sa[slot][mi][i] = buf_loadf(op.rsa, op.as[mi][i], ks * 4);
   }
-  if constexpr (is_mx(KIND)) {
+  // a run starts at every Q-th slot (slot is a constant once the ring loop is
+  // unrolled, so this is no branch)
+  constexpr int Q = Ring<KIND, MI, NI, D>::Q;
+  if constexpr (is_mx(KIND) && !STAGED) {
+    if (slot % Q == 0) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) r.xa[slot][mi] = buf_loadu8(op.rxa, op.ax[mi], ks * 4);
+      for (int mi = 0; mi < MI; ++mi) load_run<Q>(r.qa[slot / Q][mi], op.rxa, op.ax[mi], ks * 4);
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) r.xb[slot][ni] = buf_loadu8(op.rxb, op.bx[ni], ks * 4);
+      for (int ni = 0; ni < NI; ++ni) load_run<Q>(r.qb[slot / Q][ni], op.rxb, op.bx[ni], ks * 4);
+    }
   }
 }
 
 template <int KIND, int MI, int NI, int D>
-__device__ __forceinline__ void ring_compute(const Ring<KIND, MI, NI, D>& r, int slot, int ks,
+__device__ __forceinline__ void ring_compute(Ring<KIND, MI, NI, D>& r, int slot, int ks,
                                              const Operand<MI, NI>& op,
                                              const StepScales (&sc)[2], f32x4 (&acc)[MI][NI]) {
   if constexpr (KIND == KIND_FP8B) {
@@ -108,12 +192,26 @@ __device__ __forceinline__ void ring_compute(const Ring<KIND, MI, NI, D>& r, int
         for (int i = 0; i < 4; ++i) acc[mi][ni][i] += t[i] * (r.sa[slot][mi][i] * w);
       }
   } else if constexpr (is_mx(KIND)) {
+    constexpr int Q = Ring<KIND, MI, NI, D>::Q;
+    if (slot % Q == 0) {
+      // lane group g's byte of each step: K block g of the step
+      const uint32_t sh = (threadIdx.x >> 1) & 0x18u;  // 8 * (lane / 16)
+#pragma unroll
+      for (int j = 0; j < Q; ++j) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+          r.xa[mi][j] = (int)__builtin_amdgcn_ubfe(r.qa[slot / Q][mi][j], sh, 8);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          r.xb[ni][j] = (int)__builtin_amdgcn_ubfe(r.qb[slot / Q][ni][j], sh, 8);
+      }
+    }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni)
         acc[mi][ni] = mfma_step_scaled<KIND>(r.fa[slot][mi], r.fb[slot][ni], acc[mi][ni],
-                                             r.xa[slot][mi], r.xb[slot][ni]);
+                                             r.xa[mi][slot % Q], r.xb[ni][slot % Q]);
   } else {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -142,9 +240,13 @@ __device__ __forceinline__ int stagger_wg(int nsteps) {
 // acc[mi][ni] = sum over the 128-wide K steps [k_first, k_first + ksteps) of
 // A rows . B rows (with the dtype's scales), D steps of operands prefetched
 // into registers, visiting the steps from a staggered start.
-template <int KIND, int MI, int NI, int D>
+// STAGED (MX, runs of 4): the scale runs come from the wave's LDS region,
+// filled here with the rows of a_row(i) / b_row(i) (byte offsets of the
+// i-th activation / weight row's scales in their buffers).
+template <int KIND, int MI, int NI, int D, bool STAGED = false, class AR = int, class BR = int>
 __device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_first, int ksteps,
-                                           f32x4 (&acc)[MI][NI]) {
+                                           f32x4 (&acc)[MI][NI], const Stage* st = nullptr,
+                                           AR a_row = 0, BR b_row = 0) {
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -157,7 +259,10 @@ __device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_firs
     // drain the operand ring every pass
     wait_vmcnt<0>();
   }
-  const int rot = stagger_wg(ksteps);
+  // MX scale runs are contiguous in K only if no run straddles the wrap, so
+  // the rotation moves in whole runs (and stays 0 if runs do not tile the walk)
+  constexpr int Q = is_mx(KIND) ? Ring<KIND, MI, NI, D>::Q : 1;
+  const int rot = ksteps % Q == 0 ? Q * stagger_wg(ksteps / Q) : 0;
   auto rel = [&](int i) { const int k = i + rot; return k >= ksteps ? k - ksteps : k; };
   Ring<KIND, MI, NI, D> r;
   // The steady-state loop loads unconditionally, so the count of loads in
@@ -167,14 +272,50 @@ __device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_firs
   // the prologue fills every slot unconditionally too (with fewer steps than
   // slots the spare slots re-load a wrapped, in-bounds step nobody uses):
   // a skipped load here would leave the loop's first waits conservative
+  if constexpr (STAGED) {
+    static_assert(is_mx(KIND) && Ring<KIND, MI, NI, D>::Q == 4 && NI == 4, "staged MX runs");
+    // copy the scale rows: chunk c = 64 t + lane of a section is row c / cpr,
+    // slot c % cpr, which holds the row's chunk (slot - rotation) mod cpr
+    const int lane = threadIdx.x & 63, cpr = st->cpr;
+    const uint32_t m0 = lds_addr(st->lds);
+    const uint32_t koff = 4u * (uint32_t)k_first;
+    for (int t = 0; t < cpr; ++t) {  // NI * 16 * cpr / 64 instructions
+      const int c = t * 64 + lane, ri = c / cpr, ch = c - ri * cpr, rot_i = (ri & 15) % cpr;
+      const int gq = ch >= rot_i ? ch - rot_i : ch + cpr - rot_i;
+      dma16(op.dxb, m0 + t * 1024, b_row(ri) + 16 * gq, koff);
+    }
+    const int na = (MI * 16 * cpr + 63) / 64;
+    for (int t = 0; t < na; ++t) {
+      const int c = t * 64 + lane, ri = c / cpr, ch = c - ri * cpr, rot_i = (ri & 15) % cpr;
+      const int gq = ch >= rot_i ? ch - rot_i : ch + cpr - rot_i;
+      // lanes past the last row fill padding with a valid row's bytes
+      dma16(op.dxa, m0 + st->a_off + t * 1024, a_row(ri < MI * 16 ? ri : MI * 16 - 1) + 16 * gq,
+            koff);
+    }
+  }
 #pragma unroll
-  for (int d = 0; d < D; ++d) ring_load<KIND>(r, d, k_first + rel(d < ksteps ? d : d % ksteps), op);
+  for (int d = 0; d < D; ++d)
+    ring_load<KIND, MI, NI, D, STAGED>(r, d, k_first + rel(d < ksteps ? d : d % ksteps), op);
+  if constexpr (STAGED) {
+    // Direct-to-LDS loads need not complete in order with the register loads
+    // issued after them, so the region is complete only at vmcnt(0): waited
+    // once, after the first D steps of operand loads are in flight (the empty
+    // asm keeps them above the wait).
+    asm volatile("" ::: "memory");
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int d = 0; d < D; d += 4) stage_read(r, d, rel(d < ksteps ? d : d % ksteps) / 4, *st);
+  }
   int ks = 0;
   for (; ks + 2 * D <= ksteps; ks += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       ring_compute<KIND>(r, d, rel(ks + d), op, sc, acc);
-      ring_load<KIND>(r, d, k_first + rel(ks + d + D), op);
+      ring_load<KIND, MI, NI, D, STAGED>(r, d, k_first + rel(ks + d + D), op);
+      if constexpr (STAGED) {
+        if (d % 4 == 0) stage_read(r, d, rel(ks + d + D) / 4, *st);
+      }
     }
   }
 #pragma unroll
@@ -182,9 +323,35 @@ __device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_firs
     const int k = ks + d;
     if (k < ksteps) {
       ring_compute<KIND>(r, d % D, rel(k), op, sc, acc);
-      if (k + D < ksteps) ring_load<KIND>(r, d % D, k_first + rel(k + D), op);
+      if (k + D < ksteps) {
+        ring_load<KIND, MI, NI, D, STAGED>(r, d % D, k_first + rel(k + D), op);
+        if constexpr (STAGED) {
+          if (d % 4 == 0) stage_read(r, d % D, rel(k + D) / 4, *st);
+        }
+      }
     }
   }
+}
+
+// The region of the wave `w` of a workgroup of `waves` waves (dynamic LDS)
+extern __shared__ __attribute__((aligned(16))) uint8_t mx_stage[];
+
+__device__ __forceinline__ Stage make_stage(int ksteps, int mi, int waves, int w) {
+  Stage st;
+  const int bytes = stage_bytes(ksteps, mi, waves);
+  st.lds = mx_stage + w * bytes;
+  st.cpr = ksteps / 4;
+  st.rbs = 4 * ksteps;
+  const int r16 = threadIdx.x & 15;
+  st.rm = r16 % st.cpr;
+  st.a_off = 4 * 16 * st.cpr * 16;
+  st.lane_row = (uint32_t)(r16 * st.rbs);
+  return st;
+}
+
+// Region bytes per wave of the up GEMM (K groups of K / 128 / ksplit steps)
+__host__ __device__ constexpr int up_stage_bytes(int K, int mi, int ksplit, int waves) {
+  return (K / 128) % ksplit == 0 ? stage_bytes(K / 128 / ksplit, mi, waves) : 0;
 }
 
 template <int BM, int KSPLIT = 1>
@@ -227,6 +394,9 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const in
     op.rxa = make_rsrc(p.xs, (uint32_t)((size_t)p.T * (K / 32)));
     op.rxb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w1s) + (size_t)e * N * (K / 32),
                        (uint32_t)((size_t)N * (K / 32)));
+    op.dxa = make_desc(p.xs, (uint32_t)((size_t)p.T * (K / 32)));
+    op.dxb = make_desc(reinterpret_cast<const uint8_t*>(p.w1s) + (size_t)e * N * (K / 32),
+                       (uint32_t)((size_t)N * (K / 32)));
   }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
@@ -240,14 +410,14 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const in
         op.as[mi][i] = (uint32_t)token_of(ids[crow], p.top_k) * KS * 4;
       }
     }
-    if constexpr (is_mx(KIND)) op.ax[mi] = (uint32_t)tok * (K / 32) + g;
+    if constexpr (is_mx(KIND)) op.ax[mi] = (uint32_t)tok * (K / 32);
   }
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int n = (ni < 2 ? 0 : I) + s * kSlice + 32 * wn + 16 * (ni & 1) + r16;
     op.b[ni] = (uint32_t)(n * BTraits<KIND>::row_bytes(K)) + 16 * g;
     if constexpr (KIND == KIND_FP8B) op.bsel[ni] = ni < 2 ? 0 : 1;  // gate block, up block
-    if constexpr (is_mx(KIND)) op.bx[ni] = (uint32_t)n * (K / 32) + g;
+    if constexpr (is_mx(KIND)) op.bx[ni] = (uint32_t)n * (K / 32);
   }
   if constexpr (KIND == KIND_FP8B) {
     op.bsrow[0] = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + s) * KS;
@@ -255,7 +425,22 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const in
   }
   f32x4 acc[MI][4];
   const int k_lo = kg * KS / KSPLIT, k_hi = (kg + 1) * KS / KSPLIT;
-  gemm_steps<KIND, MI, 4, D>(op, k_lo, k_hi - k_lo, acc);
+  bool done = false;
+  if constexpr (is_mx(KIND) && scale_run<D>() == 4) {
+    constexpr int W = B::THREADS / 64;
+    if (up_stage_bytes(K, MI, KSPLIT, W) > 0) {
+      const Stage st = make_stage(k_hi - k_lo, MI, W, wid);
+      const uint32_t rs = (uint32_t)(K / 32);
+      auto a_row = [&](int ri) { return (uint32_t)token_of(ids[wm * 64 + ri], p.top_k) * rs; };
+      auto b_row = [&](int ri) {
+        const int ni = ri >> 4;
+        return (uint32_t)((ni < 2 ? 0 : I) + s * kSlice + 32 * wn + 16 * (ni & 1) + (ri & 15)) * rs;
+      };
+      gemm_steps<KIND, MI, 4, D, true>(op, k_lo, k_hi - k_lo, acc, &st, a_row, b_row);
+      done = true;
+    }
+  }
+  if (!done) gemm_steps<KIND, MI, 4, D>(op, k_lo, k_hi - k_lo, acc);
   if constexpr (KSPLIT > 1) {
     // partial sums of groups 1.. go through LDS (lane-contiguous floats);
     // group 0 adds them in group order
@@ -449,6 +634,9 @@ k_down(MoeArgs p) {
     op.rxa = make_rsrc(p.hs, (uint32_t)((size_t)p.blocks_cap * BM * (I / 32)));
     op.rxb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w2s) + (size_t)e * K * (I / 32),
                        (uint32_t)((size_t)K * (I / 32)));
+    op.dxa = make_desc(p.hs, (uint32_t)((size_t)p.blocks_cap * BM * (I / 32)));
+    op.dxb = make_desc(reinterpret_cast<const uint8_t*>(p.w2s) + (size_t)e * K * (I / 32),
+                       (uint32_t)((size_t)K * (I / 32)));
   }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
@@ -461,21 +649,33 @@ k_down(MoeArgs p) {
         op.as[mi][i] = cpos * IS * 4;
       }
     }
-    if constexpr (is_mx(KIND)) op.ax[mi] = pos * (I / 32) + g;
+    if constexpr (is_mx(KIND)) op.ax[mi] = pos * (I / 32);
   }
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const int c = c0 + 16 * ni + r16;
     op.b[ni] = (uint32_t)(c * BTraits<KIND>::row_bytes(I)) + 16 * g;
     if constexpr (KIND == KIND_FP8B) op.bsel[ni] = 0;
-    if constexpr (is_mx(KIND)) op.bx[ni] = (uint32_t)c * (I / 32) + g;
+    if constexpr (is_mx(KIND)) op.bx[ni] = (uint32_t)c * (I / 32);
   }
   if constexpr (KIND == KIND_FP8B) {
     op.bsrow[0] = reinterpret_cast<const float*>(p.w2s) + ((size_t)e * (K / 128) + c0 / 128) * IS;
     op.bsrow[1] = op.bsrow[0];
   }
   f32x4 acc[MI][4];
-  gemm_steps<KIND, MI, 4, D>(op, 0, IS, acc);
+  bool done = false;
+  if constexpr (is_mx(KIND) && scale_run<D>() == 4) {
+    constexpr int W = BlockShape<BM>::THREADS / 64;
+    if (stage_bytes(IS, MI, W) > 0) {
+      const Stage st = make_stage(IS, MI, W, wave_id());
+      const uint32_t rs = (uint32_t)(I / 32), b0 = (uint32_t)b * BM + wm * 64;
+      auto a_row = [&](int ri) { return (b0 + ri) * rs; };
+      auto b_row = [&](int ri) { return (uint32_t)(c0 + ri) * rs; };
+      gemm_steps<KIND, MI, 4, D, true>(op, 0, IS, acc, &st, a_row, b_row);
+      done = true;
+    }
+  }
+  if (!done) gemm_steps<KIND, MI, 4, D>(op, 0, IS, acc);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -666,11 +866,13 @@ template <int KIND, int BM, int KSPLIT = 1>
 constexpr int prefetch_depth() {
   // two K groups put two waves on each SIMD, which halves each wave's
   // registers (four groups would leave too few for any prefetch)
-  // An MXFP4 step moves half the weight bytes in half the registers, so its
-  // ring holds more steps to keep the same bytes in flight.
+  // MX depths are even (4 where registers allow) so that the scale runs are
+  // 4 (or 2) steps long; measured at 16 rows: MXFP4 depth 4 beat 6 and 8.
   if constexpr (KIND == KIND_BF16) return BM <= 32 && KSPLIT == 1 ? 2 : 1;
-  else if constexpr (KIND == KIND_MX4 && KSPLIT == 2) return BM == 16 ? 4 : 3;
-  else if constexpr (KIND == KIND_MX4) return BM == 16 ? 6 : BM == 32 ? 4 : BM == 64 ? 3 : 2;
+  else if constexpr (KIND == KIND_MX4 && KSPLIT == 2) return BM == 16 ? 4 : 2;
+  else if constexpr (KIND == KIND_MX4) return BM <= 32 ? 4 : BM == 64 ? 2 : 1;
+  else if constexpr (KIND == KIND_MX && KSPLIT == 2) return BM == 16 ? 4 : 2;
+  else if constexpr (KIND == KIND_MX) return BM == 16 ? 4 : BM <= 64 ? 2 : 1;
   else if constexpr (KSPLIT == 2) return BM == 16 ? 3 : 2;
   else return BM == 16 ? 4 : BM == 32 ? 3 : BM == 64 ? 2 : 1;
 }
@@ -684,8 +886,11 @@ template <int KIND, int BM, int KSPLIT>
 void launch_up(int split, const MoeArgs& a, unsigned grid, hipStream_t st) {
   constexpr int TH = BlockShape<BM, KSPLIT>::THREADS;
   constexpr int D = prefetch_depth<KIND, BM, KSPLIT>();
-  if (split) hipLaunchKernelGGL((k_up<KIND, BM, D, KSPLIT>), dim3(grid), dim3(TH), 0, st, a);
-  else hipLaunchKernelGGL((k_fused<KIND, BM, D, KSPLIT>), dim3(grid), dim3(TH), 0, st, a);
+  constexpr int MI = BlockShape<BM, KSPLIT>::MI, W = TH / 64;
+  const size_t lds = is_mx(KIND) && scale_run<D>() == 4
+                         ? (size_t)W * up_stage_bytes(a.K, MI, KSPLIT, W) : 0;
+  if (split) hipLaunchKernelGGL((k_up<KIND, BM, D, KSPLIT>), dim3(grid), dim3(TH), lds, st, a);
+  else hipLaunchKernelGGL((k_fused<KIND, BM, D, KSPLIT>), dim3(grid), dim3(TH), lds, st, a);
 }
 
 // K groups for the up GEMM: with few (block, slice) tiles (a narrow
@@ -734,7 +939,10 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
     mark(hk, 1, true, st);
     const int NT = (a.K + 255) / 256;
     mark(hk, 2, false, st);
-    hipLaunchKernelGGL((k_down<KIND, BM, D>), dim3((unsigned)a.blocks_cap * NT), dim3(THREADS), 0,
+    constexpr int W = THREADS / 64;
+    const size_t lds = is_mx(KIND) && scale_run<D>() == 4
+                           ? (size_t)W * stage_bytes(a.I / 128, BlockShape<BM>::MI, W) : 0;
+    hipLaunchKernelGGL((k_down<KIND, BM, D>), dim3((unsigned)a.blocks_cap * NT), dim3(THREADS), lds,
                        st, a);
     mark(hk, 2, true, st);
     const int CT = (a.K + 1023) / 1024;

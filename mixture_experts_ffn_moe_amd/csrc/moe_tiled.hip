@@ -35,51 +35,6 @@ constexpr int kChunks = 8;      // 16-byte chunks per row
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-typedef int desc_t __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor: base address, no stride, `bytes` records (loads past
-// them return zeros), 32-bit data format.
-__device__ __forceinline__ desc_t make_desc(const void* p, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  return desc_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
-                __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffff)),
-                __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const uint8_t*)p);
-}
-
-// Direct-to-LDS buffer loads: lane L's bytes land at M0 + L * size.  They are
-// issued from asm so that the only waits on them are the explicit vmcnt waits
-// of the pipeline: the compiler cannot always tell which LDS stage such a
-// load writes and would otherwise wait for every load in flight before an LDS
-// read.  They have no destination register; VMEM loads complete in order, so
-// the compiler's own vmcnt waits stay correct (at worst stricter).  M0 is set
-// in the same statement; the compiler sets it right before each of its own
-// uses.
-// The scalar operands pass through readfirstlane: the compiler may hold a
-// wave-uniform value in a vector register, which an "s" operand cannot take
-// (the read folds away for values already in scalar registers).
-__device__ __forceinline__ void dma16(desc_t r, uint32_t m0, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r),
-                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
-}
-
-__device__ __forceinline__ void dma4(desc_t r, uint32_t m0, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r),
-                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
-}
-
-// Wave index as a wave-uniform (scalar) value, so that addresses derived from
-// it (LDS stage offsets for M0, row bases) stay in scalar registers.
-__device__ __forceinline__ int wave_id() {
-  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-}
-
 // Workgroup barrier without the release fence __syncthreads() carries: that
 // fence waits for every outstanding vector load, including the direct-to-LDS
 // loads of later pipeline stages.  Stage completion is tracked with explicit

@@ -201,6 +201,20 @@ def test_ksplit_parity(kind, bm, split):
     check(c, bm, split, label="ksplit")
 
 
+@pytest.mark.parametrize("split", [1, 0])
+@pytest.mark.parametrize("kind,K,I,T,E", [
+    ("mxfp8", 1024, 512, 20, 8),     # two K groups of 4 steps: one chunk per row; down 4 steps
+    ("mxfp4", 2048, 512, 60, 8),     # two K groups of 8 steps: two chunks per row
+    ("mxfp4", 1536, 1536, 40, 32),   # one K group of 12 steps (3 chunks); down 12 steps
+    ("mxfp8", 1536, 1536, 40, 32)])
+def test_staged_scale_parity(kind, K, I, T, E, split):
+    """MX walks whose step count is a multiple of 4 read their e8m0 scale
+    runs from rows copied into LDS before the walk (block_m 16, ring depth 4),
+    with the chunk rotation taken modulo the row's chunk count."""
+    c = small_case(kind, T=T, E=E, k=2, K=K, I=I)
+    check(c, 16, split, label="staged")
+
+
 def test_ksplit_deterministic():
     c = small_case("mxfp8", T=20, E=8, k=2, K=1152, I=256)
     a, _ = moe.run_case(c, block_m=16, split=1)
