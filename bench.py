@@ -17,6 +17,14 @@ mode) is timed with HIP events recorded around it on its own stream, and its
 algorithmic HBM bytes (weights and scales of the experts it reads once, the
 token rows, its outputs) are divided by that time.
 
+Per token count the sweep also holds per-call distributions (median, p10,
+p90 of event pairs around each call): the whole call and the forward alone
+(planner outputs reused), back to back ("warm"), and the whole call with a
+1 GiB read before each call outside its events ("cold": L2 and the 256 MB
+MALL hold other, clean lines).  The line records the GPU clocks rocm-smi reports and two
+measured reference ceilings beside the spec peaks: a plain device copy, a
+read-only sum, and a large e4m3 GEMM through the vendor BLAS.
+
 The CPU baseline runs the fp64 oracle on a bounded sample of the same
 workload (a few tokens of the largest token count) on the host cores.
 """
@@ -200,6 +208,99 @@ def cpu_baseline(case, n_tokens, K, I):
             "seconds": dt}
 
 
+def percentiles(v):
+    v = sorted(v)
+    def at(q):
+        x = q / 100.0 * (len(v) - 1)
+        i = int(x)
+        return v[i] if i + 1 >= len(v) else v[i] + (x - i) * (v[i + 1] - v[i])
+    return {"n": len(v), "median_us": at(50), "p10_us": at(10), "p90_us": at(90),
+            "mean_us": sum(v) / len(v)}
+
+
+def per_call(torch, fn, n, stream, flush=None):
+    """Event pair around each of n calls on ``stream`` (the flush, when given,
+    runs before each call, outside its pair)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return percentiles([a.elapsed_time(b) * 1e3 for a, b in evs])
+
+
+def gpu_clocks():
+    """Current GPU clocks as rocm-smi reports them (None where it is absent)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    card = next(iter(d.values()), {}) if isinstance(d, dict) else {}
+    return {k.strip(" :"): v for k, v in card.items() if "clock" in k.lower()}
+
+
+def measured_ceilings(torch):
+    """Reference ceilings measured on this GPU beside the spec peaks: a plain
+    device copy (bytes read + written per second), a read-only sum, and a
+    large e4m3 GEMM through torch._scaled_mm (the vendor BLAS), each the best
+    of 6."""
+    res = {}
+    n = 2 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b)
+        best = t if best is None else min(best, t)
+    res["copy_gbs"] = 2 * n / (best * 1e-3) / 1e9
+    del dst
+    f = src.view(torch.float32)
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    best = None
+    for _ in range(6):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.sum(f, dim=0, out=sink)
+        b.record()
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b)
+        best = t if best is None else min(best, t)
+    res["read_gbs"] = n / (best * 1e-3) / 1e9
+    del src, f, sink
+    try:
+        m = 8192
+        x = torch.randn(m, m, device="cuda").to(torch.float8_e4m3fn)
+        w = torch.randn(m, m, device="cuda").to(torch.float8_e4m3fn).t()
+        one = torch.ones((), device="cuda")
+        best = None
+        for _ in range(6):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            torch._scaled_mm(x, w, scale_a=one, scale_b=one, out_dtype=torch.bfloat16)
+            b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b)
+            best = t if best is None else min(best, t)
+        res["fp8_gemm_tflops"] = 2.0 * m ** 3 / (best * 1e-3) / 1e12
+        res["fp8_gemm_shape"] = [m, m, m]
+    except Exception as exc:  # the vendor GEMM is a reference only
+        res["fp8_gemm_tflops"] = None
+        res["fp8_gemm_error"] = str(exc)[:200]
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +312,10 @@ def main():
     ap.add_argument("--split", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=20)
+    ap.add_argument("--calls", type=int, default=200,
+                    help="per-call timed calls (warm) for the median / p10 / p90")
+    ap.add_argument("--cold-calls", type=int, default=50,
+                    help="per-call timed calls with a 1 GiB write before each (cold caches)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-counters", default=None, metavar="DIR",
@@ -310,6 +415,25 @@ def main():
         print(f"[bench] T={T} bm={bm} {'split' if split else 'fused'}: {ms*1e3:.1f} us/step, "
               f"{kname} {kms*1e3:.1f} us = {dom_bytes/(kms*1e-3)/1e9:.0f} GB/s",
               file=sys.stderr, flush=True)
+        # per-call distributions: the whole call (planner + forward) and the
+        # forward alone, warm (back to back), then cold (1 GiB written before
+        # each call, outside its event pair: evicts L2 and the 256 MB MALL)
+        prot = {"full_warm": per_call(torch, step, args.calls, stream)}
+
+        def op_only():
+            moe.run_case(case, block_m=bm, split=split, workspace=ws, out=out,
+                         align_out=align_out, skip_align=True)
+
+        prot["op_warm"] = per_call(torch, op_only, args.calls, stream)
+        if args.cold_calls:
+            # a read, not a write: written scratch would leave the caches
+            # dirty, and the call would pay for writing it back
+            scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+            sink = torch.empty((), dtype=torch.float32, device=dev)
+            prot["full_cold"] = per_call(torch, step, args.cold_calls, stream,
+                                         flush=lambda: torch.sum(scratch, dim=0, out=sink))
+            del scratch, sink
+        sweep[-1]["per_call"] = prot
         last_case = case
         del ws
 
@@ -331,6 +455,9 @@ def main():
         "sweep": sweep,
         "kernel_source_hash": kernel_source_hash(),
     }
+    result["clocks"] = gpu_clocks()
+    result["measured_ceilings"] = measured_ceilings(torch)
+    result["spec_peaks"] = {"hbm_gbs": HBM_PEAK_GBS, "mfma_tflops": MFMA_PEAK_TFLOPS[kind]}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(last_case, args.cpu_tokens, K, I)

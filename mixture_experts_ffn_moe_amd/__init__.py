@@ -230,14 +230,21 @@ def fused_moe_mxfp4(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, ex
 
 
 def run_case(case, block_m=None, split=-1, stream=None, workspace=None, out=None,
-             align_out=None):
+             align_out=None, skip_align=False):
     """Planner + forward for a ``datagen.Case``-like object (attributes kind,
     x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, E, top_k).
-    Returns (out, (sorted_token_ids, expert_ids, num_tokens_post_padded))."""
+    Returns (out, (sorted_token_ids, expert_ids, num_tokens_post_padded)).
+    ``skip_align`` runs the fused forward alone on ``align_out`` as an earlier
+    call with the same routing and block_m filled it."""
     T = case.x.shape[0]
     if block_m is None:
         block_m = moe_select_block_m(T, case.top_k, case.E, case.kind, case.x.shape[1])
-    align = moe_align(case.topk_ids, case.E, block_m, stream=stream, out=align_out)
+    if skip_align:
+        if align_out is None:
+            raise ValueError("skip_align needs the align_out of an earlier call")
+        align = tuple(align_out)
+    else:
+        align = moe_align(case.topk_ids, case.E, block_m, stream=stream, out=align_out)
     args = dict(top_k=case.top_k, block_m=block_m, split=split, out=out, workspace=workspace,
                 stream=stream)
     if case.kind == "bf16":
