@@ -131,11 +131,23 @@ def load_traffic(workload, T, kernel_name):
     return None if e is None else e.get("bytes_per_launch")
 
 
-def summarize_counters(root, workload):
+# Counter runs of the traffic measurement: (directory tag, workload, tokens,
+# kernels).  Each run is a short bench.py of that workload and token count
+# under `rocprofv3 --pmc FETCH_SIZE` and, separately, `--pmc WRITE_SIZE`; the
+# fused-mode run forces the fused mode.
+COUNTER_RUNS = [
+    ("up", "fp8-k4096-i2048-e256-top6", 256, ("k_up", "k_down")),
+    ("fused", "fp8-k4096-i2048-e256-top6", 8, ("k_fused",)),
+    ("up4", "mxfp4-k4096-i2048-e256-top6", 256, ("k_up", "k_down")),
+]
+
+
+def summarize_counters(root):
     """Turn the rocprofv3 counter runs of the traffic measurement into
     profiles/hbm_traffic.json.  `root` holds one directory per run, named
-    pmc_{copy,up,fused}_{FETCH_SIZE,WRITE_SIZE} (see the command list in
-    profiles/hbm_traffic_*.md), each with the profiler's *_counter_collection.csv."""
+    pmc_{copy,<tag>}_{FETCH_SIZE,WRITE_SIZE} for the tags of COUNTER_RUNS (see
+    the command lists in profiles/hbm_traffic_*.md), each with the profiler's
+    *_counter_collection.csv."""
     import csv
     import glob
 
@@ -160,15 +172,16 @@ def summarize_counters(root, workload):
     fetch_factor = n / (fetch_copy * 1024)
     write_factor = n / (write_copy * 1024)
     entries = {}
-    for run, T, kname, sub in (("up", 256, "k_up", "::k_up<"), ("up", 256, "k_down", "::k_down<"),
-                               ("fused", 8, "k_fused", "::k_fused<")):
-        fk = values(run, "FETCH_SIZE", sub)
-        wk = values(run, "WRITE_SIZE", sub)
-        f_raw, w_raw = sum(fk) / len(fk), sum(wk) / len(wk)
-        fb, wb = f_raw * 1024 * fetch_factor, w_raw * 1024 * write_factor
-        entries[f"{workload}/T={T}/{kname}"] = {
-            "fetch_kib_raw": f_raw, "write_kib_raw": w_raw, "fetch_bytes": fb,
-            "write_bytes": wb, "bytes_per_launch": fb + wb, "dispatches": len(fk)}
+    for tag, workload, T, kernels in COUNTER_RUNS:
+        for kname in kernels:
+            sub = f"::{kname}<"
+            fk = values(tag, "FETCH_SIZE", sub)
+            wk = values(tag, "WRITE_SIZE", sub)
+            f_raw, w_raw = sum(fk) / len(fk), sum(wk) / len(wk)
+            fb, wb = f_raw * 1024 * fetch_factor, w_raw * 1024 * write_factor
+            entries[f"{workload}/T={T}/{kname}"] = {
+                "fetch_kib_raw": f_raw, "write_kib_raw": w_raw, "fetch_bytes": fb,
+                "write_bytes": wb, "bytes_per_launch": fb + wb, "dispatches": len(fk)}
     d = {"kernel_source_hash": kernel_source_hash(),
          "calibration": {"copy_bytes_read": n, "copy_bytes_written": n,
                          "fetch_kib_per_copy": fetch_copy, "write_kib_per_copy": write_copy,
@@ -234,16 +247,23 @@ def per_call(torch, fn, n, stream, flush=None):
 
 
 def gpu_clocks():
-    """Current GPU clocks as rocm-smi reports them (None where it is absent)."""
-    import subprocess
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
-                           text=True, timeout=20)
-        d = json.loads(r.stdout)
-    except Exception:
-        return None
-    card = next(iter(d.values()), {}) if isinstance(d, dict) else {}
-    return {k.strip(" :"): v for k, v in card.items() if "clock" in k.lower()}
+    """Current shader and memory clocks from the amdgpu sysfs DPM tables (the
+    level marked with '*'); None where the files are absent.  Read directly:
+    this process has initialised the GPU, and starting rocm-smi would exec."""
+    import glob
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        res = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    cur = [ln.split(":", 1)[1].strip(" *\n") for ln in f if ln.rstrip().endswith("*")]
+            except (OSError, IndexError):
+                continue
+            if cur:
+                res[name[7:]] = cur[0]
+        if res:
+            return res
+    return None
 
 
 def measured_ceilings(torch):
@@ -323,7 +343,7 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.workload)
+        summarize_counters(args.summarize_counters)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -418,13 +438,15 @@ def main():
         # per-call distributions: the whole call (planner + forward) and the
         # forward alone, warm (back to back), then cold (1 GiB written before
         # each call, outside its event pair: evicts L2 and the 256 MB MALL)
-        prot = {"full_warm": per_call(torch, step, args.calls, stream)}
+        prot = {}
 
         def op_only():
             moe.run_case(case, block_m=bm, split=split, workspace=ws, out=out,
                          align_out=align_out, skip_align=True)
 
-        prot["op_warm"] = per_call(torch, op_only, args.calls, stream)
+        if args.calls:
+            prot["full_warm"] = per_call(torch, step, args.calls, stream)
+            prot["op_warm"] = per_call(torch, op_only, args.calls, stream)
         if args.cold_calls:
             # a read, not a write: written scratch would leave the caches
             # dirty, and the call would pay for writing it back
