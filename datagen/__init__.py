@@ -143,8 +143,9 @@ def quant_mxfp4(w):
 # routing
 # ---------------------------------------------------------------------------
 
-def make_routing(T, E, top_k, routing, device="cpu", tag="routing", **kw):
-    """topk_ids (T, top_k) int32 and topk_weights (T, top_k) fp32."""
+def make_router_logits(T, E, top_k, routing, device="cpu", tag="routing", **kw):
+    """Router logits (T, E) fp32 of the given routing recipe ("uniform",
+    "normal", "normal_masked" with -inf for n_masked seeded experts, "zipf")."""
     g = _gen(device, tag, T, E, top_k, routing)
     if routing == "uniform":
         logits = torch.rand(T, E, generator=g, device=device)
@@ -159,7 +160,15 @@ def make_routing(T, E, top_k, routing, device="cpu", tag="routing", **kw):
         rank = torch.randperm(E, generator=gz).to(torch.float64) + 1.0
         bias = (-kw.get("zipf_s", 1.1) * torch.log(rank)).float()
         logits = logits + bias.to(device)[None, :]
-    probs = torch.softmax(logits.float(), dim=1)
+    return logits.float().contiguous()
+
+
+def make_routing(T, E, top_k, routing, device="cpu", tag="routing", **kw):
+    """topk_ids (T, top_k) int32 and topk_weights (T, top_k) fp32 for the
+    expert FFN's inputs: the recipe's logits through torch's softmax and
+    topk (a library stand-in for the model's gate)."""
+    logits = make_router_logits(T, E, top_k, routing, device=device, tag=tag, **kw)
+    probs = torch.softmax(logits, dim=1)
     w, ids = torch.topk(probs, top_k, dim=1, largest=True, sorted=True)
     w = w / w.sum(dim=1, keepdim=True)
     return ids.to(torch.int32).contiguous(), w.float().contiguous()

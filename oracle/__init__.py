@@ -14,6 +14,8 @@ align    the planner's output written as its plain definition (a stable
          grouping of route ids by expert, padded to ``block_m``).
 moe      the expert FFN step by step in fp64: dequantize, gate/up GEMM,
          SwiGLU, requantize, down GEMM, top-k weighted sum.
+router   the gate's routing from router logits: softmax over the experts,
+         the top-k largest (ties to the lower id), renormalized weights.
 
 Every function cites the page and passage of the source pages it follows.
 The sources are five web pages on fused MoE kernels:
