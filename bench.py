@@ -221,6 +221,38 @@ def cpu_baseline(case, n_tokens, K, I):
             "seconds": dt}
 
 
+def router_leg(torch, moe, datagen, spec, workload, T, bm, calls, stream):
+    """The router step to the left of the planner at this token count, on the
+    workload's router logits: the fused router + planner launch against
+    torch's softmax / topk / renormalization followed by the planner launch,
+    and the planner alone (median of per-call event pairs, back to back)."""
+    E, k = spec["E"], spec["top_k"]
+    kw = {key: spec[key] for key in ("n_masked", "zipf_s") if key in spec}
+    logits = datagen.make_router_logits(T, E, k, spec["routing"], device="cuda",
+                                        tag=workload, **kw)
+    ids, w, sid, eid, ntp = moe.moe_route_align(logits, k, bm)
+    outs = (ids, w, sid, eid, ntp)
+
+    def fused():
+        moe.moe_route_align(logits, k, bm, out=outs)
+
+    def separate():
+        p = torch.softmax(logits, dim=1)
+        tw, ti = torch.topk(p, k, dim=1)
+        tw = tw / tw.sum(dim=1, keepdim=True)
+        moe.moe_align(ti.to(torch.int32), E, bm, out=(sid, eid, ntp))
+
+    def planner():
+        moe.moe_align(ids, E, bm, out=(sid, eid, ntp))
+
+    res = {}
+    for name, fn in (("route_align_fused", fused), ("torch_router_then_planner", separate),
+                     ("planner_alone", planner)):
+        fn()
+        res[name] = per_call(torch, fn, calls, stream)["median_us"]
+    return res
+
+
 def percentiles(v):
     v = sorted(v)
     def at(q):
@@ -456,6 +488,9 @@ def main():
                                          flush=lambda: torch.sum(scratch, dim=0, out=sink))
             del scratch, sink
         sweep[-1]["per_call"] = prot
+        if args.calls:
+            sweep[-1]["router"] = router_leg(torch, moe, datagen, spec, args.workload, T, bm,
+                                             args.calls, stream)
         last_case = case
         del ws
 

@@ -102,6 +102,41 @@ int moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
               int32_t* num_tokens_post_padded, void* stream);
 
 /*
+ * Router and planner in one launch.  The gate's routing arrives at the
+ * planner as topk_ids and topk_weights ([prime-flash] "Usage"); the weights
+ * are the normalized routing weights ([hpc-ops RFC] "Results so far"); the
+ * planner is a grid-wide dependency ([hpc-ops RFC] "Design"), so the
+ * workgroups route their tokens and the last one to finish runs the planner.
+ *
+ *   logits                   (T, E) fp32 router logits, row-major; -inf marks
+ *                            an expert masked for that token.
+ *   topk_ids          [out]  (T, top_k) int32: the top_k largest logits of
+ *                            each token in descending order, equal logits to
+ *                            the lower expert id first (bit-exact).
+ *   topk_weights      [out]  (T, top_k) fp32: softmax over all E experts,
+ *                            renormalized over the selection (equivalently
+ *                            exp(l_j - l_max) / sum_sel exp(l_i - l_max)),
+ *                            fp32 arithmetic: within a few ulp of the exact
+ *                            value.
+ *   sorted_token_ids, expert_ids, num_tokens_post_padded [out]:
+ *                            exactly moe_align's outputs for that topk_ids.
+ *   ws, ws_bytes             device workspace of at least
+ *                            moe_route_align_workspace_size bytes, 16-byte
+ *                            aligned, all ZERO before the first call that
+ *                            uses it; every call leaves it zero.  Calls that
+ *                            may overlap need separate workspaces.
+ * E <= 1024, 1 <= top_k <= min(16, E).  NaN logits are not supported.
+ * Errors: as moe_align, plus MOE_ERR_UNSUPPORTED (top_k > 16 or > E),
+ * MOE_ERR_WORKSPACE (ws_bytes too small).  T == 0 writes moe_align's T == 0
+ * outputs.
+ */
+int moe_route_align_workspace_size(size_t* bytes);
+int moe_route_align(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t block_m,
+                    int32_t* topk_ids, float* topk_weights, int32_t* sorted_token_ids,
+                    int32_t* expert_ids, int32_t* num_tokens_post_padded, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/*
  * Mode choice by size ([prime-flash] introduction: split=False keeps the
  * intermediate on chip and accumulates a split-K down projection into the
  * output; split=True writes the H-wide activation once and runs the down

@@ -29,6 +29,7 @@ __all__ = [
     "moe_align_capacity", "moe_align", "moe_select_split", "moe_select_block_m",
     "moe_workspace_size", "moe_workspace_layout", "fused_moe_bf16",
     "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4", "EXPORTED_SYMBOLS",
+    "moe_route_align", "moe_route_align_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -41,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "moe_last_error", "moe_align_capacity", "moe_align", "moe_select_split",
     "moe_select_block_m", "moe_workspace_size", "moe_workspace_layout",
     "fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4",
-    "moe_set_timing_events",
+    "moe_set_timing_events", "moe_route_align_workspace_size", "moe_route_align",
 )
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
@@ -89,6 +90,8 @@ def lib():
     L.fused_moe_mxfp8.argtypes = [_P, _P, _P, _P, _P, _P] + tail
     L.fused_moe_mxfp4.argtypes = [_P, _P, _P, _P, _P, _P] + tail
     L.moe_set_timing_events.argtypes = [_P, _P, _I32]
+    L.moe_route_align_workspace_size.argtypes = [ctypes.POINTER(_SZ)]
+    L.moe_route_align.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
     for name in EXPORTED_SYMBOLS:
         if name != "moe_last_error":
             getattr(L, name).restype = ctypes.c_int
@@ -145,6 +148,45 @@ def moe_align(topk_ids, num_experts, block_m, stream=None, out=None):
     _check(lib().moe_align(_ptr(topk_ids.contiguous()), T, k, num_experts, block_m,
                            _ptr(sorted_ids), _ptr(expert_ids), _ptr(ntp), _stream(stream)))
     return sorted_ids, expert_ids, ntp
+
+
+def moe_route_align_workspace_size():
+    out = _SZ()
+    _check(lib().moe_route_align_workspace_size(ctypes.byref(out)))
+    return out.value
+
+
+_route_ws = {}
+
+
+def moe_route_align(logits, top_k, block_m, stream=None, out=None, workspace=None):
+    """Router + planner in one launch: (T, E) fp32 logits -> (topk_ids,
+    topk_weights, sorted_token_ids, expert_ids, num_tokens_post_padded).
+    ``out`` may pass those five preallocated.  ``workspace`` must hold zeros
+    before its first use (each call leaves it zero); by default one zeroed
+    buffer per device is kept and reused, so calls on several streams of one
+    device must pass their own."""
+    T, E = logits.shape
+    rows, blocks = moe_align_capacity(T, top_k, E, block_m)
+    dev = logits.device
+    if out is not None:
+        ids, w, sorted_ids, expert_ids, ntp = out
+    else:
+        ids = torch.empty(T, top_k, dtype=torch.int32, device=dev)
+        w = torch.empty(T, top_k, dtype=torch.float32, device=dev)
+        sorted_ids = torch.empty(max(rows, 1), dtype=torch.int32, device=dev)[:rows]
+        expert_ids = torch.empty(max(blocks, 1), dtype=torch.int32, device=dev)[:blocks]
+        ntp = torch.empty(1, dtype=torch.int32, device=dev)
+    if workspace is None:
+        key = (dev.type, dev.index)
+        if key not in _route_ws:
+            _route_ws[key] = torch.zeros(moe_route_align_workspace_size(), dtype=torch.uint8,
+                                         device=dev)
+        workspace = _route_ws[key]
+    _check(lib().moe_route_align(_ptr(logits.contiguous()), T, E, top_k, block_m, _ptr(ids),
+                                 _ptr(w), _ptr(sorted_ids), _ptr(expert_ids), _ptr(ntp),
+                                 _ptr(workspace), workspace.numel(), _stream(stream)))
+    return ids, w, sorted_ids, expert_ids, ntp
 
 
 def moe_select_split(dtype, T, K, N, num_experts, top_k, block_m):

@@ -230,6 +230,40 @@ int moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int3
   return ok();
 }
 
+int moe_route_align_workspace_size(size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+  *bytes = 256;
+  return ok();
+}
+
+int moe_route_align(const float* logits, int64_t T, int32_t E, int32_t top_k, int32_t block_m,
+                    int32_t* topk_ids, float* topk_weights, int32_t* sorted_token_ids,
+                    int32_t* expert_ids, int32_t* num_tokens_post_padded, void* ws,
+                    size_t ws_bytes, void* stream) {
+  int64_t rows, blocks;
+  int rc = moe_align_capacity(T, top_k, E, block_m, &rows, &blocks);
+  if (rc) return rc;
+  if (E > 1024) return fail(MOE_ERR_UNSUPPORTED, "moe_route_align supports E <= 1024 (got %d)", E);
+  if (top_k > 16 || top_k > E)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_route_align needs top_k <= 16 and <= E (got %d)", top_k);
+  if (T * (int64_t)E >= (int64_t(1) << 40)) return fail(MOE_ERR_SHAPE, "T*E too large");
+  if (!num_tokens_post_padded || !ws || (rows > 0 && (!sorted_token_ids || !expert_ids)) ||
+      (T > 0 && (!logits || !topk_ids || !topk_weights)))
+    return fail(MOE_ERR_NULL, "a required pointer is NULL");
+  const void* ps[] = {logits, topk_ids, topk_weights, sorted_token_ids, expert_ids};
+  for (const void* p : ps)
+    if (p && !aligned(p, 16)) return fail(MOE_ERR_ALIGN, "tensors must be 16-byte aligned");
+  if (!aligned(num_tokens_post_padded, 4) || !aligned(ws, 16))
+    return fail(MOE_ERR_ALIGN, "num_tokens_post_padded must be 4-byte and ws 16-byte aligned");
+  if (ws_bytes < 256) return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < 256 bytes", ws_bytes);
+  hipError_t e = launch_route_align(logits, (int)T, E, top_k, block_m, topk_ids, topk_weights,
+                                    sorted_token_ids, expert_ids, num_tokens_post_padded,
+                                    (int)rows, (int)blocks, static_cast<int*>(ws),
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int moe_set_timing_events(void* before, void* after, int32_t which) {
   if (which < 0 || which > 2) return fail(MOE_ERR_UNSUPPORTED, "which must be 0, 1 or 2");
   g_hook.before = static_cast<hipEvent_t>(before);

@@ -30,11 +30,12 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBatch = 8;
 
-__global__ void __launch_bounds__(kThreads)
-k_align(const int32_t* __restrict__ ids, int R, int E, int bm, int32_t* __restrict__ sorted,
-        int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntp_out, int sorted_cap,
-        int blocks_cap) {
-  extern __shared__ int smem[];
+// The planner on one workgroup of kWaves waves; smem holds
+// kWaves * E + 2 * E + kWaves + 1 ints.
+__device__ __forceinline__ void align_body(const int32_t* __restrict__ ids, int R, int E, int bm,
+                           int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
+                           int32_t* __restrict__ ntp_out, int sorted_cap, int blocks_cap,
+                           int* smem) {
   int* cnt = smem;                     // [kWaves][E]: counts, then cursors
   int* off = smem + kWaves * E;        // [E]: segment start
   int* tot = off + E;                  // [E]: route count
@@ -142,7 +143,198 @@ k_align(const int32_t* __restrict__ ids, int R, int E, int bm, int32_t* __restri
   }
 }
 
+__global__ void __launch_bounds__(kThreads)
+k_align(const int32_t* __restrict__ ids, int R, int E, int bm, int32_t* __restrict__ sorted,
+        int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntp_out, int sorted_cap,
+        int blocks_cap) {
+  extern __shared__ int smem[];
+  align_body(ids, R, E, bm, sorted, expert_ids, ntp_out, sorted_cap, blocks_cap, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Router + planner in one launch.
+//
+// The gate's routing ([prime-flash] "Usage": it arrives at the planner as
+// topk_ids and topk_weights; [hpc-ops RFC] "Results so far": normalized
+// routing weights) is computed from the router logits, then the planner runs
+// on it.  The planner needs every token's routes (grid-wide histogram and
+// prefix, [hpc-ops RFC] "Design"), so the workgroups route their tokens,
+// publish them, and take a ticket; the last one to arrive runs the planner on
+// the whole routing.  No workgroup waits for another.
+//
+// Routing of one token by one wave: lane l holds logits l, l + 64, ... (EPL
+// of them); k rounds each pick the largest logit not yet taken, ties to the
+// lower expert id, by a wave-wide arg-max; the selected ids come out in
+// descending logit order.  Weights: the softmax over all experts renormalized
+// over the selection equals exp(l_j - l_max) / sum over the selection of
+// exp(l_i - l_max), in fp32 with the library expf and an IEEE division.
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxTopK = 16;
+
+// (v, i) beats (bv, bi): larger logit, or equal logit and lower id; i < 0 is
+// "nothing" and never beats anything
+__device__ __forceinline__ bool beats(float v, int i, float bv, int bi) {
+  return i >= 0 && (bi < 0 || v > bv || (v == bv && i < bi));
+}
+
+// one DPP step of the row-wide arg-max: (bv, bi) against its partner lane
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& bv, int& bi) {
+  const float ov = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, bv), __builtin_bit_cast(int, bv),
+                                         CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(bi, bi, CTRL, 0xF, 0xF, false);
+  if (beats(ov, oi, bv, bi)) bv = ov, bi = oi;
+}
+
+// Wave-wide arg-max: xor 1 and xor 2 inside quads, then the half-row and row
+// mirrors (every lane of a 16-lane row holds the row's best), then the four
+// rows' results read out and combined (uniform over the wave).
+__device__ __forceinline__ void wave_argmax(float& bv, int& bi) {
+  argmax_step<0xB1>(bv, bi);   // quad_perm [1, 0, 3, 2]
+  argmax_step<0x4E>(bv, bi);   // quad_perm [2, 3, 0, 1]
+  argmax_step<0x141>(bv, bi);  // row_half_mirror
+  argmax_step<0x140>(bv, bi);  // row_mirror
+  float rv[4];
+  int ri[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    rv[q] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 16 * q));
+    ri[q] = __builtin_amdgcn_readlane(bi, 16 * q);
+  }
+  if (beats(rv[1], ri[1], rv[0], ri[0])) rv[0] = rv[1], ri[0] = ri[1];
+  if (beats(rv[3], ri[3], rv[2], ri[2])) rv[2] = rv[3], ri[2] = ri[3];
+  if (beats(rv[2], ri[2], rv[0], ri[0])) rv[0] = rv[2], ri[0] = ri[2];
+  bv = rv[0];
+  bi = ri[0];
+}
+
+template <int EPL>
+__device__ __forceinline__ void load_token(const float* __restrict__ row, int E, int lane,
+                                           float (&v)[EPL]) {
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? row[e] : 0.f;
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void route_token(const float (&v)[EPL], int E, int k,
+                                            int32_t* __restrict__ ids_out,
+                                            float* __restrict__ w_out, int lane) {
+  uint32_t taken = 0;  // bit j: slot j is taken (or lies past E)
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+    if (lane + 64 * j >= E) taken |= 1u << j;
+  float sv[kMaxTopK];
+  int si[kMaxTopK];
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r) {
+    if (r >= k) break;
+    float bv = 0.f;
+    int bi = -1;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)  // ascending ids: a later equal logit never wins
+      if (!((taken >> j) & 1u) && beats(v[j], lane + 64 * j, bv, bi)) bv = v[j], bi = lane + 64 * j;
+    wave_argmax(bv, bi);
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    sv[r] = bv;
+    si[r] = bi;
+  }
+  float ex[kMaxTopK];
+  float sum = 0.f;
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r) {
+    if (r >= k) break;
+    ex[r] = expf(sv[r] - sv[0]);
+    sum += ex[r];
+  }
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r) {
+    if (r >= k) break;
+    if (lane == r) {
+      ids_out[r] = si[r];
+      w_out[r] = ex[r] / sum;
+    }
+  }
+}
+
+// tokens whose logits a wave loads at once (registers: NB * EPL per lane)
+template <int EPL>
+constexpr int route_batch() { return EPL <= 2 ? 4 : EPL <= 8 ? 2 : 1; }
+
+template <int EPL>
+__global__ void __launch_bounds__(kThreads)
+k_route_align(const float* __restrict__ logits, int T, int E, int top_k, int bm,
+              int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+              int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
+              int32_t* __restrict__ ntp_out, int sorted_cap, int blocks_cap,
+              int* __restrict__ ticket, int tokens_per_wg) {
+  extern __shared__ int smem[];
+  __shared__ int is_last;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * tokens_per_wg;
+  const int t1 = min(T, t0 + tokens_per_wg);
+  constexpr int NB = route_batch<EPL>();
+  for (int t = t0 + w; t < t1; t += kWaves * NB) {
+    float v[NB][EPL];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      if (t + b * kWaves < t1) load_token<EPL>(logits + (size_t)(t + b * kWaves) * E, E, lane, v[b]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int tb = t + b * kWaves;
+      if (tb < t1)
+        route_token<EPL>(v[b], E, top_k, topk_ids + (size_t)tb * top_k,
+                         topk_w + (size_t)tb * top_k, lane);
+    }
+  }
+  if (gridDim.x == 1) {
+    // one workgroup routed every token: a workgroup barrier publishes them
+    __syncthreads();
+  } else {
+    // release this workgroup's routes device-wide, then take a ticket
+    __threadfence();
+    __syncthreads();
+    if (threadIdx.x == 0) is_last = atomicAdd(ticket, 1) == (int)gridDim.x - 1;
+    __syncthreads();
+    if (!is_last) return;
+    // acquire the other workgroups' routes; leave the ticket at zero for the
+    // next call (an atomic, so that it reaches the point where the next
+    // call's atomics are performed)
+    __threadfence();
+    if (threadIdx.x == 0) atomicExch(ticket, 0);
+  }
+  align_body(topk_ids, T * top_k, E, bm, sorted, expert_ids, ntp_out, sorted_cap, blocks_cap,
+             smem);
+}
+
 }  // namespace
+
+hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int block_m,
+                              int32_t* topk_ids, float* topk_w, int32_t* sorted,
+                              int32_t* expert_ids, int32_t* ntp, int sorted_cap, int blocks_cap,
+                              int* ticket, hipStream_t stream) {
+  const size_t smem = (size_t)(kWaves * E + 2 * E + kWaves + 1) * sizeof(int);
+  // one token per wave up to 256 workgroups, then more tokens per wave
+  const int want = (T + kWaves - 1) / kWaves;
+  const int groups = want < 1 ? 1 : (want > 256 ? 256 : want);
+  const int per = (T + groups - 1) / groups;
+  const int epl = (E + 63) / 64;
+#define MOE_ROUTE(N)                                                                          \
+  hipLaunchKernelGGL(k_route_align<N>, dim3(groups), dim3(kThreads), smem, stream, logits, T, E, \
+                     top_k, block_m, topk_ids, topk_w, sorted, expert_ids, ntp, sorted_cap,   \
+                     blocks_cap, ticket, per)
+  if (epl <= 1) MOE_ROUTE(1);
+  else if (epl <= 2) MOE_ROUTE(2);
+  else if (epl <= 4) MOE_ROUTE(4);
+  else if (epl <= 8) MOE_ROUTE(8);
+  else MOE_ROUTE(16);
+#undef MOE_ROUTE
+  return hipGetLastError();
+}
 
 hipError_t launch_align(const int32_t* topk_ids, int R, int E, int block_m, int32_t* sorted,
                         int32_t* expert_ids, int32_t* ntp, int sorted_cap, int blocks_cap,

@@ -31,6 +31,13 @@ hipError_t launch_align(const int32_t* topk_ids, int R, int E, int block_m,
                         int32_t* sorted, int32_t* expert_ids, int32_t* ntp,
                         int sorted_cap, int blocks_cap, hipStream_t stream);
 
+// Router (softmax, top-k, renormalized weights) and planner in one launch;
+// `ticket` is one int of workspace, zero before the call and after it.
+hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int block_m,
+                              int32_t* topk_ids, float* topk_w, int32_t* sorted,
+                              int32_t* expert_ids, int32_t* ntp, int sorted_cap, int blocks_cap,
+                              int* ticket, hipStream_t stream);
+
 // Events recorded around one kernel of a launch_moe sequence (profiling).
 struct TimingHook {
   hipEvent_t before = nullptr, after = nullptr;

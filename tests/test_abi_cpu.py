@@ -58,6 +58,28 @@ def test_align_errors_before_launch():
     assert b"aligned" in L.moe_last_error()
 
 
+def test_route_align_errors_before_launch():
+    L = moe.lib()
+    P = ctypes.c_void_p
+
+    def call(T=4, E=8, k=2, bm=16, logits=FAKE, ids=FAKE, ws=FAKE, ws_bytes=256):
+        return L.moe_route_align(P(logits) if logits else None, T, E, k, bm, P(ids) if ids else None,
+                                 P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(ws) if ws else None,
+                                 ws_bytes, None)
+    assert moe.moe_route_align_workspace_size() == 256
+    assert call(E=2000) == -3                  # E > 1024
+    assert call(k=17, E=64) == -3              # top_k > 16
+    assert call(k=9, E=8) == -3                # top_k > E
+    assert call(bm=48) == -3
+    assert call(T=-1) == -2
+    assert call(logits=0) == -1
+    assert call(ids=0) == -1
+    assert call(ws=0) == -1
+    assert call(logits=FAKE + 4) == -4         # misaligned
+    assert call(ws_bytes=8) == -5
+    assert b"workspace" in L.moe_last_error()
+
+
 def _ffn(L, fn, K=4096, N=4096, T=8, E=16, k=2, bm=16, split=-1, ws=FAKE, ws_bytes=1 << 40,
          x=FAKE, sorted_ids=FAKE, scales=True):
     P = ctypes.c_void_p
