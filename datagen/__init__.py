@@ -195,6 +195,7 @@ class Case:
     topk_ids: torch.Tensor
     topk_weights: torch.Tensor
     extra: dict = field(default_factory=dict)
+    n_shared: int = 0   # shared experts stored after the E routed ones in w1 / w2
 
     @property
     def N(self):
@@ -262,16 +263,18 @@ def make_tokens(kind, T, K, device="cpu", tag="x"):
 
 
 def make_case(kind, T, K, I, E, top_k, routing="uniform", device="cpu",
-              tag="case", weights=None, **kw):
+              tag="case", weights=None, n_shared=0, **kw):
     """A full input set.  ``weights`` may pass a (w1, s1, w2, s2) tuple to
-    reuse one weight set across token counts."""
+    reuse one weight set across token counts.  ``n_shared`` adds that many
+    shared experts after the E routed ones in the weights (routing stays over
+    the E routed experts)."""
     if weights is None:
-        weights = make_weights(kind, K, I, E, device=device, tag=tag,
+        weights = make_weights(kind, K, I, E + n_shared, device=device, tag=tag,
                                w_std=kw.get("w_std"))
     w1, s1, w2, s2 = weights
     x, xs = make_tokens(kind, T, K, device=device, tag=tag)
     ids, wts = make_routing(T, E, top_k, routing, device=device, tag=tag, **kw)
-    return Case(kind, T, K, I, E, top_k, x, xs, w1, s1, w2, s2, ids, wts)
+    return Case(kind, T, K, I, E, top_k, x, xs, w1, s1, w2, s2, ids, wts, n_shared=n_shared)
 
 
 def make_workload_case(name, T, device="cpu", weights=None):
@@ -321,4 +324,5 @@ def to_numpy(case, experts=None):
     return dict(kind=case.kind, x=bits(case.x), x_scale=bits(case.x_scale),
                 w1=wsel(case.w1), w1_scale=wsel(case.w1_scale),
                 w2=wsel(case.w2), w2_scale=wsel(case.w2_scale),
-                topk_ids=bits(case.topk_ids), topk_weights=bits(case.topk_weights))
+                topk_ids=bits(case.topk_ids), topk_weights=bits(case.topk_weights),
+                n_shared=case.n_shared)

@@ -196,8 +196,20 @@ def requant_bf16(h):
     return codecs.bf16_encode(hd), None, hd, alt
 
 
+def _shared_expert(e_routed, s):
+    """Weight index of shared expert s: stored after the routed experts."""
+    return e_routed + s
+
+
+def _shared_weight():
+    """Weight of a shared expert's output in the sum: the shared experts
+    take every token and are not scaled by the router."""
+    return 1.0
+
+
 def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
-            topk_weights, tokens=None, exact_h=False, keep_h=False, h_perturb=None):
+            topk_weights, tokens=None, exact_h=False, keep_h=False, h_perturb=None,
+            n_shared=0):
     """Fused MoE forward, fp64.
 
     Arrays are numpy: bf16 data as uint16 bit patterns, e4m3 data as uint8
@@ -215,6 +227,13 @@ def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
     intermediate: codes, scales and dequantized values.
     ``h_perturb``: test hook, a function applied to each expert's fp64 h
     before requantization (to model a kernel's fp32 deviations).
+    ``n_shared``: the last n_shared experts of w1 / w2 are shared experts
+    ([DeepGEMM #411] "Summary" fuses routed and shared L1 / L2; [DeepGEMM
+    #88] "Performance" runs the shared expert as a separate GEMM): every
+    token's output adds each shared expert's FFN with weight 1, computed
+    exactly like a routed expert's.  Routed ids then count as local only in
+    [0, E - n_shared).  With keep_h, shared route (t, s) is keyed
+    T*top_k + t*n_shared + s.
 
     Returns a dict with ``out64`` (n, K) fp64, ``out_bf16`` (n, K) uint16,
     ``flip_bound`` (n, K) fp64 (the near-tie allowance, see the module
@@ -223,8 +242,17 @@ def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
     """
     ids = np.asarray(topk_ids, dtype=np.int64)
     wts = np.asarray(topk_weights, dtype=np.float32).astype(np.float64)
-    T, k = ids.shape
-    E = w1.shape[0]
+    T, k_routed = ids.shape
+    E_all = w1.shape[0]
+    E = E_all - n_shared                                # routed experts
+    if n_shared:
+        # routes outside the routed experts are skipped; then one route per
+        # (token, shared expert) with weight 1
+        ids = np.where((ids >= 0) & (ids < E), ids, -1)
+        sh = np.array([_shared_expert(E, s) for s in range(n_shared)], dtype=np.int64)
+        ids = np.concatenate([ids, np.broadcast_to(sh, (T, n_shared))], axis=1)
+        wts = np.concatenate([wts, np.full((T, n_shared), _shared_weight())], axis=1)
+    k = ids.shape[1]
     K = w1.shape[2] * (2 if kind == "mxfp4" else 1)
     I = w1.shape[1] // 2
     if tokens is None:
@@ -244,7 +272,7 @@ def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
     else:
         raise ValueError(kind)
     for e in np.unique(sel):
-        if e < 0 or e >= E:
+        if e < 0 or e >= E_all or (e >= E and not n_shared):
             continue                                    # not a local expert
         n_idx, j_idx = np.nonzero(sel == e)
         t_rows = tokens[n_idx]
@@ -280,8 +308,8 @@ def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
             if yb is not None:
                 bound[local[t]] += abs(wts[t, j]) * yb[r]
             if keep_h:
-                hkeep[t * k + j] = (None if q is None else q[r],
-                                    None if s is None else s[r], hd[r])
+                key = t * k_routed + j if j < k_routed else T * k_routed + t * n_shared + j - k_routed
+                hkeep[key] = (None if q is None else q[r], None if s is None else s[r], hd[r])
     res = {"out64": out64, "out_bf16": codecs.bf16_encode(out64), "flip_bound": bound}
     if keep_h:
         res["h"] = hkeep

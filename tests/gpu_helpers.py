@@ -28,10 +28,11 @@ def oracle(case, tokens=None, keep_h=False):
     ids = case.topk_ids.cpu().numpy()
     sel = ids if tokens is None else ids[np.asarray(tokens)]
     experts = sorted(set(int(e) for e in np.unique(sel) if 0 <= e < case.E))
+    experts += [case.E + s for s in range(case.n_shared)]
     d = datagen.to_numpy(case, experts=experts)
     return moe_ref(d["kind"], d["x"], d["x_scale"], d["w1"], d["w1_scale"], d["w2"],
                    d["w2_scale"], d["topk_ids"], d["topk_weights"], tokens=tokens,
-                   keep_h=keep_h)
+                   keep_h=keep_h, n_shared=case.n_shared)
 
 
 def check(case, block_m, split, tokens=None, ref=None, label=""):
