@@ -145,10 +145,30 @@ __device__ __forceinline__ f32x4 mfma_step_mx(const Frag<KIND_MX>& a, const Frag
 }
 
 // The same with B in e2m1 (format 4: only the first four registers are read).
+// e4m3 A x e2m1 B (blgp 4), emitted with its wait states.  Measured on the
+// MI355X: where the compiler read the accumulator of this instruction 7
+// instructions and 7 wait states after it (copying it between registers),
+// the copy held the value from before the instruction, and the down GEMM
+// lost one K step of one row in every 16-column tile; whether it happened
+// depended on the code around it.  The instruction issues at the e4m3 rate
+// (measured), slower than an e2m1 x e2m1 one, and the compiler's wait states
+// after it are too few.  Written as asm with 32 wait states after it (and 5
+// before, for operands written just before), nothing reads its result
+// sooner: every reader depends on the asm's output.  The accumulator stays
+// in accumulation registers (D = C).
 __device__ __forceinline__ f32x4 mfma_step_mx4(const Frag<KIND_MX4>& a, const FragB<KIND_MX4>& b,
                                                f32x4 acc, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-      as_i32x8(a.c[0], a.c[1]), as_i32x8(b.c[0], make_uint4(0, 0, 0, 0)), acc, 0, 4, 0, sa, 0, sb);
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x8 av = as_i32x8(a.c[0], a.c[1]);
+  const i32x4 bv = __builtin_bit_cast(i32x4, b.c[0]);
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] blgp:4\n\t"
+      "s_nop 15\n\t"
+      "s_nop 15"
+      : "+a"(acc)
+      : "v"(av), "v"(bv), "v"(sa), "v"(sb));
+  return acc;
 }
 
 // MX-scaled step for either MX kind (the B fragment type follows the kind).
