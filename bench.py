@@ -221,6 +221,51 @@ def cpu_baseline(case, n_tokens, K, I):
             "seconds": dt}
 
 
+def shared_leg(torch, moe, datagen, case, shared_w, calls, stream):
+    """One shared expert at this token count: one call that runs it with the
+    routed experts (planner + forward, split mode) against the routed call
+    followed by the shared expert as a call of its own (every token routed to
+    it with weight 1) and an add of the two outputs (median of per-call event
+    pairs, back to back)."""
+    import dataclasses
+    sw, cat = shared_w
+    T, E, k = case.T, case.E, case.top_k
+    both = dataclasses.replace(case, w1=cat[0], w1_scale=cat[1], w2=cat[2], w2_scale=cat[3],
+                               n_shared=1)
+    alone = dataclasses.replace(case, w1=sw[0], w1_scale=sw[1], w2=sw[2], w2_scale=sw[3], E=1,
+                                top_k=1, topk_ids=torch.zeros_like(case.topk_ids[:, :1]),
+                                topk_weights=torch.ones_like(case.topk_weights[:, :1]))
+    bm_both = moe.moe_select_block_m(T, k + 1, E + 1, case.kind, case.K)
+    bm_r = moe.moe_select_block_m(T, k, E, case.kind, case.K)
+    bm_s = moe.moe_select_block_m(T, 1, 1, case.kind, case.K)
+    out = torch.empty(T, case.K, dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty_like(out)
+    ws = {}
+
+    def run(c, bm, o):
+        key = id(c)
+        if key not in ws:
+            need = moe.moe_workspace_size(c.kind, T, c.K, 2 * c.I, c.E + c.n_shared,
+                                          c.top_k + c.n_shared, bm, 1)
+            ws[key] = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+        moe.run_case(c, block_m=bm, split=1, workspace=ws[key], out=o)
+
+    def fused():
+        run(both, bm_both, out)
+
+    def separate():
+        run(case, bm_r, out)
+        run(alone, bm_s, out2)
+        out.add_(out2)
+
+    res = {}
+    for name, fn in (("routed_and_shared_one_call", fused),
+                     ("routed_then_shared_then_add", separate)):
+        fn()
+        res[name] = per_call(torch, fn, calls, stream)["median_us"]
+    return res
+
+
 def router_leg(torch, moe, datagen, spec, workload, T, bm, calls, stream):
     """The router step to the left of the planner at this token count, on the
     workload's router logits: the fused router + planner launch against
@@ -412,6 +457,13 @@ def main():
     weights = datagen.make_weights(kind, K, I, E, device=dev, tag=args.workload,
                                    w_std=spec.get("w_std"))
     torch.cuda.synchronize()
+    # one shared expert of the same format, stored after the routed ones
+    shared_w = None
+    if args.calls:
+        sw = datagen.make_weights(kind, K, I, 1, device=dev, tag=args.workload + "/shared",
+                                  w_std=spec.get("w_std"))
+        shared_w = (sw, [None if a is None else torch.cat([a, b]) for a, b in zip(weights, sw)])
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     sweep = []
     last_case = None
@@ -491,6 +543,8 @@ def main():
         if args.calls:
             sweep[-1]["router"] = router_leg(torch, moe, datagen, spec, args.workload, T, bm,
                                              args.calls, stream)
+            sweep[-1]["shared"] = shared_leg(torch, moe, datagen, case, shared_w, args.calls,
+                                             stream)
         last_case = case
         del ws
 

@@ -290,6 +290,46 @@ int fused_moe_mxfp4(const void* x, const uint8_t* x_scale, const void* w1,
                     void* stream);
 
 /*
+ * Shared experts.  [DeepGEMM #411] "Summary" runs the routed and the shared
+ * experts' two GEMMs in one kernel; [DeepGEMM #88] "Performance" runs the
+ * shared expert as a separate GEMM.  A shared expert is an FFN of the same
+ * format as the routed ones that every token adds with weight 1; here it is
+ * computed by the same kernels, as one more route per token.
+ *
+ * Planner: moe_align with n_shared shared experts numbered E .. E+n_shared-1:
+ * routes t*top_k + j keep topk_ids[t][j] (local only in [0, E)), and route
+ * T*top_k + t*n_shared + s goes to expert E + s.  Capacities are
+ * moe_align_capacity(T, top_k + n_shared, E + n_shared, block_m).  Errors as
+ * moe_align, plus MOE_ERR_SHAPE (n_shared < 0), MOE_ERR_UNSUPPORTED
+ * (E + n_shared > 1024).
+ */
+int moe_align_shared(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
+                     int32_t n_shared, int32_t block_m, int32_t* sorted_token_ids,
+                     int32_t* expert_ids, int32_t* num_tokens_post_padded, void* stream);
+
+/*
+ * Forward with shared experts, any dtype (dtype: moe_dtype; operands and
+ * scales as in that dtype's fused_moe_* entry point, bf16 passes NULL
+ * scales).  w1, w2 and their scales hold E + n_shared experts: the E routed
+ * ones, then the n_shared shared ones (concatenated once at load time).
+ * sorted_token_ids / expert_ids / num_tokens_post_padded come from
+ * moe_align_shared with the same n_shared.  E is the routed expert count and
+ * top_k the routed top-k; the workspace is moe_workspace_size(dtype, T, K, N,
+ * E + n_shared, top_k + n_shared, block_m, split).
+ *   out[t] = bf16(sum_j topk_weights[t][j] * FFN_{topk_ids[t][j]}(x[t])
+ *                 + sum_s FFN_{E+s}(x[t]))
+ * one rounding at the end.  n_shared = 0 is exactly the fused_moe_* call.
+ * Errors as the fused_moe_* entry points, plus MOE_ERR_SHAPE (n_shared < 0).
+ */
+int fused_moe_shared(int32_t dtype, const void* x, const void* x_scale, const void* w1,
+                     const void* w1_scale, const void* w2, const void* w2_scale,
+                     int32_t n_shared, const int32_t* sorted_token_ids,
+                     const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                     const float* topk_weights, void* out, int64_t T, int64_t K, int64_t N,
+                     int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * Profiling hook (changes no result): the next fused_moe_* calls made by the
  * calling thread record the caller's hipEvent_t handles `before` and `after`
  * (passed as void*) on their stream immediately before and after one kernel:

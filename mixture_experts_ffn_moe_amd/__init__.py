@@ -29,7 +29,7 @@ __all__ = [
     "moe_align_capacity", "moe_align", "moe_select_split", "moe_select_block_m",
     "moe_workspace_size", "moe_workspace_layout", "fused_moe_bf16",
     "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4", "EXPORTED_SYMBOLS",
-    "moe_route_align", "moe_route_align_workspace_size",
+    "moe_route_align", "moe_route_align_workspace_size", "moe_align_shared", "fused_moe_shared",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -43,6 +43,7 @@ EXPORTED_SYMBOLS = (
     "moe_select_block_m", "moe_workspace_size", "moe_workspace_layout",
     "fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4",
     "moe_set_timing_events", "moe_route_align_workspace_size", "moe_route_align",
+    "moe_align_shared", "fused_moe_shared",
 )
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
@@ -92,6 +93,8 @@ def lib():
     L.moe_set_timing_events.argtypes = [_P, _P, _I32]
     L.moe_route_align_workspace_size.argtypes = [ctypes.POINTER(_SZ)]
     L.moe_route_align.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    L.moe_align_shared.argtypes = [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P]
+    L.fused_moe_shared.argtypes = [_I32, _P, _P, _P, _P, _P, _P, _I32] + tail
     for name in EXPORTED_SYMBOLS:
         if name != "moe_last_error":
             getattr(L, name).restype = ctypes.c_int
@@ -189,6 +192,49 @@ def moe_route_align(logits, top_k, block_m, stream=None, out=None, workspace=Non
     return ids, w, sorted_ids, expert_ids, ntp
 
 
+def moe_align_shared(topk_ids, num_experts, n_shared, block_m, stream=None, out=None):
+    """Planner with ``n_shared`` shared experts (ids num_experts ..
+    num_experts + n_shared - 1) that every token routes to after its routed
+    experts; returns (sorted_token_ids, expert_ids, num_tokens_post_padded)."""
+    T, k = topk_ids.shape
+    rows, blocks = moe_align_capacity(T, k + n_shared, num_experts + n_shared, block_m)
+    dev = topk_ids.device
+    if out is not None:
+        sorted_ids, expert_ids, ntp = out
+    else:
+        sorted_ids = torch.empty(max(rows, 1), dtype=torch.int32, device=dev)[:rows]
+        expert_ids = torch.empty(max(blocks, 1), dtype=torch.int32, device=dev)[:blocks]
+        ntp = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().moe_align_shared(_ptr(topk_ids.contiguous()), T, k, num_experts, n_shared,
+                                  block_m, _ptr(sorted_ids), _ptr(expert_ids), _ptr(ntp),
+                                  _stream(stream)))
+    return sorted_ids, expert_ids, ntp
+
+
+def fused_moe_shared(dtype, x, x_scale, w1, w1_scale, w2, w2_scale, n_shared, sorted_token_ids,
+                     expert_ids, num_tokens_post_padded, topk_weights, top_k, block_m, split=-1,
+                     out=None, workspace=None, stream=None):
+    """Forward with shared experts: w1 / w2 (and scales) hold the routed
+    experts followed by ``n_shared`` shared ones; planner outputs from
+    moe_align_shared."""
+    T, K = x.shape
+    E_all, N, _ = w1.shape
+    E = E_all - n_shared
+    dev = w1.device
+    if out is None:
+        out = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
+    need = moe_workspace_size(dtype, T, K, N, E_all, top_k + n_shared, block_m, split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib().fused_moe_shared(_DTYPE_CODE.get(dtype, dtype), _ptr(x), _ptr(x_scale), _ptr(w1),
+                                  _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), n_shared,
+                                  _ptr(sorted_token_ids), _ptr(expert_ids),
+                                  _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(out), T,
+                                  K, N, E, top_k, block_m, split, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
 def moe_select_split(dtype, T, K, N, num_experts, top_k, block_m):
     out = _I32()
     _check(lib().moe_select_split(_DTYPE_CODE.get(dtype, dtype), T, K, N, num_experts, top_k,
@@ -281,15 +327,21 @@ def run_case(case, block_m=None, split=-1, stream=None, workspace=None, out=None
     T = case.x.shape[0]
     if block_m is None:
         block_m = moe_select_block_m(T, case.top_k, case.E, case.kind, case.x.shape[1])
+    S = getattr(case, "n_shared", 0)
     if skip_align:
         if align_out is None:
             raise ValueError("skip_align needs the align_out of an earlier call")
         align = tuple(align_out)
+    elif S:
+        align = moe_align_shared(case.topk_ids, case.E, S, block_m, stream=stream, out=align_out)
     else:
         align = moe_align(case.topk_ids, case.E, block_m, stream=stream, out=align_out)
     args = dict(top_k=case.top_k, block_m=block_m, split=split, out=out, workspace=workspace,
                 stream=stream)
-    if case.kind == "bf16":
+    if S:
+        o = fused_moe_shared(case.kind, case.x, case.x_scale, case.w1, case.w1_scale, case.w2,
+                             case.w2_scale, S, *align, case.topk_weights, **args)
+    elif case.kind == "bf16":
         o = fused_moe_bf16(case.x, case.w1, case.w2, *align, case.topk_weights, **args)
     elif case.kind == "fp8_blockwise":
         o = fused_moe_fp8_blockwise(case.x, case.x_scale, case.w1, case.w1_scale, case.w2,

@@ -131,8 +131,13 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
             const void* w2, const void* w2s, const int32_t* sorted, const int32_t* expert_ids,
             const int32_t* ntp, const float* topk_w, void* out, int64_t T, int64_t K, int64_t N,
             int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* ws, size_t ws_bytes,
-            void* stream) {
-  int rc = check_ffn(dtype, T, K, N, E, top_k, block_m);
+            void* stream, int32_t n_shared = 0) {
+  // E routed experts, then n_shared shared ones in the weights; every token
+  // adds one route per shared expert.  Capacities and workspace follow the
+  // totals.
+  if (n_shared < 0) return fail(MOE_ERR_SHAPE, "n_shared must be >= 0");
+  const int32_t E_all = E + n_shared, k_all = top_k + n_shared;
+  int rc = check_ffn(dtype, T, K, N, E_all, k_all, block_m);
   if (rc) return rc;
   if (split < -1 || split > 1) return fail(MOE_ERR_UNSUPPORTED, "split must be -1, 0 or 1");
   if (block_m == 256 && split == 0)
@@ -148,13 +153,13 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
   if (dtype == MOE_FP8_BLOCKWISE && (!aligned(xs, 4) || !aligned(w1s, 4) || !aligned(w2s, 4)))
     return fail(MOE_ERR_ALIGN, "fp32 scales must be 4-byte aligned");
   if (!aligned(ntp, 4)) return fail(MOE_ERR_ALIGN, "num_tokens_post_padded must be 4-byte aligned");
-  const int sp = split < 0 ? pick_split(dtype, T, K, N, E, top_k, block_m) : split;
-  const Layout L = layout(dtype, T, K, N, E, top_k, block_m, sp);
+  const int sp = split < 0 ? pick_split(dtype, T, K, N, E_all, k_all, block_m) : split;
+  const Layout L = layout(dtype, T, K, N, E_all, k_all, block_m, sp);
   if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
   if (ws_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
   int64_t rows, blocks;
-  capacity(T, top_k, E, block_m, &rows, &blocks);
+  capacity(T, k_all, E_all, block_m, &rows, &blocks);
   uint8_t* w = static_cast<uint8_t*>(ws);
   MoeArgs a{};
   a.x = static_cast<const uint8_t*>(x);
@@ -179,8 +184,9 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
   a.T = (int)T;
   a.K = (int)K;
   a.I = (int)(N / 2);
-  a.E = E;
+  a.E = E_all;
   a.top_k = top_k;
+  a.n_shared = n_shared;
   a.blocks_cap = (int)blocks;
   static_assert(MOE_BF16 == KIND_BF16 && MOE_FP8_BLOCKWISE == KIND_FP8B && MOE_MXFP8 == KIND_MX &&
                     MOE_MXFP4 == KIND_MX4,
@@ -228,6 +234,44 @@ int moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int3
                               static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int moe_align_shared(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
+                     int32_t n_shared, int32_t block_m, int32_t* sorted_token_ids,
+                     int32_t* expert_ids, int32_t* num_tokens_post_padded, void* stream) {
+  if (n_shared < 0) return fail(MOE_ERR_SHAPE, "n_shared must be >= 0");
+  int64_t rows, blocks;
+  int rc = moe_align_capacity(T, top_k + n_shared, E + n_shared, block_m, &rows, &blocks);
+  if (rc) return rc;
+  if (E + n_shared > 1024)
+    return fail(MOE_ERR_UNSUPPORTED, "the planner supports E + n_shared <= 1024 (got %d)",
+                E + n_shared);
+  if (!num_tokens_post_padded || (rows > 0 && (!sorted_token_ids || !expert_ids)) ||
+      (T > 0 && !topk_ids))
+    return fail(MOE_ERR_NULL, "a required pointer is NULL");
+  const void* ps[] = {topk_ids, sorted_token_ids, expert_ids};
+  for (const void* p : ps)
+    if (p && !aligned(p, 16)) return fail(MOE_ERR_ALIGN, "tensors must be 16-byte aligned");
+  if (!aligned(num_tokens_post_padded, 4))
+    return fail(MOE_ERR_ALIGN, "num_tokens_post_padded must be 4-byte aligned");
+  hipError_t e = launch_align(topk_ids, (int)(T * top_k), E, block_m, sorted_token_ids,
+                              expert_ids, num_tokens_post_padded, (int)rows, (int)blocks,
+                              static_cast<hipStream_t>(stream), (int)T, n_shared);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int fused_moe_shared(int32_t dtype, const void* x, const void* x_scale, const void* w1,
+                     const void* w1_scale, const void* w2, const void* w2_scale,
+                     int32_t n_shared, const int32_t* sorted_token_ids,
+                     const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
+                     const float* topk_weights, void* out, int64_t T, int64_t K, int64_t N,
+                     int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (dtype < MOE_BF16 || dtype > MOE_MXFP4) return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  return run_ffn(dtype, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
+                 num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m, split,
+                 workspace, workspace_bytes, stream, n_shared);
 }
 
 int moe_route_align_workspace_size(size_t* bytes) {

@@ -31,11 +31,24 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBatch = 8;
 
 // The planner on one workgroup of kWaves waves; smem holds
-// kWaves * E + 2 * E + kWaves + 1 ints.
-__device__ __forceinline__ void align_body(const int32_t* __restrict__ ids, int R, int E, int bm,
-                           int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
-                           int32_t* __restrict__ ntp_out, int sorted_cap, int blocks_cap,
-                           int* smem) {
+// kWaves * ET + 2 * ET + kWaves + 1 ints, ET = E + S.
+// Routes: ids[0 .. R) name routed experts (valid in [0, E)); with S shared
+// experts, route R + t * S + s (t < T) goes to expert E + s.
+__device__ __forceinline__ void align_body(const int32_t* __restrict__ ids, int R, int E_routed,
+                                           int bm, int32_t* __restrict__ sorted,
+                                           int32_t* __restrict__ expert_ids,
+                                           int32_t* __restrict__ ntp_out, int sorted_cap,
+                                           int blocks_cap, int* smem, int T, int S) {
+  const int E = E_routed + S;  // every expert, shared ones last
+  const int R_routed = R;
+  auto expert_of = [=](int i) -> int {
+    if (i < R_routed) {
+      const int e = ids[i];
+      return (unsigned)e < (unsigned)E_routed ? e : -1;
+    }
+    return E_routed + (i - R_routed) % S;
+  };
+  R = R_routed + T * S;        // every route, shared ones last
   int* cnt = smem;                     // [kWaves][E]: counts, then cursors
   int* off = smem + kWaves * E;        // [E]: segment start
   int* tot = off + E;                  // [E]: route count
@@ -54,7 +67,7 @@ __device__ __forceinline__ void align_body(const int32_t* __restrict__ ids, int 
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = base + u * 64 + lane;
-      eb[u] = i < hi ? ids[i] : -1;
+      eb[u] = i < hi ? expert_of(i) : -1;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
@@ -118,7 +131,7 @@ __device__ __forceinline__ void align_body(const int32_t* __restrict__ ids, int 
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = base0 + u * 64 + lane;
-      eb[u] = i < hi ? ids[i] : -1;
+      eb[u] = i < hi ? expert_of(i) : -1;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
@@ -146,9 +159,9 @@ __device__ __forceinline__ void align_body(const int32_t* __restrict__ ids, int 
 __global__ void __launch_bounds__(kThreads)
 k_align(const int32_t* __restrict__ ids, int R, int E, int bm, int32_t* __restrict__ sorted,
         int32_t* __restrict__ expert_ids, int32_t* __restrict__ ntp_out, int sorted_cap,
-        int blocks_cap) {
+        int blocks_cap, int T, int S) {
   extern __shared__ int smem[];
-  align_body(ids, R, E, bm, sorted, expert_ids, ntp_out, sorted_cap, blocks_cap, smem);
+  align_body(ids, R, E, bm, sorted, expert_ids, ntp_out, sorted_cap, blocks_cap, smem, T, S);
 }
 
 // ---------------------------------------------------------------------------
@@ -308,7 +321,7 @@ k_route_align(const float* __restrict__ logits, int T, int E, int top_k, int bm,
     if (threadIdx.x == 0) atomicExch(ticket, 0);
   }
   align_body(topk_ids, T * top_k, E, bm, sorted, expert_ids, ntp_out, sorted_cap, blocks_cap,
-             smem);
+             smem, T, 0);
 }
 
 }  // namespace
@@ -338,9 +351,10 @@ hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int 
 
 hipError_t launch_align(const int32_t* topk_ids, int R, int E, int block_m, int32_t* sorted,
                         int32_t* expert_ids, int32_t* ntp, int sorted_cap, int blocks_cap,
-                        hipStream_t stream) {
-  const size_t smem = (size_t)(kWaves * E + 2 * E + kWaves + 1) * sizeof(int);
+                        hipStream_t stream, int T, int n_shared) {
+  const int ET = E + n_shared;
+  const size_t smem = (size_t)(kWaves * ET + 2 * ET + kWaves + 1) * sizeof(int);
   hipLaunchKernelGGL(k_align, dim3(1), dim3(kThreads), smem, stream, topk_ids, R, E, block_m,
-                     sorted, expert_ids, ntp, sorted_cap, blocks_cap);
+                     sorted, expert_ids, ntp, sorted_cap, blocks_cap, T, n_shared);
   return hipGetLastError();
 }

@@ -24,12 +24,29 @@ struct MoeArgs {
   int32_t* flags;  // split: (T*top_k) route placed flags
   float* acc;      // fused: (T, K) fp32 accumulator
   int T, K, I, E, top_k;
+  int n_shared;    // shared experts: the last n_shared of the E experts
   int blocks_cap;  // planner block capacity (grid bound)
 };
 
+// Route ids: t * top_k + j for the routed experts (weight topk_w[id]), then
+// T * top_k + t * n_shared + s for the shared ones (weight 1).
+inline size_t total_routes(const MoeArgs& a) { return (size_t)a.T * (a.top_k + a.n_shared); }
+
+__device__ __forceinline__ int route_token(const MoeArgs& p, int id) {
+  const int R = p.T * p.top_k;
+  return id < 0 ? 0 : id < R ? id / p.top_k : (id - R) / p.n_shared;  // padding rows: token 0
+}
+
+__device__ __forceinline__ float route_weight(const MoeArgs& p, int id) {
+  return id < p.T * p.top_k ? p.topk_w[id] : 1.f;
+}
+
+// Planner; n_shared > 0 appends one route per (token, shared expert), the
+// shared experts numbered E .. E + n_shared - 1 (T tokens: R = T * top_k).
 hipError_t launch_align(const int32_t* topk_ids, int R, int E, int block_m,
                         int32_t* sorted, int32_t* expert_ids, int32_t* ntp,
-                        int sorted_cap, int blocks_cap, hipStream_t stream);
+                        int sorted_cap, int blocks_cap, hipStream_t stream, int T = 0,
+                        int n_shared = 0);
 
 // Router (softmax, top-k, renormalized weights) and planner in one launch;
 // `ticket` is one int of workspace, zero before the call and after it.

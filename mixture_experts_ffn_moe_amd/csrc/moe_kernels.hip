@@ -364,9 +364,6 @@ struct BlockShape {
   static constexpr int RED = KSPLIT > 1 ? (KSPLIT - 1) * WG * MI * 4 * 4 * 64 : 1;
 };
 
-__device__ __forceinline__ int token_of(int id, int top_k) {
-  return id >= 0 ? id / top_k : 0;  // padding rows read token 0 and are discarded
-}
 
 // Gate/up GEMM + SwiGLU for one (block, slice) tile: h[mi][j] holds the
 // lane's C elements of gate/up column pair j (columns 32*wn + 16*j + l%16 of
@@ -401,13 +398,13 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const in
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
     const int row = wm * 64 + mi * 16 + r16;
-    const int tok = token_of(ids[row], p.top_k);
+    const int tok = route_token(p, ids[row]);
     op.a[mi] = (uint32_t)tok * K * ES + 16 * g;
     if constexpr (KIND == KIND_FP8B) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int crow = wm * 64 + mi * 16 + 4 * g + i;
-        op.as[mi][i] = (uint32_t)token_of(ids[crow], p.top_k) * KS * 4;
+        op.as[mi][i] = (uint32_t)route_token(p, ids[crow]) * KS * 4;
       }
     }
     if constexpr (is_mx(KIND)) op.ax[mi] = (uint32_t)tok * (K / 32);
@@ -431,7 +428,7 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const in
     if (up_stage_bytes(K, MI, KSPLIT, W) > 0) {
       const Stage st = make_stage(k_hi - k_lo, MI, W, wid);
       const uint32_t rs = (uint32_t)(K / 32);
-      auto a_row = [&](int ri) { return (uint32_t)token_of(ids[wm * 64 + ri], p.top_k) * rs; };
+      auto a_row = [&](int ri) { return (uint32_t)route_token(p, ids[wm * 64 + ri]) * rs; };
       auto b_row = [&](int ri) {
         const int ni = ri >> 4;
         return (uint32_t)((ni < 2 ? 0 : I) + s * kSlice + 32 * wn + 16 * (ni & 1) + (ri & 15)) * rs;
@@ -687,7 +684,8 @@ k_down(MoeArgs p) {
     }
 }
 
-// out[t, c:c+4] = bf16(sum_j w[t,j] * y[t*top_k+j, c:c+4]), j ascending.
+// out[t, c:c+4] = bf16(sum_j w[t,j] * y[t*top_k+j, c:c+4] + sum_s y[shared s of t]),
+// j then s ascending.
 __global__ void __launch_bounds__(256) k_combine(MoeArgs p) {
   const int K = p.K;
   const int CT = (K + 1023) / 1024;
@@ -704,6 +702,16 @@ __global__ void __launch_bounds__(256) k_combine(MoeArgs p) {
     s.y += w * y.y;
     s.z += w * y.z;
     s.w += w * y.w;
+  }
+  // shared experts: every token, weight 1, after its routed experts
+  for (int j = 0; j < p.n_shared; ++j) {
+    const size_t id = (size_t)p.T * p.top_k + (size_t)t * p.n_shared + j;
+    if (!p.flags[id]) continue;
+    const float4 y = *reinterpret_cast<const float4*>(p.yr + id * K + c);
+    s.x += y.x;
+    s.y += y.y;
+    s.z += y.z;
+    s.w += y.w;
   }
   uint2 o;
   o.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
@@ -788,8 +796,8 @@ k_fused(MoeArgs p) {
     for (int i = 0; i < 4; ++i) {
       const int crow = wm * 64 + mi * 16 + 4 * g + i;
       const int id = ids[crow];
-      ctok[mi][i] = id >= 0 ? id / p.top_k : -1;
-      cw[mi][i] = id >= 0 ? p.topk_w[id] : 0.f;
+      ctok[mi][i] = id >= 0 ? route_token(p, id) : -1;
+      cw[mi][i] = id >= 0 ? route_weight(p, id) : 0.f;
       if constexpr (KIND == KIND_FP8B) rsf[mi][i] = lds_sf[crow];
     }
   }
@@ -820,10 +828,11 @@ k_fused(MoeArgs p) {
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) {
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (is_mx(KIND))
+        if constexpr (is_mx(KIND)) {
           y = mfma_step_scaled<KIND>(fa[mi], fb[ni], y, xa[mi], xb[ni]);
-        else
+              } else {
           y = mfma_step<KIND>(fa[mi], fb[ni], y);
+        }
         const int c = c0 + 16 * ni + r16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -902,7 +911,7 @@ int pick_ksplit(const MoeArgs& a) {
   if constexpr (BM > 32) {
     return 1;
   } else {
-    const size_t R = (size_t)a.T * a.top_k;
+    const size_t R = total_routes(a);
     const size_t tiles = (R < (size_t)a.E ? R : (size_t)a.E) * (size_t)(a.I / kSlice);
     if (a.K / 128 < 8) return 1;  // too few K steps to share out
     return tiles <= 256 ? 2 : 1;
@@ -922,7 +931,7 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
   constexpr int THREADS = BlockShape<BM>::THREADS;
   constexpr int D = prefetch_depth<KIND, BM>();
   const int S = a.I / kSlice;
-  const size_t R = (size_t)a.T * a.top_k;
+  const size_t R = total_routes(a);
   if (split) {
     const size_t fbytes = (R * 4 + 15) / 16;
     hipLaunchKernelGGL(k_zero, dim3(grid_for(fbytes, 256)), dim3(256), 0, st,
@@ -963,7 +972,7 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
 template <int KIND>
 hipError_t launch_tiled_only(const MoeArgs& a, hipStream_t st, const TimingHook& hk) {
   if (!tiled_supported(KIND, 256, a.K, a.I)) return hipErrorInvalidValue;
-  const size_t R = (size_t)a.T * a.top_k;
+  const size_t R = total_routes(a);
   const size_t fbytes = (R * 4 + 15) / 16;
   hipLaunchKernelGGL(k_zero, dim3(grid_for(fbytes, 256)), dim3(256), 0, st,
                      reinterpret_cast<uint4*>(a.flags), fbytes);

@@ -295,7 +295,6 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, int
   __syncthreads();  // the caller reuses the LDS
 }
 
-__device__ __forceinline__ int token_of(int id, int top_k) { return id >= 0 ? id / top_k : 0; }
 
 // gate/up GEMM + SwiGLU + requantization, one (block, 128-wide slice) tile
 template <int KIND, int BM, int NS>
@@ -326,7 +325,7 @@ __global__ void __launch_bounds__(BM == 256 ? 512 : 256) __attribute__((amdgpu_w
   for (int t = 0; t < C::A_INSTR; ++t) {
     int row, q;
     dma_rows<C::NW>(t, row, q);
-    a_off[t] = (uint32_t)token_of(ids[row], p.top_k) * K + q * 16;
+    a_off[t] = (uint32_t)route_token(p, ids[row]) * K + q * 16;
   }
 #pragma unroll
   for (int t = 0; t < C::B_INSTR; ++t) {
@@ -339,12 +338,12 @@ __global__ void __launch_bounds__(BM == 256 ? 512 : 256) __attribute__((amdgpu_w
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
   if constexpr (KIND == KIND_FP8B) {
     src.rsa = make_desc(p.xs, (uint32_t)((size_t)p.T * KS * 4));
-    sa_off = (uint32_t)token_of(ids[srow < BM ? srow : 0], p.top_k) * KS * 4;
+    sa_off = (uint32_t)route_token(p, ids[srow < BM ? srow : 0]) * KS * 4;
     src.bsc = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + s) * KS;
     src.bsc2 = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + S + s) * KS;
   } else {
     src.rsa = make_desc(p.xs, (uint32_t)((size_t)p.T * (K / 32)));
-    sa_off = (uint32_t)token_of(ids[srow < BM ? srow : 0], p.top_k) * (K / 32);
+    sa_off = (uint32_t)route_token(p, ids[srow < BM ? srow : 0]) * (K / 32);
     src.rsb = make_desc(reinterpret_cast<const uint8_t*>(p.w1s) + (size_t)e * N * (K / 32),
                         (uint32_t)((size_t)N * (K / 32)));
     const int brow = min(wid * C::SB_ROWS + lane, 255);  // B scale row this lane stages
