@@ -297,10 +297,11 @@ __device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_firs
   for (int d = 0; d < D; ++d)
     ring_load<KIND, MI, NI, D, STAGED>(r, d, k_first + rel(d < ksteps ? d : d % ksteps), op);
   if constexpr (STAGED) {
-    // Direct-to-LDS loads need not complete in order with the register loads
-    // issued after them, so the region is complete only at vmcnt(0): waited
-    // once, after the first D steps of operand loads are in flight (the empty
-    // asm keeps them above the wait).
+    // Wait for the copy once, after the first D steps of operand loads are
+    // in flight (the empty asm keeps them above the wait).  Vector loads
+    // complete in order, so a wait for "at most the loads issued after the
+    // copy" would do as well; the full wait measured no slower and does not
+    // depend on that count.
     asm volatile("" ::: "memory");
     wait_vmcnt<0>();
     asm volatile("" ::: "memory");
