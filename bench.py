@@ -13,7 +13,8 @@ is the largest one's throughput and ``sweep`` lists all of them.
 Throughput: algorithmic FLOPs 6 * R * K * I per step (R = routes to local
 experts; padding rows do not count) over the step time.  Roofline: the
 dominant kernel (the fused kernel in fused mode, the gate/up kernel in split
-mode) is timed with HIP events recorded around it on its own stream, and its
+mode, the persistent kernel in ring mode, ``--split 2``) is timed with HIP
+events recorded around it on its own stream, and its
 algorithmic HBM bytes (weights and scales of the experts it reads once, the
 token rows, its outputs) are divided by that time.
 
@@ -21,7 +22,7 @@ Per token count the sweep also holds per-call distributions (median, p10,
 p90 of event pairs around each call): the whole call and the forward alone
 (planner outputs reused), back to back ("warm"), and the whole call with a
 1 GiB read before each call outside its events ("cold": L2 and the 256 MB
-MALL hold other, clean lines).  The line records the GPU clocks rocm-smi reports and two
+MALL hold other, clean lines).  The line records the GPU clocks (from sysfs) and two
 measured reference ceilings beside the spec peaks: a plain device copy, a
 read-only sum, and a large e4m3 GEMM through the vendor BLAS.
 
@@ -106,8 +107,11 @@ def byte_model(kind, K, I, E_act, T, R, split):
     out_b = T * K * 2
     route_b = R * 8
     step = E_act * (w1e + w2e) + x_b + out_b + route_b
-    if split:
-        hs = 0 if kind == "bf16" else (R * (I // 128) * 4 if kind == "fp8_blockwise" else R * (I // 32))
+    hs = 0 if kind == "bf16" else (R * (I // 128) * 4 if kind == "fp8_blockwise" else R * (I // 32))
+    if split == 2:
+        # persistent ring kernel: both GEMMs, H written and read back, fp32 route rows
+        dom = E_act * (w1e + w2e) + x_b + 2 * (R * I * es + hs) + R * K * 4
+    elif split:
         dom = E_act * w1e + x_b + R * I * es + hs          # gate/up kernel: w1, x, H write
     else:
         dom = E_act * (w1e + w2e) + x_b + 2 * T * K * 4    # fused: weights, x, fp32 acc r/w
@@ -412,7 +416,7 @@ def main():
     ap.add_argument("--calls", type=int, default=200,
                     help="per-call timed calls (warm) for the median / p10 / p90")
     ap.add_argument("--cold-calls", type=int, default=50,
-                    help="per-call timed calls with a 1 GiB write before each (cold caches)")
+                    help="per-call timed calls with a 1 GiB read before each (cold caches)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (counter calibration)")
     ap.add_argument("--summarize-counters", default=None, metavar="DIR",
@@ -505,10 +509,11 @@ def main():
         hev.close()
         flops = 6.0 * R * K * I
         step_bytes, dom_bytes = byte_model(kind, K, I, E_act, T, R, split)
-        kname = "k_up" if split else "k_fused"
+        kname = {0: "k_fused", 1: "k_up", 2: "k_ring"}[split]
+        mode = {0: "fused", 1: "split", 2: "ring"}[split]
         sweep.append({
             "T": T, "routes": R, "active_experts": E_act, "block_m": bm,
-            "mode": "split" if split else "fused",
+            "mode": mode,
             "us_per_step": ms * 1e3, "tflops": flops / (ms * 1e-3) / 1e12,
             "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[kind],
             "step_gbs": step_bytes / (ms * 1e-3) / 1e9,
@@ -516,7 +521,7 @@ def main():
             "dominant_kernel": kname, "dominant_us": kms * 1e3,
             "dominant_bytes": dom_bytes, "dominant_gbs": dom_bytes / (kms * 1e-3) / 1e9,
         })
-        print(f"[bench] T={T} bm={bm} {'split' if split else 'fused'}: {ms*1e3:.1f} us/step, "
+        print(f"[bench] T={T} bm={bm} {mode}: {ms*1e3:.1f} us/step, "
               f"{kname} {kms*1e3:.1f} us = {dom_bytes/(kms*1e-3)/1e9:.0f} GB/s",
               file=sys.stderr, flush=True)
         # per-call distributions: the whole call (planner + forward) and the

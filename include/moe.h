@@ -163,12 +163,49 @@ int moe_select_block_m(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32
 
 /*
  * Workspace bytes a fused_moe_* call with these sizes needs (host out-param).
- * split = -1 means "as moe_select_split picks".  Errors: as the fused calls'
- * size checks.
+ * split = -1 means "as moe_select_split picks"; for split = 2 (ring mode)
+ * the size with the default ring (see moe_ring_layout).  Errors: as the
+ * fused calls' size checks.
  */
 int moe_workspace_size(int32_t dtype, int64_t T, int64_t K, int64_t N,
                        int32_t E, int32_t top_k, int32_t block_m,
                        int32_t split, size_t* bytes);
+
+/*
+ * Ring-mode workspace ([DeepGEMM #88] "How it works": the intermediate pool
+ * becomes a ring of block slots; "What the bound moves": the ring capacity
+ * is the buffer's).  A split = 2 call takes
+ *   slots = min(blocks_cap, (workspace_bytes - *fixed_bytes) / *slot_bytes)
+ * ring slots of block_m intermediate rows (at least one is required); with
+ * one slot per planner block the ring never wraps.  Host out-params:
+ *   *fixed_bytes    bytes ahead of the ring (control words, flags, per-route
+ *                   rows)
+ *   *slot_bytes     bytes per slot (block_m rows of values and scales)
+ *   *default_slots  the slots moe_workspace_size(.., split = 2, ..) provides:
+ *                   twice the lag that the largest resident grid can ask
+ *                   for, plus two, capped at blocks_cap
+ * block_m must be 16 or 32.  Errors: MOE_ERR_NULL, and as moe_workspace_size.
+ */
+int moe_ring_layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E,
+                    int32_t top_k, int32_t block_m, size_t* fixed_bytes,
+                    size_t* slot_bytes, int64_t* default_slots);
+
+/*
+ * The ring mode's task stream, for inspection (host only, no device work;
+ * [DeepGEMM #88] "How it works": a block's down tasks sit lag units after
+ * its up tasks).  For n_blocks planner blocks with up_per_block = I/128
+ * gate/up tasks and down_per_block = ceil(K/256) down tasks each, ticket t
+ * (t = first .. first + count - 1) is described by kind[j] (1 up, 2 down,
+ * 0 past the end of the stream), block[j] and index[j] (the slice of I, or
+ * the 256-column tile of the output).  Rounds r = 0, 1, .. hold the up
+ * tasks of block r, then the down tasks of block r - lag; tickets
+ * 0 .. n_blocks * (up_per_block + down_per_block) - 1 cover every task once.
+ * A call's lag is below its ring's slot count.  kind, block, index: host
+ * arrays of count int32.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE.
+ */
+int moe_ring_schedule(int32_t n_blocks, int32_t up_per_block, int32_t down_per_block,
+                      int32_t lag, int64_t first, int64_t count, int32_t* kind,
+                      int32_t* block, int32_t* index);
 
 /*
  * Byte offsets, inside the workspace of a split-mode call, of the
@@ -211,7 +248,16 @@ int moe_workspace_layout(int32_t dtype, int64_t T, int64_t K, int64_t N,
  *                    1: split mode (the requantized intermediate is written
  *                    to the workspace once, the down GEMM runs with no
  *                    split-K, and the combine is deterministic: the same
- *                    inputs give bitwise the same output).
+ *                    inputs give bitwise the same output);
+ *                    2: ring mode, block_m 16 or 32 ([DeepGEMM #88] "How it
+ *                    works"): one persistent grid runs the split mode's
+ *                    gate/up and down tiles from a lag-ordered task stream,
+ *                    the intermediate in a ring of block slots sized by the
+ *                    workspace (moe_ring_layout); bitwise equal to split
+ *                    mode.  Its waits are bounded: the int at byte offset 4
+ *                    of the workspace is nonzero after a call in which one
+ *                    gave up (a broken invariant; the output is then
+ *                    invalid).
  *   workspace, workspace_bytes
  *                    device scratch of at least moe_workspace_size bytes;
  *                    contents undefined on return; concurrent calls need

@@ -16,7 +16,8 @@ Entry points (same names as the C ABI):
   fused_moe_mxfp8(x, x_scale, w1, w1_scale, w2, w2_scale, ...)
   fused_moe_mxfp4(x, x_scale, w1, w1_scale, w2, w2_scale, ...)   (packed e2m1 weights)
 plus the host helpers moe_align_capacity, moe_workspace_size,
-moe_workspace_layout, moe_select_split and moe_select_block_m.
+moe_workspace_layout, moe_ring_layout, moe_select_split and moe_select_block_m.
+``split=2`` runs the persistent ring mode (block_m 16 or 32).
 """
 
 import ctypes
@@ -27,7 +28,8 @@ import torch
 __all__ = [
     "MoeError", "lib", "LIB_PATH", "MOE_BF16", "MOE_FP8_BLOCKWISE", "MOE_MXFP8", "MOE_MXFP4",
     "moe_align_capacity", "moe_align", "moe_select_split", "moe_select_block_m",
-    "moe_workspace_size", "moe_workspace_layout", "fused_moe_bf16",
+    "moe_workspace_size", "moe_workspace_layout", "moe_ring_layout", "moe_ring_schedule",
+    "fused_moe_bf16",
     "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4", "EXPORTED_SYMBOLS",
     "moe_route_align", "moe_route_align_workspace_size", "moe_align_shared", "fused_moe_shared",
 ]
@@ -43,7 +45,7 @@ EXPORTED_SYMBOLS = (
     "moe_select_block_m", "moe_workspace_size", "moe_workspace_layout",
     "fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4",
     "moe_set_timing_events", "moe_route_align_workspace_size", "moe_route_align",
-    "moe_align_shared", "fused_moe_shared",
+    "moe_align_shared", "fused_moe_shared", "moe_ring_layout", "moe_ring_schedule",
 )
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
@@ -85,6 +87,9 @@ def lib():
                                      ctypes.POINTER(_SZ)]
     L.moe_workspace_layout.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32,
                                        ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
+    L.moe_ring_schedule.argtypes = [_I32, _I32, _I32, _I32, _I64, _I64, _P, _P, _P]
+    L.moe_ring_layout.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32, ctypes.POINTER(_SZ),
+                                  ctypes.POINTER(_SZ), ctypes.POINTER(_I64)]
     tail = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]
     L.fused_moe_bf16.argtypes = [_P, _P, _P] + tail
     L.fused_moe_fp8_blockwise.argtypes = [_P, _P, _P, _P, _P, _P] + tail
@@ -261,6 +266,29 @@ def moe_workspace_layout(dtype, T, K, N, num_experts, top_k, block_m):
     _check(lib().moe_workspace_layout(_DTYPE_CODE.get(dtype, dtype), T, K, N, num_experts,
                                       top_k, block_m, ctypes.byref(h), ctypes.byref(hs)))
     return h.value, hs.value
+
+
+def moe_ring_layout(dtype, T, K, N, num_experts, top_k, block_m):
+    """Ring-mode workspace: (bytes ahead of the ring, bytes per slot,
+    default slots).  A split=2 call uses as many slots as its workspace
+    holds, at most one per planner block."""
+    fixed, slot, slots = _SZ(), _SZ(), _I64()
+    _check(lib().moe_ring_layout(_DTYPE_CODE.get(dtype, dtype), T, K, N, num_experts, top_k,
+                                 block_m, ctypes.byref(fixed), ctypes.byref(slot),
+                                 ctypes.byref(slots)))
+    return fixed.value, slot.value, slots.value
+
+
+def moe_ring_schedule(n_blocks, up_per_block, down_per_block, lag, first=0, count=None):
+    """Tickets first .. first+count-1 of the ring stream as three int32 numpy
+    arrays (kind: 1 up, 2 down, 0 past the end; block; index)."""
+    import numpy as np
+    if count is None:
+        count = n_blocks * (up_per_block + down_per_block) - first
+    kind, block, index = (np.zeros(max(count, 0), np.int32) for _ in range(3))
+    _check(lib().moe_ring_schedule(n_blocks, up_per_block, down_per_block, lag, first, count,
+                                   kind.ctypes.data, block.ctypes.data, index.ctypes.data))
+    return kind, block, index
 
 
 def _run(fn, dtype, operands, w1, sorted_token_ids, expert_ids, num_tokens_post_padded,

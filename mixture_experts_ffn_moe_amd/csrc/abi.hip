@@ -95,8 +95,16 @@ int pick_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_
 }
 
 struct Layout {
-  size_t flags, hq, hs, yr, acc, total;
+  size_t ctl, flags, hq, hs, yr, acc, total;
+  size_t ring_fixed, slot_bytes;  // ring mode: bytes before the ring, bytes per slot
+  int64_t slots;                  // ring mode: slots of the default size
 };
+
+// Scale bytes per intermediate row.
+size_t h_scale_bytes(int32_t dtype, int64_t I) {
+  return dtype == MOE_FP8_BLOCKWISE ? (size_t)(I / 128) * 4
+         : (dtype == MOE_MXFP8 || dtype == MOE_MXFP4) ? (size_t)(I / 32) : 0;
+}
 
 Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
               int32_t block_m, int split) {
@@ -108,6 +116,24 @@ Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
   capacity(T, top_k, E, block_m, &rows, &blocks);
   rows = blocks * block_m;  // whole blocks, so every block's rows exist
   size_t off = 0;
+  if (split == 2) {
+    // control words and flags first (one clear), then the per-route rows,
+    // then the ring: slots of block_m rows, values then scales
+    L.ctl = off;
+    off += ring_ctl_bytes(blocks);
+    L.flags = off;
+    off = round_up(off + R * 4, 256);
+    L.yr = off;
+    off = round_up(off + R * (size_t)K * 4, 256);
+    L.ring_fixed = off;
+    L.slot_bytes = (size_t)block_m * ((size_t)I * es + h_scale_bytes(dtype, I));
+    L.slots = ring_default_slots(blocks, (int)(I / 128));
+    L.hq = off;
+    L.hs = dtype == MOE_BF16 ? L.hq : L.hq + (size_t)L.slots * block_m * I * es;
+    off += (size_t)L.slots * L.slot_bytes;
+    L.total = round_up(off, 256);
+    return L;
+  }
   if (split) {
     L.flags = off;
     off = round_up(off + R * 4, 256);
@@ -139,9 +165,11 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
   const int32_t E_all = E + n_shared, k_all = top_k + n_shared;
   int rc = check_ffn(dtype, T, K, N, E_all, k_all, block_m);
   if (rc) return rc;
-  if (split < -1 || split > 1) return fail(MOE_ERR_UNSUPPORTED, "split must be -1, 0 or 1");
+  if (split < -1 || split > 2) return fail(MOE_ERR_UNSUPPORTED, "split must be -1, 0, 1 or 2");
   if (block_m == 256 && split == 0)
     return fail(MOE_ERR_UNSUPPORTED, "block_m 256 runs the split mode only");
+  if (split == 2 && block_m > 32)
+    return fail(MOE_ERR_UNSUPPORTED, "the ring mode runs block_m 16 or 32 (got %d)", block_m);
   if (T == 0) return ok();
   if (!x || !w1 || !w2 || !sorted || !expert_ids || !ntp || !topk_w || !out)
     return fail(MOE_ERR_NULL, "a required pointer is NULL");
@@ -154,12 +182,26 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
     return fail(MOE_ERR_ALIGN, "fp32 scales must be 4-byte aligned");
   if (!aligned(ntp, 4)) return fail(MOE_ERR_ALIGN, "num_tokens_post_padded must be 4-byte aligned");
   const int sp = split < 0 ? pick_split(dtype, T, K, N, E_all, k_all, block_m) : split;
-  const Layout L = layout(dtype, T, K, N, E_all, k_all, block_m, sp);
-  if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
-  if (ws_bytes < L.total)
-    return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  Layout L = layout(dtype, T, K, N, E_all, k_all, block_m, sp);
   int64_t rows, blocks;
   capacity(T, k_all, E_all, block_m, &rows, &blocks);
+  if (sp == 2) {
+    // the ring takes as many slots as the workspace holds (at least one, at
+    // most one per block: then it never wraps)
+    const size_t min_bytes = L.ring_fixed + L.slot_bytes;
+    if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+    if (ws_bytes < min_bytes)
+      return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes (one ring slot)",
+                  ws_bytes, min_bytes);
+    int64_t slots = (int64_t)((ws_bytes - L.ring_fixed) / L.slot_bytes);
+    if (slots > blocks) slots = blocks;
+    L.slots = slots;
+    if (dtype != MOE_BF16) L.hs = L.hq + (size_t)slots * block_m * (N / 2);  // e4m3 values
+  } else {
+    if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+    if (ws_bytes < L.total)
+      return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  }
   uint8_t* w = static_cast<uint8_t*>(ws);
   MoeArgs a{};
   a.x = static_cast<const uint8_t*>(x);
@@ -178,6 +220,12 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
     a.hq = w + L.hq;
     a.hs = w + L.hs;
     a.yr = reinterpret_cast<float*>(w + L.yr);
+    a.h_rows = (int)(blocks * block_m);
+    if (sp == 2) {
+      a.ctl = reinterpret_cast<int*>(w + L.ctl);
+      a.ring = (int)L.slots;
+      a.h_rows = (int)(L.slots * block_m);
+    }
   } else {
     a.acc = reinterpret_cast<float*>(w + L.acc);
   }
@@ -347,9 +395,46 @@ int moe_workspace_size(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E
   if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
   int rc = check_ffn(dtype, T, K, N, E, top_k, block_m);
   if (rc) return rc;
-  if (split < -1 || split > 1) return fail(MOE_ERR_UNSUPPORTED, "split must be -1, 0 or 1");
+  if (split < -1 || split > 2) return fail(MOE_ERR_UNSUPPORTED, "split must be -1, 0, 1 or 2");
+  if (split == 2 && block_m > 32)
+    return fail(MOE_ERR_UNSUPPORTED, "the ring mode runs block_m 16 or 32 (got %d)", block_m);
   const int sp = split < 0 ? pick_split(dtype, T, K, N, E, top_k, block_m) : split;
   *bytes = layout(dtype, T, K, N, E, top_k, block_m, sp).total;
+  return ok();
+}
+
+int moe_ring_layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+                    int32_t block_m, size_t* fixed_bytes, size_t* slot_bytes,
+                    int64_t* default_slots) {
+  if (!fixed_bytes || !slot_bytes || !default_slots)
+    return fail(MOE_ERR_NULL, "output pointers are NULL");
+  int rc = check_ffn(dtype, T, K, N, E, top_k, block_m);
+  if (rc) return rc;
+  if (block_m > 32)
+    return fail(MOE_ERR_UNSUPPORTED, "the ring mode runs block_m 16 or 32 (got %d)", block_m);
+  const Layout L = layout(dtype, T, K, N, E, top_k, block_m, 2);
+  *fixed_bytes = L.ring_fixed;
+  *slot_bytes = L.slot_bytes;
+  *default_slots = L.slots;
+  return ok();
+}
+
+int moe_ring_schedule(int32_t n_blocks, int32_t up_per_block, int32_t down_per_block,
+                      int32_t lag, int64_t first, int64_t count, int32_t* kind, int32_t* block,
+                      int32_t* index) {
+  if (count > 0 && (!kind || !block || !index)) return fail(MOE_ERR_NULL, "output pointers are NULL");
+  if (n_blocks < 0 || up_per_block < 1 || down_per_block < 1 || lag < 0 || first < 0 || count < 0)
+    return fail(MOE_ERR_SHAPE, "sizes must be non-negative (tasks per block positive)");
+  const int64_t total = (int64_t)n_blocks * (up_per_block + down_per_block);
+  if (total >= (int64_t(1) << 31)) return fail(MOE_ERR_SHAPE, "the stream must hold < 2^31 tasks");
+  for (int64_t j = 0; j < count; ++j) {
+    const int64_t t = first + j;
+    const RingTask k = t < total ? ring_task((int)t, n_blocks, up_per_block, down_per_block, lag)
+                                 : RingTask{0, 0, 0};
+    kind[j] = k.kind;
+    block[j] = k.b;
+    index[j] = k.i;
+  }
   return ok();
 }
 

@@ -68,12 +68,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// Cache policy of a buffer access: 0, or kDeviceScope (the sc1 bit), which
+// makes a load read, and a store write, at the point where all XCDs see the
+// same data (the per-CU and per-XCD caches are not coherent with each other).
+constexpr int kDeviceScope = 16;
+
+template <int CP = 0>
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, CP));
 }
 
+template <int CP = 0>
 __device__ __forceinline__ float buf_loadf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, CP));
 }
 
 __device__ __forceinline__ int buf_loadu8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
@@ -82,11 +89,11 @@ __device__ __forceinline__ int buf_loadu8(__amdgpu_buffer_rsrc_t r, uint32_t vof
 
 // Fragment of one row for one K step: `voff` is the row's byte offset plus
 // 16 * lane group, `soff` the step's byte offset (wave-uniform).
-template <int KIND>
+template <int KIND, int CP = 0>
 __device__ __forceinline__ void load_frag(Frag<KIND>& f, __amdgpu_buffer_rsrc_t r, uint32_t voff,
                                           uint32_t soff) {
 #pragma unroll
-  for (int c = 0; c < KindTraits<KIND>::NCHUNK; ++c) f.c[c] = buf_load16(r, voff + c * 64, soff);
+  for (int c = 0; c < KindTraits<KIND>::NCHUNK; ++c) f.c[c] = buf_load16<CP>(r, voff + c * 64, soff);
 }
 
 template <int KIND>
@@ -259,10 +266,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // The scalar operands pass through readfirstlane: the compiler may hold a
 // wave-uniform value in a vector register, which an "s" operand cannot take
 // (the read folds away for values already in scalar registers).
+template <int CP = 0>
 __device__ __forceinline__ void dma16(desc_t r, uint32_t m0, uint32_t voff, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r),
-                  "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
+  if constexpr (CP == kDeviceScope)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen sc1 lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r),
+                    "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :: "s"(__builtin_amdgcn_readfirstlane(m0)), "v"(voff), "s"(r),
+                    "s"(__builtin_amdgcn_readfirstlane(soff)) : "memory");
 }
 
 __device__ __forceinline__ void dma4(desc_t r, uint32_t m0, uint32_t voff, uint32_t soff) {

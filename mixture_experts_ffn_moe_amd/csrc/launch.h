@@ -26,7 +26,63 @@ struct MoeArgs {
   int T, K, I, E, top_k;
   int n_shared;    // shared experts: the last n_shared of the E experts
   int blocks_cap;  // planner block capacity (grid bound)
+  int h_rows;      // rows of the intermediate buffer (blocks_cap * block_m, or the ring's)
+  // persistent ring mode: control words in the workspace (ticket, error flag,
+  // then per block the finished up tiles and the finished down tiles), the
+  // lag of a block's down tiles behind its up tiles in the task stream, and
+  // the ring's size in blocks (block b's intermediate lives in slot b % ring)
+  int* ctl;
+  int lag, ring;
 };
+
+// Ring mode sizing ([DeepGEMM #88] "How it works": the lag follows from the
+// work in flight, the ring from the lag).  The whole grid takes a ticket at
+// once, and the stream opens with rounds of up tasks only (up_per_block
+// tickets each), so a block's down tasks find its up tasks finished only if
+// at least one grid's worth of tickets, with a margin, lies between them:
+// lag * up_per_block >= 1.5 x the resident workgroups (measured: with a
+// third less, half the grid polls at decode sizes).  A ring of twice the lag
+// (plus 2) likewise leaves the down tasks of a slot's previous block time
+// to finish before the slot is overwritten.  The default ring assumes a
+// grid of 2048 workgroups (8 per CU on 256 CUs, far above the one per CU
+// the launch uses), so the launch's own lag always fits it.
+constexpr int kRingMaxResident = 2048;
+inline int ring_lag(int resident, int up_per_block) {
+  return (3 * resident + 2 * up_per_block - 1) / (2 * up_per_block);
+}
+inline int64_t ring_default_slots(int64_t blocks_cap, int up_per_block) {
+  const int64_t r = 2 * (int64_t)ring_lag(kRingMaxResident, up_per_block) + 2;
+  return r < blocks_cap ? r : blocks_cap;
+}
+// One task of the ring stream.
+struct RingTask {
+  int kind;  // 0: none, 1: up (slice i of block b), 2: down (column tile i of block b)
+  int b, i;
+};
+
+// Ticket t -> task, for nb blocks of S up and NT down tasks each: rounds
+// r = 0, 1, .. hold the up tasks of block r (while r < nb), then the down
+// tasks of block r - lag (once r >= lag); empty parts take no tickets, so
+// tickets 0 .. nb * (S + NT) - 1 cover every task once.
+__host__ __device__ inline RingTask ring_task(int t, int nb, int S, int NT, int lag) {
+  const int h = lag < nb ? lag : nb;  // leading rounds with up tasks only
+  if (t < h * S) return {1, t / S, t % S};
+  t -= h * S;
+  const int per = S + NT, m = nb - h;  // rounds with both kinds
+  if (t < m * per) {
+    const int r = h + t / per, i = t % per;
+    return i < S ? RingTask{1, r, i} : RingTask{2, r - lag, i - S};
+  }
+  t -= m * per;
+  const int b0 = nb - h;  // trailing rounds: down tasks only
+  if (t < h * NT) return {2, b0 + t / NT, t % NT};
+  return {0, 0, 0};
+}
+
+// control words: ticket, error word, per block finished up and down tasks
+inline size_t ring_ctl_bytes(int64_t blocks_cap) {
+  return ((size_t)(2 + 2 * blocks_cap) * 4 + 255) / 256 * 256;
+}
 
 // Route ids: t * top_k + j for the routed experts (weight topk_w[id]), then
 // T * top_k + t * n_shared + s for the shared ones (weight 1).

@@ -110,17 +110,17 @@ struct Ring {
   int xb[NI][Q];
 };
 
-template <int Q>
+template <int Q, int CP = 0>
 __device__ __forceinline__ void load_run(uint32_t (&q)[Q], __amdgpu_buffer_rsrc_t r, uint32_t voff,
                                          uint32_t soff) {
   if constexpr (Q == 4) {
-    const uint4 v = buf_load16(r, voff, soff);
+    const uint4 v = buf_load16<CP>(r, voff, soff);
     q[0] = v.x, q[1] = v.y, q[2] = v.z, q[3] = v.w;
   } else if constexpr (Q == 2) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, CP);
     q[0] = v[0], q[1] = v[1];
   } else {
-    q[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+    q[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, CP);
   }
 }
 
@@ -145,12 +145,13 @@ __device__ __forceinline__ void stage_read(Ring<KIND, MI, NI, D>& r, int slot, i
   }
 }
 
-template <int KIND, int MI, int NI, int D, bool STAGED = false>
+// CPA: cache policy of the activation-side loads (values and scales).
+template <int KIND, int MI, int NI, int D, bool STAGED = false, int CPA = 0>
 __device__ __forceinline__ void ring_load(Ring<KIND, MI, NI, D>& r, int slot, int ks,
                                           const Operand<MI, NI>& op) {
   const uint32_t soff = (uint32_t)ks * KindTraits<KIND>::STEP_BYTES;
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) load_frag<KIND>(r.fa[slot][mi], op.ra, op.a[mi], soff);
+  for (int mi = 0; mi < MI; ++mi) load_frag<KIND, CPA>(r.fa[slot][mi], op.ra, op.a[mi], soff);
 #pragma unroll
   for (int ni = 0; ni < NI; ++ni)
     load_frag_b<KIND>(r.fb[slot][ni], op.rb, op.b[ni], (uint32_t)ks * BTraits<KIND>::STEP_BYTES);
@@ -158,7 +159,7 @@ __device__ __forceinline__ void ring_load(Ring<KIND, MI, NI, D>& r, int slot, in
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r.sa[slot][mi][i] = buf_loadf(op.rsa, op.as[mi][i], ks * 4);
+      for (int i = 0; i < 4; ++i) r.sa[slot][mi][i] = buf_loadf<CPA>(op.rsa, op.as[mi][i], ks * 4);
   }
   // a run starts at every Q-th slot (slot is a constant once the ring loop is
   // unrolled, so this is no branch)
@@ -166,7 +167,8 @@ __device__ __forceinline__ void ring_load(Ring<KIND, MI, NI, D>& r, int slot, in
   if constexpr (is_mx(KIND) && !STAGED) {
     if (slot % Q == 0) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi) load_run<Q>(r.qa[slot / Q][mi], op.rxa, op.ax[mi], ks * 4);
+      for (int mi = 0; mi < MI; ++mi)
+        load_run<Q, CPA>(r.qa[slot / Q][mi], op.rxa, op.ax[mi], ks * 4);
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) load_run<Q>(r.qb[slot / Q][ni], op.rxb, op.bx[ni], ks * 4);
     }
@@ -221,31 +223,30 @@ __device__ __forceinline__ void ring_compute(Ring<KIND, MI, NI, D>& r, int slot,
   }
 }
 
-// Start step of a wave's walk along K.  A dot product may visit its K steps
-// in any order, and waves that all start at step 0 read the same offset of
-// rows 4 KiB apart at the same time, which concentrates the traffic on a few
-// HBM channels (measured: 1.8 TB/s against 6.2 TB/s with staggered starts).
-// Each wave therefore starts at a step hashed from its workgroup and wave.
-__device__ __forceinline__ int stagger(int nsteps) {
-  const uint32_t gw = blockIdx.x * 8u + (threadIdx.x >> 6);
-  return (int)(((gw * 2654435761u) >> 16) % (uint32_t)nsteps);
-}
-
-// The same, uniform over the workgroup (for loops whose iterations the waves
-// of a workgroup share out among themselves).
-__device__ __forceinline__ int stagger_wg(int nsteps) {
-  return (int)(((blockIdx.x * 2654435761u) >> 16) % (uint32_t)nsteps);
+// Start step of a K walk.  A dot product may visit its K steps in any
+// order, and walks that all start at step 0 read the same offset of rows
+// 4 KiB apart at the same time, which concentrates the traffic on a few HBM
+// channels (measured: 1.8 TB/s against 6.2 TB/s with staggered starts).
+// Each tile therefore starts at a step hashed from its tile index (its grid
+// position in the split kernels, the same index in the persistent ring), so
+// a tile's summation order, hence its rounding, does not depend on which
+// workgroup runs it.
+__device__ __forceinline__ int stagger(uint32_t tile, int nsteps) {
+  return (int)(((tile * 2654435761u) >> 16) % (uint32_t)nsteps);
 }
 
 // acc[mi][ni] = sum over the 128-wide K steps [k_first, k_first + ksteps) of
 // A rows . B rows (with the dtype's scales), D steps of operands prefetched
-// into registers, visiting the steps from a staggered start.
+// into registers, visiting the steps from the tile's staggered start.
 // STAGED (MX, runs of 4): the scale runs come from the wave's LDS region,
 // filled here with the rows of a_row(i) / b_row(i) (byte offsets of the
-// i-th activation / weight row's scales in their buffers).
-template <int KIND, int MI, int NI, int D, bool STAGED = false, class AR = int, class BR = int>
+// i-th activation / weight row's scales in their buffers).  CPA: cache
+// policy of every activation-side load.
+template <int KIND, int MI, int NI, int D, bool STAGED = false, int CPA = 0, class AR = int,
+          class BR = int>
 __device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_first, int ksteps,
-                                           f32x4 (&acc)[MI][NI], const Stage* st = nullptr,
+                                           uint32_t tile, f32x4 (&acc)[MI][NI],
+                                           const Stage* st = nullptr,
                                            AR a_row = 0, BR b_row = 0) {
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
@@ -262,7 +263,7 @@ __device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_firs
   // MX scale runs are contiguous in K only if no run straddles the wrap, so
   // the rotation moves in whole runs (and stays 0 if runs do not tile the walk)
   constexpr int Q = is_mx(KIND) ? Ring<KIND, MI, NI, D>::Q : 1;
-  const int rot = ksteps % Q == 0 ? Q * stagger_wg(ksteps / Q) : 0;
+  const int rot = ksteps % Q == 0 ? Q * stagger(tile, ksteps / Q) : 0;
   auto rel = [&](int i) { const int k = i + rot; return k >= ksteps ? k - ksteps : k; };
   Ring<KIND, MI, NI, D> r;
   // The steady-state loop loads unconditionally, so the count of loads in
@@ -289,13 +290,13 @@ __device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_firs
       const int c = t * 64 + lane, ri = c / cpr, ch = c - ri * cpr, rot_i = (ri & 15) % cpr;
       const int gq = ch >= rot_i ? ch - rot_i : ch + cpr - rot_i;
       // lanes past the last row fill padding with a valid row's bytes
-      dma16(op.dxa, m0 + st->a_off + t * 1024, a_row(ri < MI * 16 ? ri : MI * 16 - 1) + 16 * gq,
-            koff);
+      dma16<CPA>(op.dxa, m0 + st->a_off + t * 1024,
+                 a_row(ri < MI * 16 ? ri : MI * 16 - 1) + 16 * gq, koff);
     }
   }
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    ring_load<KIND, MI, NI, D, STAGED>(r, d, k_first + rel(d < ksteps ? d : d % ksteps), op);
+    ring_load<KIND, MI, NI, D, STAGED, CPA>(r, d, k_first + rel(d < ksteps ? d : d % ksteps), op);
   if constexpr (STAGED) {
     // Wait for the copy once, after the first D steps of operand loads are
     // in flight (the empty asm keeps them above the wait).  Vector loads
@@ -313,7 +314,7 @@ __device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_firs
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       ring_compute<KIND>(r, d, rel(ks + d), op, sc, acc);
-      ring_load<KIND, MI, NI, D, STAGED>(r, d, k_first + rel(ks + d + D), op);
+      ring_load<KIND, MI, NI, D, STAGED, CPA>(r, d, k_first + rel(ks + d + D), op);
       if constexpr (STAGED) {
         if (d % 4 == 0) stage_read(r, d, rel(ks + d + D) / 4, *st);
       }
@@ -325,7 +326,7 @@ __device__ __forceinline__ void gemm_steps(const Operand<MI, NI>& op, int k_firs
     if (k < ksteps) {
       ring_compute<KIND>(r, d % D, rel(k), op, sc, acc);
       if (k + D < ksteps) {
-        ring_load<KIND, MI, NI, D, STAGED>(r, d % D, k_first + rel(k + D), op);
+        ring_load<KIND, MI, NI, D, STAGED, CPA>(r, d % D, k_first + rel(k + D), op);
         if constexpr (STAGED) {
           if (d % 4 == 0) stage_read(r, d % D, rel(k + D) / 4, *st);
         }
@@ -366,12 +367,14 @@ struct BlockShape {
 };
 
 
-// Gate/up GEMM + SwiGLU for one (block, slice) tile: h[mi][j] holds the
+// Gate/up GEMM + SwiGLU for one (block, slice) tile (index `tile` for the
+// stagger of its K walk): h[mi][j] holds the
 // lane's C elements of gate/up column pair j (columns 32*wn + 16*j + l%16 of
 // the slice), rows 64*wm + 16*mi + 4*(l/16) + i.
 template <int KIND, int BM, int D, int KSPLIT>
-__device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const int* ids,
-                                        f32x4 (&h)[BlockShape<BM>::MI][2], float* red) {
+__device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, uint32_t tile,
+                                        const int* ids, f32x4 (&h)[BlockShape<BM>::MI][2],
+                                        float* red) {
   using B = BlockShape<BM, KSPLIT>;
   constexpr int MI = B::MI;
   constexpr int ES = KindTraits<KIND>::ES;
@@ -434,11 +437,11 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, const in
         const int ni = ri >> 4;
         return (uint32_t)((ni < 2 ? 0 : I) + s * kSlice + 32 * wn + 16 * (ni & 1) + (ri & 15)) * rs;
       };
-      gemm_steps<KIND, MI, 4, D, true>(op, k_lo, k_hi - k_lo, acc, &st, a_row, b_row);
+      gemm_steps<KIND, MI, 4, D, true>(op, k_lo, k_hi - k_lo, tile, acc, &st, a_row, b_row);
       done = true;
     }
   }
-  if (!done) gemm_steps<KIND, MI, 4, D>(op, k_lo, k_hi - k_lo, acc);
+  if (!done) gemm_steps<KIND, MI, 4, D>(op, k_lo, k_hi - k_lo, tile, acc);
   if constexpr (KSPLIT > 1) {
     // partial sums of groups 1.. go through LDS (lane-contiguous floats);
     // group 0 adds them in group order
@@ -547,24 +550,28 @@ __device__ __forceinline__ void requant_tile(const f32x4 (&h)[BlockShape<BM>::MI
 // split mode
 // ---------------------------------------------------------------------------
 
-template <int KIND, int BM, int D, int KSPLIT>
-__global__ void __launch_bounds__((BlockShape<BM, KSPLIT>::THREADS))
-k_up(MoeArgs p) {
+// Gate/up GEMM, SwiGLU and requantization of the tile (block b of expert
+// e, slice s; tile index b * S + s), written to intermediate rows
+// hrow0 .. hrow0 + block_m - 1;
+// ids holds the block's route ids in LDS.  Every wave of the workgroup
+// calls it (it has workgroup barriers).
+// Store of the intermediate: plain, or (DEV) a relaxed device-scope atomic
+// store, written where every XCD reads the same data.
+template <bool DEV, class T>
+__device__ __forceinline__ void store_h(T* ptr, T v) {
+  if constexpr (DEV) __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *ptr = v;
+}
+
+template <int KIND, int BM, int D, int KSPLIT, bool DEV = false>
+__device__ __forceinline__ void up_block(const MoeArgs& p, int e, int s, uint32_t tile,
+                                         size_t hrow0, const int* ids, float* lds_amax,
+                                         float* red) {
   using B = BlockShape<BM, KSPLIT>;
   constexpr int MI = B::MI;
   constexpr int ES = KindTraits<KIND>::ES;
-  const int S = p.I / kSlice;
-  const int b = blockIdx.x / S, s = blockIdx.x % S;
-  if (b * BM >= *p.ntp) return;
-  const int e = p.expert_ids[b];
-  if ((unsigned)e >= (unsigned)p.E) return;
-  __shared__ int ids[BM];
-  __shared__ float lds_amax[4 * BM];
-  __shared__ float red[B::RED];
-  if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
-  __syncthreads();
   f32x4 h[MI][2];
-  up_tile<KIND, BM, D, KSPLIT>(p, e, s, ids, h, red);
+  up_tile<KIND, BM, D, KSPLIT>(p, e, s, tile, ids, h, red);
   uint32_t codes[MI][2][4];
   float sf[MI][4];
   int sx[MI][4];
@@ -580,20 +587,20 @@ k_up(MoeArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wm * 64 + mi * 16 + 4 * g + i;
-      const size_t pos = (size_t)b * BM + row;
+      const size_t pos = hrow0 + row;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int col = s * kSlice + 32 * wn + 16 * j + r16;
         if constexpr (ES == 2)
-          reinterpret_cast<uint16_t*>(p.hq)[pos * I + col] = (uint16_t)codes[mi][j][i];
+          store_h<DEV>(reinterpret_cast<uint16_t*>(p.hq) + pos * I + col, (uint16_t)codes[mi][j][i]);
         else
-          p.hq[pos * I + col] = (uint8_t)codes[mi][j][i];
+          store_h<DEV>(p.hq + pos * I + col, (uint8_t)codes[mi][j][i]);
       }
       if (r16 == 0) {
         if constexpr (KIND == KIND_FP8B) {
-          if (wn == 0) reinterpret_cast<float*>(p.hs)[pos * (I / 128) + s] = sf[mi][i];
+          if (wn == 0) store_h<DEV>(reinterpret_cast<float*>(p.hs) + pos * (I / 128) + s, sf[mi][i]);
         }
-        if constexpr (is_mx(KIND)) p.hs[pos * (I / 32) + s * 4 + wn] = (uint8_t)sx[mi][i];
+        if constexpr (is_mx(KIND)) store_h<DEV>(p.hs + pos * (I / 32) + s * 4 + wn, (uint8_t)sx[mi][i]);
       }
     }
   if (s == 0 && threadIdx.x < BM) {
@@ -602,20 +609,33 @@ k_up(MoeArgs p) {
   }
 }
 
-template <int KIND, int BM, int D>
-__global__ void __launch_bounds__(BlockShape<BM>::THREADS)
-k_down(MoeArgs p) {
-  constexpr int MI = BlockShape<BM>::MI;
-  constexpr int ES = KindTraits<KIND>::ES;
-  const int K = p.K, I = p.I;
-  const int NT = (K + 255) / 256;
-  const int b = blockIdx.x / NT, ct = blockIdx.x % NT;
+template <int KIND, int BM, int D, int KSPLIT>
+__global__ void __launch_bounds__((BlockShape<BM, KSPLIT>::THREADS))
+k_up(MoeArgs p) {
+  using B = BlockShape<BM, KSPLIT>;
+  const int S = p.I / kSlice;
+  const int b = blockIdx.x / S, s = blockIdx.x % S;
   if (b * BM >= *p.ntp) return;
   const int e = p.expert_ids[b];
   if ((unsigned)e >= (unsigned)p.E) return;
   __shared__ int ids[BM];
+  __shared__ float lds_amax[4 * BM];
+  __shared__ float red[B::RED];
   if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
   __syncthreads();
+  up_block<KIND, BM, D, KSPLIT>(p, e, s, blockIdx.x, (size_t)b * BM, ids, lds_amax, red);
+}
+
+// Down GEMM of the tile (block b of expert e, output columns ct*256 ..
+// ct*256 + 255; tile index b * NT + ct) from intermediate rows hrow0 ..:
+// fp32 per-route rows of yr.
+// CPA: cache policy of the intermediate's loads.
+template <int KIND, int BM, int D, int CPA = 0>
+__device__ __forceinline__ void down_block(const MoeArgs& p, int e, int ct, uint32_t tile,
+                                           size_t hrow0, const int* ids) {
+  constexpr int MI = BlockShape<BM>::MI;
+  constexpr int ES = KindTraits<KIND>::ES;
+  const int K = p.K, I = p.I;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int wn = wid & 3, wm = wid >> 2;
   const int g = lane >> 4, r16 = lane & 15;
@@ -623,27 +643,27 @@ k_down(MoeArgs p) {
   if (c0 >= K) return;
   const int IS = I / 128;
   Operand<MI, 4> op;
-  op.ra = make_rsrc(p.hq, (uint32_t)((size_t)p.blocks_cap * BM * I * ES));
+  op.ra = make_rsrc(p.hq, (uint32_t)((size_t)p.h_rows * I * ES));
   op.rb = make_rsrc(p.w2 + (size_t)e * K * BTraits<KIND>::row_bytes(I),
                     (uint32_t)(K * BTraits<KIND>::row_bytes(I)));
   if constexpr (KIND == KIND_FP8B)
-    op.rsa = make_rsrc(p.hs, (uint32_t)((size_t)p.blocks_cap * BM * IS * 4));
+    op.rsa = make_rsrc(p.hs, (uint32_t)((size_t)p.h_rows * IS * 4));
   if constexpr (is_mx(KIND)) {
-    op.rxa = make_rsrc(p.hs, (uint32_t)((size_t)p.blocks_cap * BM * (I / 32)));
+    op.rxa = make_rsrc(p.hs, (uint32_t)((size_t)p.h_rows * (I / 32)));
     op.rxb = make_rsrc(reinterpret_cast<const uint8_t*>(p.w2s) + (size_t)e * K * (I / 32),
                        (uint32_t)((size_t)K * (I / 32)));
-    op.dxa = make_desc(p.hs, (uint32_t)((size_t)p.blocks_cap * BM * (I / 32)));
+    op.dxa = make_desc(p.hs, (uint32_t)((size_t)p.h_rows * (I / 32)));
     op.dxb = make_desc(reinterpret_cast<const uint8_t*>(p.w2s) + (size_t)e * K * (I / 32),
                        (uint32_t)((size_t)K * (I / 32)));
   }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
-    const uint32_t pos = (uint32_t)b * BM + wm * 64 + mi * 16 + r16;
+    const uint32_t pos = (uint32_t)hrow0 + wm * 64 + mi * 16 + r16;
     op.a[mi] = pos * I * ES + 16 * g;
     if constexpr (KIND == KIND_FP8B) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t cpos = (uint32_t)b * BM + wm * 64 + mi * 16 + 4 * g + i;
+        const uint32_t cpos = (uint32_t)hrow0 + wm * 64 + mi * 16 + 4 * g + i;
         op.as[mi][i] = cpos * IS * 4;
       }
     }
@@ -666,14 +686,14 @@ k_down(MoeArgs p) {
     constexpr int W = BlockShape<BM>::THREADS / 64;
     if (stage_bytes(IS, MI, W) > 0) {
       const Stage st = make_stage(IS, MI, W, wave_id());
-      const uint32_t rs = (uint32_t)(I / 32), b0 = (uint32_t)b * BM + wm * 64;
+      const uint32_t rs = (uint32_t)(I / 32), b0 = (uint32_t)hrow0 + wm * 64;
       auto a_row = [&](int ri) { return (b0 + ri) * rs; };
       auto b_row = [&](int ri) { return (uint32_t)(c0 + ri) * rs; };
-      gemm_steps<KIND, MI, 4, D, true>(op, 0, IS, acc, &st, a_row, b_row);
+      gemm_steps<KIND, MI, 4, D, true, CPA>(op, 0, IS, tile, acc, &st, a_row, b_row);
       done = true;
     }
   }
-  if (!done) gemm_steps<KIND, MI, 4, D>(op, 0, IS, acc);
+  if (!done) gemm_steps<KIND, MI, 4, D, false, CPA>(op, 0, IS, tile, acc);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -683,6 +703,120 @@ k_down(MoeArgs p) {
 #pragma unroll
       for (int ni = 0; ni < 4; ++ni) p.yr[(size_t)id * K + c0 + 16 * ni + r16] = acc[mi][ni][i];
     }
+}
+
+template <int KIND, int BM, int D>
+__global__ void __launch_bounds__(BlockShape<BM>::THREADS)
+k_down(MoeArgs p) {
+  const int NT = (p.K + 255) / 256;
+  const int b = blockIdx.x / NT, ct = blockIdx.x % NT;
+  if (b * BM >= *p.ntp) return;
+  const int e = p.expert_ids[b];
+  if ((unsigned)e >= (unsigned)p.E) return;
+  __shared__ int ids[BM];
+  if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
+  __syncthreads();
+  down_block<KIND, BM, D>(p, e, ct, blockIdx.x, (size_t)b * BM, ids);
+}
+
+// ---------------------------------------------------------------------------
+// persistent ring mode ([DeepGEMM #88] "How it works" and "Why the order
+// and not the pool size"): one resident grid takes tasks from a ticket.
+// The stream holds, per block of rows in planner order, its up tasks (one
+// per 128-wide slice of I) followed, lag blocks later, by its down tasks
+// (one per 256 output columns).  Block b's intermediate lives in
+// ring slot b % ring: its up tasks first wait until the down tasks of block
+// b - ring have read the slot, and its down tasks wait until all its up
+// tasks have written it.  Every wait is on a lower ticket, and tickets are
+// taken in order by running workgroups, so the lowest unfinished ticket can
+// always run: the stream drains for any grid size and any lag < ring.  The
+// arithmetic per tile is the split mode's, so results are bitwise equal.
+// ---------------------------------------------------------------------------
+
+constexpr int kRingSpinLimit = 1 << 20;  // ~1 s of polling: only a broken invariant gets there
+
+// Thread 0 polls *w until it reaches v (bounded; past the bound it raises
+// the error word and goes on, and once the word is up no wait polls again,
+// so the kernel always ends soon).
+__device__ __forceinline__ void ring_wait(int* w, int v, int* err) {
+  if (threadIdx.x != 0) return;
+  if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+  for (int n = 0; __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < v; ++n) {
+    if (n == kRingSpinLimit) {
+      atomicOr(err, 1);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Waves per SIMD: two where the larger task body fits half the register
+// file (as the split kernels at 16 rows), else one.  MXFP8 at 16 rows needs
+// slightly more than half once both bodies share one kernel.
+template <int KIND, int BM>
+constexpr int ring_waves_per_simd() { return BM <= 16 && KIND != KIND_MX ? 2 : 1; }
+
+// p.ctl: [0] ticket, [1] error word, then blocks_cap finished-up counts and
+// blocks_cap finished-down counts; all zero at launch.
+template <int KIND, int BM, int D>
+__global__ void __launch_bounds__(BlockShape<BM>::THREADS)
+__attribute__((amdgpu_waves_per_eu(ring_waves_per_simd<KIND, BM>())))
+k_ring(MoeArgs p) {
+  using B = BlockShape<BM>;
+  const int S = p.I / kSlice, NT = (p.K + 255) / 256;
+  const int nb = *p.ntp / BM;
+  const int total = nb * (S + NT);
+  int* const ticket = p.ctl;
+  int* const err = p.ctl + 1;
+  int* const up_done = p.ctl + 2;
+  int* const down_done = up_done + p.blocks_cap;
+  __shared__ int ids[BM];
+  __shared__ float lds_amax[4 * BM];
+  __shared__ float red[B::RED];
+  __shared__ int next;
+  if (threadIdx.x == 0) next = atomicAdd(ticket, 1);
+  __syncthreads();
+  for (;;) {
+    // wave-uniform: every index and offset derived from it stays scalar
+    const int t = __builtin_amdgcn_readfirstlane(next);
+    if (t >= total) break;
+    // no memory operation of the last task is left in flight: the streaming
+    // loops then start from a known count of outstanding loads, which keeps
+    // their waits counted (with an unknown count they wait for every load)
+    wait_vmcnt<0>();
+    __syncthreads();  // every thread holds t; the last task's LDS is dead
+    // the next task's ticket, taken now and read after this task's last barrier
+    if (threadIdx.x == 0) next = atomicAdd(ticket, 1);
+    const RingTask k = ring_task(t, nb, S, NT, p.lag);
+    const int e = p.expert_ids[k.b];
+    const size_t hrow0 = (size_t)(k.b % p.ring) * BM;
+    if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[k.b * BM + threadIdx.x];
+    if (k.kind == 1) {
+      // the slot's previous block has been read: its down tasks consumed
+      // the loaded values before they counted themselves done
+      if (k.b >= p.ring) ring_wait(down_done + (k.b - p.ring), NT, err);
+      __syncthreads();
+      if ((unsigned)e < (unsigned)p.E)
+        up_block<KIND, BM, D, 1, true>(p, e, k.i, (uint32_t)(k.b * S + k.i), hrow0, ids, lds_amax,
+                                       red);
+      // the slice's device-scope stores have completed (been acknowledged)
+      // before the count that publishes them moves
+      asm volatile("" ::: "memory");
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+      __syncthreads();
+      if (threadIdx.x == 0) atomicAdd(up_done + k.b, 1);
+    } else {
+      ring_wait(up_done + k.b, S, err);
+      __syncthreads();
+      // the intermediate is read with device-scope loads, past any stale
+      // copy in this CU's or this XCD's cache
+      if ((unsigned)e < (unsigned)p.E)
+        down_block<KIND, BM, D, kDeviceScope>(p, e, k.i, (uint32_t)(k.b * NT + k.i), hrow0, ids);
+      __syncthreads();
+      if (threadIdx.x == 0) atomicAdd(down_done + k.b, 1);
+    }
+  }
 }
 
 // out[t, c:c+4] = bf16(sum_j w[t,j] * y[t*top_k+j, c:c+4] + sum_s y[shared s of t]),
@@ -745,7 +879,7 @@ k_fused(MoeArgs p) {
   if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
   __syncthreads();
   f32x4 h[MI][2];
-  up_tile<KIND, BM, D, KSPLIT>(p, e, s, ids, h, red);
+  up_tile<KIND, BM, D, KSPLIT>(p, e, s, blockIdx.x, ids, h, red);
   uint32_t codes[MI][2][4];
   float sf[MI][4];
   int sx[MI][4];
@@ -808,9 +942,9 @@ k_fused(MoeArgs p) {
       make_rsrc(p.w2 + (size_t)e * K * BTraits<KIND>::row_bytes(I),
                 (uint32_t)(K * BTraits<KIND>::row_bytes(I)));
   const uint32_t soff = (uint32_t)s * BTraits<KIND>::STEP_BYTES;  // this slice's K step of w2 rows
-  const int qrot = stagger_wg(nchunks);
+  const int qrot = stagger(blockIdx.x, nchunks);
   for (int qi = wn + 4 * kg; qi < nchunks; qi += 4 * KSPLIT) {
-    const int q = (qi + qrot) % nchunks;  // staggered start, see stagger_wg()
+    const int q = (qi + qrot) % nchunks;  // staggered start, see stagger()
     const int c0 = q * 64;
     FragB<KIND> fb[4];
     int xb[4];
@@ -888,7 +1022,7 @@ constexpr int prefetch_depth() {
 }
 
 inline void mark(const TimingHook& h, int which, bool after, hipStream_t st) {
-  if (h.which == which && h.before && h.after) hipEventRecord(after ? h.after : h.before, st);
+  if (h.which == which && h.before && h.after) (void)hipEventRecord(after ? h.after : h.before, st);
 }
 
 // Launch of the up-GEMM kernel (k_up or k_fused) with KSPLIT K groups.
@@ -927,12 +1061,81 @@ void launch_up_any(int split, const MoeArgs& a, unsigned grid, hipStream_t st) {
   launch_up<KIND, BM, 1>(split, a, grid, st);
 }
 
+// Persistent grid of k_ring for a dynamic LDS size (cached per device and
+// size): one workgroup per CU, provided one fits.  Measured (K=4096,
+// I=2048, E=256, top-6, blockwise FP8): 242 / 927 / 1190 us at T = 8 / 64
+// / 256 with one per CU against 326 / 1058 / 1334 us with the two that fit;
+// the second workgroup mostly waits for up tasks that the first has not
+// finished, while one per CU keeps the waits near zero.
+template <int KIND, int BM, int D>
+int ring_grid(size_t lds) {
+  struct Entry {
+    int dev;
+    size_t lds;
+    int n;
+  };
+  static thread_local Entry cache[8];
+  static thread_local int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  for (int i = 0; i < used; ++i)
+    if (cache[i].dev == dev && cache[i].lds == lds) return cache[i].n;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_ring<KIND, BM, D>,
+                                                   BlockShape<BM>::THREADS, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (per_cu < 1 || cus < 1) return 0;
+  cache[used < 8 ? used++ : 7] = Entry{dev, lds, cus};
+  return cus;
+}
+
+// Ring mode: clear the control words and flags (adjacent in the
+// workspace), one resident grid over the lag-ordered task stream, then the
+// combine.
+template <int KIND, int BM>
+hipError_t launch_ring(const MoeArgs& a0, hipStream_t st, const TimingHook& hk) {
+  constexpr int THREADS = BlockShape<BM>::THREADS, W = THREADS / 64;
+  constexpr int D = prefetch_depth<KIND, BM>();
+  constexpr int MI = BlockShape<BM>::MI;
+  MoeArgs a = a0;
+  const int S = a.I / kSlice, per = S + (a.K + 255) / 256;
+  if (a.ring < 1 || reinterpret_cast<uint8_t*>(a.flags) !=
+                        reinterpret_cast<uint8_t*>(a.ctl) + ring_ctl_bytes(a.blocks_cap))
+    return hipErrorInvalidValue;
+  size_t lds = 0;
+  if constexpr (is_mx(KIND) && scale_run<D>() == 4) {
+    const size_t up = (size_t)W * up_stage_bytes(a.K, MI, 1, W);
+    const size_t dn = (size_t)W * stage_bytes(a.I / 128, MI, W);
+    lds = up > dn ? up : dn;
+  }
+  const int g = ring_grid<KIND, BM, D>(lds);
+  if (g <= 0) return hipErrorInvalidDeviceFunction;
+  const int lag = ring_lag(g, S);
+  a.lag = lag < a.ring - 1 ? lag : a.ring - 1;
+  const size_t tasks = (size_t)a.blocks_cap * per;
+  const unsigned grid = (unsigned)((size_t)g < tasks ? (size_t)g : tasks);
+  const size_t n16 = (ring_ctl_bytes(a.blocks_cap) + total_routes(a) * 4 + 15) / 16;
+  hipLaunchKernelGGL(k_zero, dim3(grid_for(n16, 256)), dim3(256), 0, st,
+                     reinterpret_cast<uint4*>(a.ctl), n16);
+  mark(hk, 1, false, st);
+  hipLaunchKernelGGL((k_ring<KIND, BM, D>), dim3(grid), dim3(THREADS), lds, st, a);
+  mark(hk, 1, true, st);
+  const int CT = (a.K + 1023) / 1024;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int KIND, int BM>
 hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const TimingHook& hk) {
   constexpr int THREADS = BlockShape<BM>::THREADS;
   constexpr int D = prefetch_depth<KIND, BM>();
   const int S = a.I / kSlice;
   const size_t R = total_routes(a);
+  if (split == 2) {
+    if constexpr (BM <= 32) return launch_ring<KIND, BM>(a, st, hk);
+    else return hipErrorInvalidValue;
+  }
   if (split) {
     const size_t fbytes = (R * 4 + 15) / 16;
     hipLaunchKernelGGL(k_zero, dim3(grid_for(fbytes, 256)), dim3(256), 0, st,

@@ -106,7 +106,10 @@ def test_ffn_errors_before_launch(fn):
         assert _ffn(L, fn, bm=256, split=0) == -3       # 256 runs the split mode only
     assert _ffn(L, fn, T=-1) == -2
     assert _ffn(L, fn, k=0) == -2
-    assert _ffn(L, fn, split=2) == -3
+    assert _ffn(L, fn, split=3) == -3
+    assert _ffn(L, fn, split=2, bm=64) == -3            # the ring mode runs 16 or 32 rows
+    assert _ffn(L, fn, split=2, ws_bytes=100) == -5     # not even one ring slot
+    assert b"ring slot" in L.moe_last_error()
     assert _ffn(L, fn, x=0) == -1                       # null input
     assert _ffn(L, fn, x=FAKE + 8) == -4                # misaligned
     assert _ffn(L, fn, ws=0) == -5                      # no workspace
