@@ -182,8 +182,9 @@ int moe_workspace_size(int32_t dtype, int64_t T, int64_t K, int64_t N,
  *                   rows)
  *   *slot_bytes     bytes per slot (block_m rows of values and scales)
  *   *default_slots  the slots moe_workspace_size(.., split = 2, ..) provides:
- *                   twice the lag that the largest resident grid can ask
- *                   for, plus two, capped at blocks_cap
+ *                   twice the lag of a 512-workgroup grid (the launch uses
+ *                   one workgroup per CU), plus two, capped at blocks_cap;
+ *                   the lag is 1.5 x the grid / (I/128) blocks
  * block_m must be 16 or 32.  Errors: MOE_ERR_NULL, and as moe_workspace_size.
  */
 int moe_ring_layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E,

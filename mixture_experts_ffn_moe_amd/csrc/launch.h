@@ -44,9 +44,9 @@ struct MoeArgs {
 // third less, half the grid polls at decode sizes).  A ring of twice the lag
 // (plus 2) likewise leaves the down tasks of a slot's previous block time
 // to finish before the slot is overwritten.  The default ring assumes a
-// grid of 2048 workgroups (8 per CU on 256 CUs, far above the one per CU
-// the launch uses), so the launch's own lag always fits it.
-constexpr int kRingMaxResident = 2048;
+// grid of 512 workgroups, twice the one per CU that the launch uses on
+// 256 CUs, so the launch's own lag fits it with room to spare.
+constexpr int kRingMaxResident = 512;
 inline int ring_lag(int resident, int up_per_block) {
   return (3 * resident + 2 * up_per_block - 1) / (2 * up_per_block);
 }

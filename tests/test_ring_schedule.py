@@ -120,7 +120,7 @@ def test_ring_workspace(dtype, es, sb, T, bm):
     I = N // 2
     assert slot == bm * (I * es + sb)
     _, blocks = moe.moe_align_capacity(T, k, E, bm)
-    lag_max = -(-3 * 2048 // (2 * (I // 128)))
+    lag_max = -(-3 * 512 // (2 * (I // 128)))
     assert slots == min(blocks, 2 * lag_max + 2)
     total = moe.moe_workspace_size(dtype, T, K, N, E, k, bm, split=2)
     assert total == -(-(fixed + slots * slot) // 256) * 256
