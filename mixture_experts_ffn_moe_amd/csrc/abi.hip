@@ -380,12 +380,24 @@ int moe_select_block_m(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32
   const int64_t R = T * top_k;
   const int64_t act = R < E ? (R > 0 ? R : 1) : E;
   const double per = (double)R / (double)act;
+  if (dtype == MOE_FP8_BLOCKWISE && K % 256 == 0) {
+    // measured (whole forward, blockwise FP8): 16-row streaming blocks while
+    // experts hold about one block (7 rows/expert, K=4096, I=2048, E=288:
+    // 1253 us against 1402 for 32); 32 rows up to ~24 (14 rows: 1392 against
+    // 1447 for 16; 16 rows at K=7168, I=3072, E=384: 3097 against 4061 for
+    // 16 and 4548 for 128); beyond, the 128-row LDS-tiled kernels with two
+    // waves per SIMD (28 rows: 1664 against 1729 for 64; 64 rows at K=7168:
+    // 6328 against 7322; 227 rows: 4042 against 4532 for 256)
+    *block_m = per <= 10 ? 16 : per <= 24 ? 32 : 128;
+    return ok();
+  }
   // the 256-row tile pays off where the MFMA applies the scales itself; the
   // blockwise path's per-step promotion does not fit its register budget
   const bool big_ok = dtype == MOE_MXFP8 && K % 256 == 0;
   // measured: 16 rows stream the weights best while experts hold about a
-  // block; past that the 64-row LDS-tiled kernels win (32 measured slower
-  // than 64 at 28 rows per expert)
+  // block; past that the 64-row LDS-tiled kernels win (MXFP8, K=4096,
+  // I=256, E=32: 73 us at 32 rows/expert against 87 for 16 and 128; 93 us
+  // at 128 rows against 107 for 128)
   *block_m = per <= 16 ? 16 : per <= 160 ? 64 : (per <= 200 || !big_ok) ? 128 : 256;
   return ok();
 }

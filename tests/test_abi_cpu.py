@@ -137,9 +137,12 @@ def test_heuristics():
     assert moe.moe_select_block_m(8192, 8, 288, "mxfp8", 4096) == 256
     assert moe.moe_select_block_m(8192, 8, 288, "mxfp8", 4096 + 128) == 128
     assert moe.moe_select_block_m(8192, 8, 288, "bf16", 4096) == 128
-    assert moe.moe_select_block_m(4096, 8, 288, "fp8_blockwise", 4096) == 64
-    assert moe.moe_select_block_m(1024, 8, 288, "fp8_blockwise", 4096) == 64   # 28 rows/expert
-    assert moe.moe_select_block_m(1024, 6, 384, "fp8_blockwise", 7168) == 16   # 16 rows/expert
+    assert moe.moe_select_block_m(4096, 8, 288, "fp8_blockwise", 4096) == 128
+    assert moe.moe_select_block_m(1024, 8, 288, "fp8_blockwise", 4096) == 128  # 28 rows/expert
+    assert moe.moe_select_block_m(1024, 6, 384, "fp8_blockwise", 7168) == 32   # 16 rows/expert
+    assert moe.moe_select_block_m(256, 8, 288, "fp8_blockwise", 4096) == 16    # 7 rows/expert
+    assert moe.moe_select_block_m(512, 8, 288, "fp8_blockwise", 4096) == 32    # 14 rows/expert
+    assert moe.moe_select_block_m(64, 6, 256, "fp8_blockwise", 4096 + 128) == 16
     assert moe.moe_select_split("fp8_blockwise", 8, 4096, 4096, 256, 6, 16) == 1  # 6.4 GB of weights
     assert moe.moe_select_split("mxfp8", 8, 4096, 512, 32, 8, 16) == 1         # 100 MB
     assert moe.moe_select_split("bf16", 32, 512, 512, 8, 2, 16) == 0            # 6.3 MB: fused
