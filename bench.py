@@ -477,7 +477,8 @@ def main():
         valid = (ids >= 0) & (ids < E)
         R = int(valid.sum().item())
         E_act = int(torch.unique(ids[valid]).numel())
-        bm = args.block_m or moe.moe_select_block_m(T, k, E, kind, K)
+        # block size from the routing at hand: routes per active expert
+        bm = args.block_m or moe.moe_select_block_m_routed(T, k, E, E_act, kind, K)
         split = args.split if args.split >= 0 else moe.moe_select_split(kind, T, K, N, E, k, bm)
         rows, blocks = moe.moe_align_capacity(T, k, E, bm)
         align_out = (torch.empty(rows, dtype=torch.int32, device=dev),

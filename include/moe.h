@@ -155,11 +155,26 @@ int moe_select_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E,
 /*
  * Suggested block_m for a call (small blocks for decode-sized batches, so
  * that padding does not dominate; larger blocks once experts hold many
- * rows; 256 only where the dtype and K allow it).  *block_m is a host
+ * rows; 256 only where the dtype and K allow it).  The choice follows the
+ * mean routes per active expert, assuming here that the T*top_k routes
+ * spread evenly over min(T*top_k, E) experts.  *block_m is a host
  * out-param.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE.
  */
 int moe_select_block_m(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32_t E,
                        int32_t* block_m);
+
+/*
+ * The same, with the number of experts that hold at least one route
+ * (active_experts, in [0, E]; a caller that has the routing on the host
+ * counts them).  A skewed routing concentrates the routes on few experts,
+ * which then hold many rows each: blockwise FP8 at K=7168, I=3072, E=384,
+ * T=256 under a zipf routing (59 active experts, 26 rows each) runs in
+ * 961 us with 64-row tiles against 1389 us with the 16-row blocks the
+ * even-spread estimate (4 rows per expert) picks.  Errors: MOE_ERR_NULL,
+ * MOE_ERR_SHAPE.
+ */
+int moe_select_block_m_routed(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32_t E,
+                              int32_t active_experts, int32_t* block_m);
 
 /*
  * Workspace bytes a fused_moe_* call with these sizes needs (host out-param).

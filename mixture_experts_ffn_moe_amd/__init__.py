@@ -28,6 +28,7 @@ import torch
 __all__ = [
     "MoeError", "lib", "LIB_PATH", "MOE_BF16", "MOE_FP8_BLOCKWISE", "MOE_MXFP8", "MOE_MXFP4",
     "moe_align_capacity", "moe_align", "moe_select_split", "moe_select_block_m",
+    "moe_select_block_m_routed",
     "moe_workspace_size", "moe_workspace_layout", "moe_ring_layout", "moe_ring_schedule",
     "fused_moe_bf16",
     "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4", "EXPORTED_SYMBOLS",
@@ -46,6 +47,7 @@ EXPORTED_SYMBOLS = (
     "fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4",
     "moe_set_timing_events", "moe_route_align_workspace_size", "moe_route_align",
     "moe_align_shared", "fused_moe_shared", "moe_ring_layout", "moe_ring_schedule",
+    "moe_select_block_m_routed",
 )
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
@@ -83,6 +85,8 @@ def lib():
     L.moe_select_split.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32,
                                    ctypes.POINTER(_I32)]
     L.moe_select_block_m.argtypes = [_I32, _I64, _I64, _I32, _I32, ctypes.POINTER(_I32)]
+    L.moe_select_block_m_routed.argtypes = [_I32, _I64, _I64, _I32, _I32, _I32,
+                                            ctypes.POINTER(_I32)]
     L.moe_workspace_size.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
                                      ctypes.POINTER(_SZ)]
     L.moe_workspace_layout.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32,
@@ -254,6 +258,22 @@ def moe_select_block_m(T, top_k, num_experts, dtype="fp8_blockwise", K=4096):
     return out.value
 
 
+def moe_select_block_m_routed(T, top_k, num_experts, active_experts, dtype="fp8_blockwise",
+                              K=4096):
+    """block_m from the number of experts that hold at least one route."""
+    out = _I32()
+    _check(lib().moe_select_block_m_routed(_DTYPE_CODE.get(dtype, dtype), T, K, top_k,
+                                           num_experts, active_experts, ctypes.byref(out)))
+    return out.value
+
+
+def active_experts(topk_ids, num_experts):
+    """Experts holding at least one route of topk_ids (a host-side count)."""
+    ids = topk_ids.reshape(-1)
+    valid = ids[(ids >= 0) & (ids < num_experts)]
+    return int(torch.unique(valid).numel())
+
+
 def moe_workspace_size(dtype, T, K, N, num_experts, top_k, block_m, split=-1):
     out = _SZ()
     _check(lib().moe_workspace_size(_DTYPE_CODE.get(dtype, dtype), T, K, N, num_experts, top_k,
@@ -354,7 +374,9 @@ def run_case(case, block_m=None, split=-1, stream=None, workspace=None, out=None
     call with the same routing and block_m filled it."""
     T = case.x.shape[0]
     if block_m is None:
-        block_m = moe_select_block_m(T, case.top_k, case.E, case.kind, case.x.shape[1])
+        block_m = moe_select_block_m_routed(T, case.top_k, case.E,
+                                            active_experts(case.topk_ids, case.E), case.kind,
+                                            case.x.shape[1])
     S = getattr(case, "n_shared", 0)
     if skip_align:
         if align_out is None:

@@ -371,35 +371,50 @@ int moe_select_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, 
   return ok();
 }
 
+int moe_select_block_m_routed(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32_t E,
+                              int32_t active_experts, int32_t* block_m) {
+  if (!block_m) return fail(MOE_ERR_NULL, "block_m is NULL");
+  int rc = check_routes(T, top_k, E);
+  if (rc) return rc;
+  if (active_experts < 0 || active_experts > E)
+    return fail(MOE_ERR_SHAPE, "active_experts must lie in [0, E] (got %d)", active_experts);
+  const int64_t R = T * top_k;
+  const int64_t act = active_experts > 0 ? active_experts : 1;
+  const double per = (double)R / (double)act;     // rows per active expert
+  const double per_all = (double)R / (double)E;   // rows per expert, all experts
+  if (dtype == MOE_FP8_BLOCKWISE && K % 256 == 0) {
+    // measured (whole forward, blockwise FP8; K=4096, I=2048, E=256 / 288,
+    // near-uniform routing; K=7168, I=3072, E=384, zipf routing):
+    // - 16-row streaming blocks up to ~12 rows per active expert (6: 1135 us
+    //   against 1189 for 64; 12: 1198 against 1206);
+    // - 64-row LDS-tiled blocks up to ~64 (14.6: 1345 against 1450 for 16;
+    //   29: 1407 against 1508 for 128; 26 under zipf: 961 against 1389 for 16);
+    // - 256 rows only where every expert holds that many (234 per expert:
+    //   2824 against 3166 for 128); under a skewed routing the long tail of
+    //   small experts wastes most of a 256-row tile (zipf, 110 rows per active
+    //   expert, 32 per expert: 3018 against 2714 for 128);
+    // - 128 rows otherwise (117: 1972 against 2487 for 64 and 2376 for 256).
+    *block_m = per <= 12 ? 16 : per <= 64 ? 64 : (per > 160 && per_all > 160) ? 256 : 128;
+    return ok();
+  }
+  // MXFP8 (the MFMA applies the scales itself) and the streaming-only dtypes;
+  // measured (MXFP8, K=4096, I=256, E=32): 69 us at 32 rows per expert with
+  // 64-row tiles against 92 for 16 and 82 for 128; 88 us at 128 rows against
+  // 101 for 128; 219 us at 512 rows with 256-row tiles against 253 for 128
+  const bool big_ok = dtype == MOE_MXFP8 && K % 256 == 0;
+  *block_m = per <= 16 ? 16 : per <= 160 ? 64 : (per <= 200 || !big_ok) ? 128 : 256;
+  return ok();
+}
+
 int moe_select_block_m(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32_t E,
                        int32_t* block_m) {
   if (!block_m) return fail(MOE_ERR_NULL, "block_m is NULL");
   int rc = check_routes(T, top_k, E);
   if (rc) return rc;
-  // mean rows per non-empty expert, if routes spread evenly
+  // routes spread evenly: min(R, E) experts hold routes
   const int64_t R = T * top_k;
-  const int64_t act = R < E ? (R > 0 ? R : 1) : E;
-  const double per = (double)R / (double)act;
-  if (dtype == MOE_FP8_BLOCKWISE && K % 256 == 0) {
-    // measured (whole forward, blockwise FP8): 16-row streaming blocks while
-    // experts hold about one block (7 rows/expert, K=4096, I=2048, E=288:
-    // 1253 us against 1402 for 32); 32 rows up to ~24 (14 rows: 1392 against
-    // 1447 for 16; 16 rows at K=7168, I=3072, E=384: 3097 against 4061 for
-    // 16 and 4548 for 128); beyond, the 128-row LDS-tiled kernels with two
-    // waves per SIMD (28 rows: 1664 against 1729 for 64; 64 rows at K=7168:
-    // 6328 against 7322; 227 rows: 4042 against 4532 for 256)
-    *block_m = per <= 10 ? 16 : per <= 24 ? 32 : 128;
-    return ok();
-  }
-  // the 256-row tile pays off where the MFMA applies the scales itself; the
-  // blockwise path's per-step promotion does not fit its register budget
-  const bool big_ok = dtype == MOE_MXFP8 && K % 256 == 0;
-  // measured: 16 rows stream the weights best while experts hold about a
-  // block; past that the 64-row LDS-tiled kernels win (MXFP8, K=4096,
-  // I=256, E=32: 73 us at 32 rows/expert against 87 for 16 and 128; 93 us
-  // at 128 rows against 107 for 128)
-  *block_m = per <= 16 ? 16 : per <= 160 ? 64 : (per <= 200 || !big_ok) ? 128 : 256;
-  return ok();
+  const int32_t act = (int32_t)(R < E ? (R > 0 ? R : 1) : E);
+  return moe_select_block_m_routed(dtype, T, K, top_k, E, act, block_m);
 }
 
 int moe_workspace_size(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,

@@ -47,11 +47,17 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Logical workgroup index: consecutive logical tiles go to one XCD (hardware
-// dispatches workgroup ids round-robin over the 8 XCDs).
-__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
-  const int per = nwg / 8;
-  return (bid % 8) * per + bid / 8;
+// Logical tile index of workgroup `bid`.  The hardware dispatches workgroup
+// ids round-robin over the 8 XCDs; the `valid` tiles that have a planner
+// block (read on the device) are split into 8 contiguous runs, run x on XCD
+// x, so consecutive tiles share that XCD's L2 and every XCD gets an equal
+// share.  (Splitting the whole grid instead, whose blocks past the padded
+// count are empty, left the last XCDs idle: at K=4096, I=2048, E=288,
+// top-8, T=8192 only 656 of 798 blocks hold routes.)  -1: past the runs.
+__device__ __forceinline__ int xcd_remap(int bid, int valid) {
+  const int per = (valid + 7) / 8;
+  const int j = bid / 8;
+  return j < per ? (bid % 8) * per + j : -1;
 }
 
 template <int KIND, int BM, int BN, int NS>
@@ -309,7 +315,8 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   __shared__ int ids[BM];
   __shared__ float lds_amax[C::WN * BM];
   const int S = p.I / 128;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int logical = xcd_remap(blockIdx.x, (*p.ntp / BM) * S);
+  if (logical < 0) return;
   const int b = logical / S, s = logical % S;
   if (b >= p.blocks_cap || b * BM >= *p.ntp) return;
   const int e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);  // uniform: descriptors in SGPRs
@@ -446,7 +453,8 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   __shared__ int ids[BM];
   const int K = p.K, I = p.I, IS = I / 128;
   const int NT = K / 256;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int logical = xcd_remap(blockIdx.x, (*p.ntp / BM) * NT);
+  if (logical < 0) return;
   const int b = logical / NT, ct = logical % NT;
   if (b >= p.blocks_cap || b * BM >= *p.ntp) return;
   const int e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);  // uniform: descriptors in SGPRs

@@ -133,16 +133,37 @@ def test_workspace_sizes_grow_with_tokens():
 
 def test_heuristics():
     assert moe.moe_select_block_m(8, 6, 256) == 16
-    assert moe.moe_select_block_m(8192, 8, 288, "fp8_blockwise", 4096) == 128
+    assert moe.moe_select_block_m(8192, 8, 288, "fp8_blockwise", 4096) == 256  # 228 rows/expert
     assert moe.moe_select_block_m(8192, 8, 288, "mxfp8", 4096) == 256
     assert moe.moe_select_block_m(8192, 8, 288, "mxfp8", 4096 + 128) == 128
     assert moe.moe_select_block_m(8192, 8, 288, "bf16", 4096) == 128
-    assert moe.moe_select_block_m(4096, 8, 288, "fp8_blockwise", 4096) == 128
-    assert moe.moe_select_block_m(1024, 8, 288, "fp8_blockwise", 4096) == 128  # 28 rows/expert
-    assert moe.moe_select_block_m(1024, 6, 384, "fp8_blockwise", 7168) == 32   # 16 rows/expert
+    assert moe.moe_select_block_m(4096, 8, 288, "fp8_blockwise", 4096) == 128  # 114 rows/expert
+    assert moe.moe_select_block_m(1024, 8, 288, "fp8_blockwise", 4096) == 64   # 28 rows/expert
+    assert moe.moe_select_block_m(1024, 6, 384, "fp8_blockwise", 7168) == 64   # 16 rows/expert
     assert moe.moe_select_block_m(256, 8, 288, "fp8_blockwise", 4096) == 16    # 7 rows/expert
-    assert moe.moe_select_block_m(512, 8, 288, "fp8_blockwise", 4096) == 32    # 14 rows/expert
+    assert moe.moe_select_block_m(256, 6, 256, "fp8_blockwise", 4096) == 16    # 6 rows/expert
+    assert moe.moe_select_block_m(512, 8, 288, "fp8_blockwise", 4096) == 64    # 14 rows/expert
     assert moe.moe_select_block_m(64, 6, 256, "fp8_blockwise", 4096 + 128) == 16
+
+
+def test_routed_heuristic():
+    # the even-spread selector is the routed one with min(T*top_k, E) active experts
+    for T, k, E in [(8, 6, 256), (256, 6, 256), (1024, 8, 288), (8192, 8, 288), (3, 2, 64)]:
+        for kind in ("fp8_blockwise", "mxfp8", "bf16", "mxfp4"):
+            act = min(T * k, E)
+            assert (moe.moe_select_block_m(T, k, E, kind, 4096)
+                    == moe.moe_select_block_m_routed(T, k, E, act, kind, 4096))
+    # skewed routing: few active experts holding many rows each
+    assert moe.moe_select_block_m_routed(256, 6, 384, 59, "fp8_blockwise", 7168) == 64
+    assert moe.moe_select_block_m_routed(2048, 6, 384, 112, "fp8_blockwise", 7168) == 128
+    # 203 rows per active expert but 64 per expert: not every expert fills 256 rows
+    assert moe.moe_select_block_m_routed(4096, 6, 384, 121, "fp8_blockwise", 7168) == 128
+    assert moe.moe_select_block_m_routed(8192, 8, 288, 280, "fp8_blockwise", 4096) == 256
+    assert moe.moe_select_block_m_routed(0, 6, 256, 0, "fp8_blockwise", 4096) == 16
+    for bad in (-1, 257):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_select_block_m_routed(8, 6, 256, bad, "fp8_blockwise", 4096)
+        assert ei.value.status == -2
     assert moe.moe_select_split("fp8_blockwise", 8, 4096, 4096, 256, 6, 16) == 1  # 6.4 GB of weights
     assert moe.moe_select_split("mxfp8", 8, 4096, 512, 32, 8, 16) == 1         # 100 MB
     assert moe.moe_select_split("bf16", 32, 512, 512, 8, 2, 16) == 0            # 6.3 MB: fused

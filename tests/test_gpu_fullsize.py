@@ -47,7 +47,7 @@ def sample_tokens(case, n):
 def test_full_size_sampled(name, T):
     c = datagen.make_workload_case(name, T, device="cuda", weights=weights(name))
     K, I, E, k = c.K, c.I, c.E, c.top_k
-    bm = moe.moe_select_block_m(T, k, E, c.kind, K)
+    bm = moe.moe_select_block_m_routed(T, k, E, moe.active_experts(c.topk_ids, E), c.kind, K)
     split = moe.moe_select_split(c.kind, T, K, 2 * I, E, k, bm)
     say(f"[gpu] full size {name} T={T} block_m={bm} split={split}")
     out, (sid, eid, ntp) = moe.run_case(c, block_m=bm, split=split)
@@ -74,7 +74,8 @@ def test_full_size_modes_agree(name, T):
     """Both modes at full size on the same inputs agree on sampled tokens
     within the oracle gate."""
     c = datagen.make_workload_case(name, T, device="cuda", weights=weights(name))
-    bm = moe.moe_select_block_m(T, c.top_k, c.E, c.kind, c.K)
+    bm = moe.moe_select_block_m_routed(T, c.top_k, c.E, moe.active_experts(c.topk_ids, c.E),
+                                       c.kind, c.K)
     toks = sample_tokens(c, 3)
     ref = oracle(c, tokens=toks)
     for split in (0, 1):
