@@ -137,6 +137,29 @@ int moe_route_align(const float* logits, int64_t T, int32_t E, int32_t top_k, in
                     size_t ws_bytes, void* stream);
 
 /*
+ * The planner of moe_align / moe_align_shared (n_shared = 0 for the former)
+ * for many routes.  One workgroup plans the whole call in moe_align, which
+ * keeps every dependency a workgroup barrier; past 16,384 routes
+ * (T * (top_k + n_shared)) moe_align_ws instead plans over chunks of 1,024
+ * route ids in three launches: per-chunk expert counts, one workgroup
+ * turning them into per-chunk cursors and the padding, one wave per chunk
+ * scattering its ids in order ([hpc-ops RFC] "Design": histogram, prefix
+ * sums, row-to-token mapping).  The outputs are those of moe_align(_shared),
+ * bit for bit.
+ *   moe_align_ws_size: *bytes (host out) = workspace bytes the call needs:
+ *     0 at or below 16,384 routes (workspace unused, may be NULL), else
+ *     4 * ceil(routes / 1024) * (E + n_shared).
+ *   workspace: device memory, 16-byte aligned, contents undefined on return;
+ *     concurrent calls need separate workspaces.
+ * Errors: as moe_align / moe_align_shared, plus MOE_ERR_WORKSPACE.
+ */
+int moe_align_ws_size(int64_t T, int32_t top_k, int32_t E, int32_t n_shared, size_t* bytes);
+int moe_align_ws(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int32_t n_shared,
+                 int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
+                 int32_t* num_tokens_post_padded, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
  * Mode choice by size ([prime-flash] introduction: split=False keeps the
  * intermediate on chip and accumulates a split-K down projection into the
  * output; split=True writes the H-wide activation once and runs the down

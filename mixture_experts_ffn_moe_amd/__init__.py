@@ -28,7 +28,7 @@ import torch
 __all__ = [
     "MoeError", "lib", "LIB_PATH", "MOE_BF16", "MOE_FP8_BLOCKWISE", "MOE_MXFP8", "MOE_MXFP4",
     "moe_align_capacity", "moe_align", "moe_select_split", "moe_select_block_m",
-    "moe_select_block_m_routed",
+    "moe_select_block_m_routed", "moe_align_ws_size", "moe_align_ws",
     "moe_workspace_size", "moe_workspace_layout", "moe_ring_layout", "moe_ring_schedule",
     "fused_moe_bf16",
     "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4", "EXPORTED_SYMBOLS",
@@ -47,7 +47,7 @@ EXPORTED_SYMBOLS = (
     "fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4",
     "moe_set_timing_events", "moe_route_align_workspace_size", "moe_route_align",
     "moe_align_shared", "fused_moe_shared", "moe_ring_layout", "moe_ring_schedule",
-    "moe_select_block_m_routed",
+    "moe_select_block_m_routed", "moe_align_ws_size", "moe_align_ws",
 )
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
@@ -85,6 +85,8 @@ def lib():
     L.moe_select_split.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32,
                                    ctypes.POINTER(_I32)]
     L.moe_select_block_m.argtypes = [_I32, _I64, _I64, _I32, _I32, ctypes.POINTER(_I32)]
+    L.moe_align_ws_size.argtypes = [_I64, _I32, _I32, _I32, ctypes.POINTER(_SZ)]
+    L.moe_align_ws.argtypes = [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
     L.moe_select_block_m_routed.argtypes = [_I32, _I64, _I64, _I32, _I32, _I32,
                                             ctypes.POINTER(_I32)]
     L.moe_workspace_size.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
@@ -217,6 +219,43 @@ def moe_align_shared(topk_ids, num_experts, n_shared, block_m, stream=None, out=
     _check(lib().moe_align_shared(_ptr(topk_ids.contiguous()), T, k, num_experts, n_shared,
                                   block_m, _ptr(sorted_ids), _ptr(expert_ids), _ptr(ntp),
                                   _stream(stream)))
+    return sorted_ids, expert_ids, ntp
+
+
+def moe_align_ws_size(T, top_k, num_experts, n_shared=0):
+    out = _SZ()
+    _check(lib().moe_align_ws_size(T, top_k, num_experts, n_shared, ctypes.byref(out)))
+    return out.value
+
+
+_ALIGN_WS = {}
+
+
+def moe_align_ws(topk_ids, num_experts, block_m, n_shared=0, stream=None, out=None,
+                 workspace=None):
+    """Planner for any route count (chunked launches past 16,384 routes);
+    the outputs of moe_align / moe_align_shared.  Without ``workspace`` a
+    cached one per device is used (calls on one device run in stream order)."""
+    T, k = topk_ids.shape
+    rows, blocks = moe_align_capacity(T, k + n_shared, num_experts + n_shared, block_m)
+    dev = topk_ids.device
+    if out is not None:
+        sorted_ids, expert_ids, ntp = out
+    else:
+        sorted_ids = torch.empty(max(rows, 1), dtype=torch.int32, device=dev)[:rows]
+        expert_ids = torch.empty(max(blocks, 1), dtype=torch.int32, device=dev)[:blocks]
+        ntp = torch.empty(1, dtype=torch.int32, device=dev)
+    need = moe_align_ws_size(T, k, num_experts, n_shared)
+    if workspace is None and need:
+        ws = _ALIGN_WS.get(dev)
+        if ws is None or ws.numel() < need:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            _ALIGN_WS[dev] = ws
+        workspace = ws
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().moe_align_ws(_ptr(topk_ids.contiguous()), T, k, num_experts, n_shared, block_m,
+                              _ptr(sorted_ids), _ptr(expert_ids), _ptr(ntp), _ptr(workspace),
+                              nbytes, _stream(stream)))
     return sorted_ids, expert_ids, ntp
 
 
@@ -382,10 +421,9 @@ def run_case(case, block_m=None, split=-1, stream=None, workspace=None, out=None
         if align_out is None:
             raise ValueError("skip_align needs the align_out of an earlier call")
         align = tuple(align_out)
-    elif S:
-        align = moe_align_shared(case.topk_ids, case.E, S, block_m, stream=stream, out=align_out)
     else:
-        align = moe_align(case.topk_ids, case.E, block_m, stream=stream, out=align_out)
+        align = moe_align_ws(case.topk_ids, case.E, block_m, n_shared=S, stream=stream,
+                             out=align_out)
     args = dict(top_k=case.top_k, block_m=block_m, split=split, out=out, workspace=workspace,
                 stream=stream)
     if S:

@@ -104,6 +104,14 @@ hipError_t launch_align(const int32_t* topk_ids, int R, int E, int block_m,
                         int sorted_cap, int blocks_cap, hipStream_t stream, int T = 0,
                         int n_shared = 0);
 
+// The same plan from three launches over chunks of route ids, for many
+// routes; `counts` holds align_chunked_ws(routes, E + n_shared) bytes.
+size_t align_chunked_ws(int64_t routes, int ET);
+hipError_t launch_align_chunked(const int32_t* topk_ids, int R, int E, int block_m,
+                                int32_t* sorted, int32_t* expert_ids, int32_t* ntp,
+                                int sorted_cap, int blocks_cap, hipStream_t stream, int T,
+                                int n_shared, int* counts);
+
 // Router (softmax, top-k, renormalized weights) and planner in one launch;
 // `ticket` is one int of workspace, zero before the call and after it.
 hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int block_m,

@@ -168,3 +168,21 @@ def test_routed_heuristic():
     assert moe.moe_select_split("mxfp8", 8, 4096, 512, 32, 8, 16) == 1         # 100 MB
     assert moe.moe_select_split("bf16", 32, 512, 512, 8, 2, 16) == 0            # 6.3 MB: fused
     assert moe.moe_select_split("fp8_blockwise", 8192, 4096, 4096, 288, 8, 128) == 1
+
+
+def test_align_ws_sizes_and_errors():
+    assert moe.moe_align_ws_size(256, 6, 256) == 0                 # 1,536 routes: one workgroup
+    assert moe.moe_align_ws_size(2048, 8, 288) == 0                # 16,384: still one
+    assert moe.moe_align_ws_size(2049, 8, 288) == 4 * 17 * 288     # 16,392 routes, 17 chunks
+    assert moe.moe_align_ws_size(8192, 8, 288, 1) == 4 * 72 * 289  # 73,728 routes with a shared expert
+    L = moe.lib()
+    P = ctypes.c_void_p
+    args = (P(FAKE), 8192, 8, 288, 0, 128, P(FAKE), P(FAKE), P(FAKE))
+    assert L.moe_align_ws(*args, None, 0, None) == -5              # no workspace
+    assert L.moe_align_ws(*args, P(FAKE), 100, None) == -5         # too small
+    assert b"workspace" in L.moe_last_error()
+    assert L.moe_align_ws(*args, P(FAKE + 8), 1 << 30, None) == -4  # misaligned workspace
+    assert L.moe_align_ws(P(FAKE), 8192, 8, 2000, 0, 128, P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                          1 << 30, None) == -3                     # E > 1024
+    with pytest.raises(moe.MoeError):
+        moe.moe_align_ws_size(8, 6, 256, -1)

@@ -60,3 +60,55 @@ def test_align_repeatable():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# moe_align_ws: chunked planning past 16,384 routes (three launches over
+# chunks of 1,024 route ids), bit for bit the one-workgroup plan
+CHUNKED = [
+    ("uniform", 2049, 288, 8),      # 16,392 routes: just past the switch
+    ("masked", 8192, 288, 8),       # 65,536 routes
+    ("zipf", 4096, 384, 6),         # 24,576 routes, a few huge experts
+    ("oor", 9000, 10, 2),           # ids outside [0, E): not routes
+    ("uniform", 5000, 1024, 4),     # E = 1024, last chunk partial
+    ("one", 20000, 8, 1),           # one expert per token, 8 experts
+]
+
+
+@pytest.mark.parametrize("bm", [16, 64, 128, 256])
+@pytest.mark.parametrize("kind,T,E,k", CHUNKED)
+def test_align_chunked_bit_exact(kind, T, E, k, bm):
+    say(f"[gpu] align chunked kind={kind} T={T} E={E} k={k} bm={bm}")
+    assert moe.moe_align_ws_size(T, k, E) > 0
+    ids = _routing(kind, T, E, k, T * 7 + E)
+    s_ref, e_ref, n_ref = align_ref(ids.numpy(), E, bm)
+    # a workspace full of garbage: the chunk counts must not depend on it
+    ws = torch.full((moe.moe_align_ws_size(T, k, E),), 0x5A, dtype=torch.uint8, device="cuda")
+    s, e, n = moe.moe_align_ws(ids.cuda(), E, bm, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(n.item()) == n_ref
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(e.cpu().numpy(), e_ref)
+
+
+@pytest.mark.parametrize("S", [1, 2])
+def test_align_chunked_shared(S):
+    """Shared experts through the chunked planner equal moe_align_shared."""
+    T, E, k = 3000, 64, 6
+    ids = _routing("uniform", T, E, k, 91).cuda()
+    assert moe.moe_align_ws_size(T, k, E, S) > 0
+    a = moe.moe_align_ws(ids, E, 64, n_shared=S)
+    b = moe.moe_align_shared(ids, E, S, 64)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_align_ws_small_is_moe_align():
+    """At or below 16,384 routes moe_align_ws needs no workspace and is moe_align."""
+    ids = _routing("uniform", 256, 256, 6, 5).cuda()
+    assert moe.moe_align_ws_size(256, 6, 256) == 0
+    a = moe.moe_align_ws(ids, 256, 16)
+    b = moe.moe_align(ids, 256, 16)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
