@@ -94,8 +94,22 @@ int pick_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_
   return (T * top_k <= 512 && weight_bytes <= 32e6) ? 0 : 1;
 }
 
+// Gate/up K split over 4 workgroups per tile (split mode, 16- or 32-row
+// streaming blocks) where few (block, slice) tiles exist: at most 128 by the
+// even-spread estimate, K/128 a multiple of 8 and at least 16.  Measured
+// (MXFP8, K=4096, I=256, E=32, top-8): see the kernel.
+int pick_kw(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+            int32_t block_m, int split) {
+  if (split != 1 || block_m > 32) return 1;
+  const int64_t KS = K / 128, R = T * top_k;
+  if (KS % 8 || KS < 16) return 1;
+  const int64_t tiles = (R < E ? R : (int64_t)E) * ((N / 2) / 128);
+  (void)dtype;
+  return tiles <= 128 ? 4 : 1;
+}
+
 struct Layout {
-  size_t ctl, flags, hq, hs, yr, acc, total;
+  size_t ctl, flags, tickets, part, hq, hs, yr, acc, total;
   size_t ring_fixed, slot_bytes;  // ring mode: bytes before the ring, bytes per slot
   int64_t slots;                  // ring mode: slots of the default size
 };
@@ -137,6 +151,11 @@ Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
   if (split) {
     L.flags = off;
     off = round_up(off + R * 4, 256);
+    const int kw = pick_kw(dtype, T, K, N, E, top_k, block_m, split);
+    if (kw > 1) {  // tile tickets right after the flags (one clear)
+      L.tickets = off;
+      off = round_up(off + (size_t)blocks * (I / 128) * 4, 256);
+    }
     L.hq = off;
     off = round_up(off + (size_t)rows * I * es, 256);
     L.hs = off;
@@ -145,6 +164,10 @@ Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
     if (dtype == MOE_BF16) L.hs = L.hq;
     L.yr = off;
     off = round_up(off + R * (size_t)K * 4, 256);
+    if (kw > 1) {  // per tile and workgroup: block_m rows x 256 gate/up sums
+      L.part = off;
+      off = round_up(off + (size_t)blocks * (I / 128) * kw * block_m * 256 * 4, 256);
+    }
   } else {
     L.acc = off;
     off = round_up(off + (size_t)T * K * 4, 256);
@@ -221,6 +244,11 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
     a.hs = w + L.hs;
     a.yr = reinterpret_cast<float*>(w + L.yr);
     a.h_rows = (int)(blocks * block_m);
+    a.kw = pick_kw(dtype, T, K, N, E_all, k_all, block_m, sp);
+    if (a.kw > 1) {
+      a.tickets = reinterpret_cast<int*>(w + L.tickets);
+      a.part = reinterpret_cast<float*>(w + L.part);
+    }
     if (sp == 2) {
       a.ctl = reinterpret_cast<int*>(w + L.ctl);
       a.ring = (int)L.slots;

@@ -33,6 +33,11 @@ struct MoeArgs {
   // the ring's size in blocks (block b's intermediate lives in slot b % ring)
   int* ctl;
   int lag, ring;
+  // gate/up K split over kw workgroups (1: off): per-tile tickets (zero at
+  // launch, right after the flags) and the workgroups' gate/up sums
+  int kw;
+  int* tickets;
+  float* part;
 };
 
 // Ring mode sizing ([DeepGEMM #88] "How it works": the lag follows from the

@@ -371,10 +371,15 @@ struct BlockShape {
 // stagger of its K walk): h[mi][j] holds the
 // lane's C elements of gate/up column pair j (columns 32*wn + 16*j + l%16 of
 // the slice), rows 64*wm + 16*mi + 4*(l/16) + i.
-template <int KIND, int BM, int D, int KSPLIT>
+// RANGE: only the K steps [k0, k0 + kn), and no SwiGLU: the raw gate (ni <
+// 2) and up (ni >= 2) sums go to part[mi][ni] (K group 0 holds them).  The
+// default form is kept apart under `if constexpr`: the full-K kernels'
+// register allocation moves with any change to their code.
+template <int KIND, int BM, int D, int KSPLIT, bool RANGE = false>
 __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, uint32_t tile,
                                         const int* ids, f32x4 (&h)[BlockShape<BM>::MI][2],
-                                        float* red) {
+                                        float* red, int k0 = 0, int kn = 0,
+                                        f32x4 (*part)[4] = nullptr) {
   using B = BlockShape<BM, KSPLIT>;
   constexpr int MI = B::MI;
   constexpr int ES = KindTraits<KIND>::ES;
@@ -425,11 +430,18 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, uint32_t
     op.bsrow[1] = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + S + s) * KS;
   }
   f32x4 acc[MI][4];
-  const int k_lo = kg * KS / KSPLIT, k_hi = (kg + 1) * KS / KSPLIT;
+  int k_lo, k_hi;
+  if constexpr (RANGE) {
+    k_lo = k0 + kg * kn / KSPLIT;
+    k_hi = k0 + (kg + 1) * kn / KSPLIT;
+  } else {
+    k_lo = kg * KS / KSPLIT;
+    k_hi = (kg + 1) * KS / KSPLIT;
+  }
   bool done = false;
   if constexpr (is_mx(KIND) && scale_run<D>() == 4) {
     constexpr int W = B::THREADS / 64;
-    if (up_stage_bytes(K, MI, KSPLIT, W) > 0) {
+    if (up_stage_bytes(RANGE ? kn * 128 : K, MI, KSPLIT, W) > 0) {
       const Stage st = make_stage(k_hi - k_lo, MI, W, wid);
       const uint32_t rs = (uint32_t)(K / 32);
       auto a_row = [&](int ri) { return (uint32_t)route_token(p, ids[wm * 64 + ri]) * rs; };
@@ -469,12 +481,19 @@ __device__ __forceinline__ void up_tile(const MoeArgs& p, int e, int s, uint32_t
       }
     }
   }
+  if constexpr (RANGE) {
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int ni = 0; ni < 4; ++ni) part[mi][ni] = acc[mi][ni];
+  } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[mi][j][i] = swiglu(acc[mi][j][i], acc[mi][2 + j][i]);
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[mi][j][i] = swiglu(acc[mi][j][i], acc[mi][2 + j][i]);
+  }
 }
 
 // Requantize the tile: codes[mi][j][i] (bf16 bits or e4m3 code) and the
@@ -563,15 +582,21 @@ __device__ __forceinline__ void store_h(T* ptr, T v) {
   else *ptr = v;
 }
 
-template <int KIND, int BM, int D, int KSPLIT, bool DEV = false>
+// GIVEN: the SwiGLU tile comes in as hg (no GEMM here).
+template <int KIND, int BM, int D, int KSPLIT, bool DEV = false, bool GIVEN = false>
 __device__ __forceinline__ void up_block(const MoeArgs& p, int e, int s, uint32_t tile,
                                          size_t hrow0, const int* ids, float* lds_amax,
-                                         float* red) {
+                                         float* red, const f32x4 (*hg)[2] = nullptr) {
   using B = BlockShape<BM, KSPLIT>;
   constexpr int MI = B::MI;
   constexpr int ES = KindTraits<KIND>::ES;
   f32x4 h[MI][2];
-  up_tile<KIND, BM, D, KSPLIT>(p, e, s, tile, ids, h, red);
+  if constexpr (GIVEN) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) h[mi][0] = hg[mi][0], h[mi][1] = hg[mi][1];
+  } else {
+    up_tile<KIND, BM, D, KSPLIT>(p, e, s, tile, ids, h, red);
+  }
   uint32_t codes[MI][2][4];
   float sf[MI][4];
   int sx[MI][4];
@@ -624,6 +649,84 @@ k_up(MoeArgs p) {
   if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
   __syncthreads();
   up_block<KIND, BM, D, KSPLIT>(p, e, s, blockIdx.x, (size_t)b * BM, ids, lds_amax, red);
+}
+
+// Gate/up with K split over KW workgroups, for calls with few (block,
+// slice) tiles, where one workgroup per tile leaves most CUs idle and walks
+// all of K alone (MXFP8, K=4096, I=256, E=32, T=8: 60 tiles on 256 CUs).
+// Workgroup (t, kw) sums the K steps [kw*KS/KW, (kw+1)*KS/KW) of tile t and
+// stores the raw gate/up sums in the workspace with device-scope stores;
+// the last of the tile's workgroups to count itself in (a ticket per tile,
+// zero at launch) adds the KW sums in the order kw = 0, 1, .. and runs
+// SwiGLU, requantization and the stores of the tile.  The fixed order keeps
+// the result deterministic.
+template <int KIND, int BM, int D, int KSPLIT, int KW>
+__global__ void __launch_bounds__((BlockShape<BM, KSPLIT>::THREADS))
+k_up_sk(MoeArgs p) {
+  using B = BlockShape<BM, KSPLIT>;
+  constexpr int MI = B::MI;
+  constexpr int PER = MI * 16;  // floats per lane: a wave's gate/up sums
+  const int S = p.I / kSlice;
+  const int t = blockIdx.x / KW, kw = blockIdx.x % KW;
+  const int b = t / S, s = t % S;
+  if (b * BM >= *p.ntp) return;
+  const int e = p.expert_ids[b];
+  if ((unsigned)e >= (unsigned)p.E) return;
+  __shared__ int ids[BM];
+  __shared__ float lds_amax[4 * BM];
+  __shared__ float red[B::RED];
+  __shared__ int last;
+  if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
+  __syncthreads();
+  const int kn = p.K / 128 / KW;
+  f32x4 h[MI][2];
+  f32x4 part[MI][4];
+  up_tile<KIND, BM, D, KSPLIT, true>(p, e, s, blockIdx.x, ids, h, red, kw * kn, kn, part);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  float* const pt = p.part + (size_t)t * KW * (B::WG * PER * 64);
+  if (wid < B::WG) {  // K group 0 holds the workgroup's sums
+    float* dst = pt + ((size_t)kw * B::WG + wid) * PER * 64 + lane;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(dst + ((mi * 4 + ni) * 4 + i) * 64, part[mi][ni][i], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // the sums have been acknowledged device-wide before the ticket moves
+  asm volatile("" ::: "memory");
+  wait_vmcnt<0>();
+  asm volatile("" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) last = atomicAdd(p.tickets + t, 1) == KW - 1;
+  __syncthreads();
+  if (!last) return;
+  if (wid < B::WG) {
+    const float* src = pt + (size_t)wid * PER * 64 + lane;
+    f32x4 acc[MI][4];
+#pragma unroll
+    for (int q = 0; q < KW; ++q)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = __hip_atomic_load(src + (size_t)q * B::WG * PER * 64 +
+                                                  ((mi * 4 + ni) * 4 + i) * 64,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            acc[mi][ni][i] = q == 0 ? v : acc[mi][ni][i] + v;
+          }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[mi][j][i] = swiglu(acc[mi][j][i], acc[mi][2 + j][i]);
+  }
+  up_block<KIND, BM, D, KSPLIT, false, true>(p, e, s, 0, (size_t)b * BM, ids, lds_amax, red, h);
 }
 
 // Down GEMM of the tile (block b of expert e, output columns ct*256 ..
@@ -1053,6 +1156,22 @@ int pick_ksplit(const MoeArgs& a) {
   }
 }
 
+// Gate/up with K split over workgroups (k_up_sk): 4 workgroups per tile,
+// two K groups each (K/128 a multiple of 8; the host checks).
+constexpr int kUpKW = 4;
+template <int KIND, int BM>
+void launch_up_sk(const MoeArgs& a, hipStream_t st) {
+  constexpr int KSPLIT = 2;
+  constexpr int TH = BlockShape<BM, KSPLIT>::THREADS;
+  constexpr int D = prefetch_depth<KIND, BM, KSPLIT>();
+  constexpr int MI = BlockShape<BM, KSPLIT>::MI, W = TH / 64;
+  const int S = a.I / kSlice;
+  const size_t lds = is_mx(KIND) && scale_run<D>() == 4
+                         ? (size_t)W * up_stage_bytes(a.K / kUpKW, MI, KSPLIT, W) : 0;
+  hipLaunchKernelGGL((k_up_sk<KIND, BM, D, KSPLIT, kUpKW>),
+                     dim3((unsigned)a.blocks_cap * S * kUpKW), dim3(TH), lds, st, a);
+}
+
 template <int KIND, int BM>
 void launch_up_any(int split, const MoeArgs& a, unsigned grid, hipStream_t st) {
   if constexpr (BM <= 32) {
@@ -1137,7 +1256,17 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
     else return hipErrorInvalidValue;
   }
   if (split) {
-    const size_t fbytes = (R * 4 + 15) / 16;
+    size_t fbytes = (R * 4 + 15) / 16;
+    if (a.kw > 1) {
+      // the tile tickets follow the flags: one clear for both
+      if constexpr (BM > 32) return hipErrorInvalidValue;
+      if (a.kw != kUpKW || reinterpret_cast<uint8_t*>(a.tickets) <
+                               reinterpret_cast<uint8_t*>(a.flags) + R * 4)
+        return hipErrorInvalidValue;
+      fbytes = ((size_t)(reinterpret_cast<uint8_t*>(a.tickets) -
+                         reinterpret_cast<uint8_t*>(a.flags)) +
+                (size_t)a.blocks_cap * S * 4 + 15) / 16;
+    }
     hipLaunchKernelGGL(k_zero, dim3(grid_for(fbytes, 256)), dim3(256), 0, st,
                        reinterpret_cast<uint4*>(a.flags), fbytes);
     if (tiled_supported(KIND, BM, a.K, a.I)) {
@@ -1148,7 +1277,12 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
       return hipGetLastError();
     }
     mark(hk, 1, false, st);
-    launch_up_any<KIND, BM>(1, a, (unsigned)a.blocks_cap * S, st);
+    if constexpr (BM <= 32) {
+      if (a.kw > 1) launch_up_sk<KIND, BM>(a, st);
+      else launch_up_any<KIND, BM>(1, a, (unsigned)a.blocks_cap * S, st);
+    } else {
+      launch_up_any<KIND, BM>(1, a, (unsigned)a.blocks_cap * S, st);
+    }
     mark(hk, 1, true, st);
     const int NT = (a.K + 255) / 256;
     mark(hk, 2, false, st);

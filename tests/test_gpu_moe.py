@@ -243,3 +243,32 @@ def test_tiled_deterministic():
         b, _ = moe.run_case(c, block_m=bm, split=1)
         torch.cuda.synchronize()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("bm", [16, 32])
+@pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
+def test_k_split_over_workgroups_parity(kind, bm):
+    """Few tiles (8 experts x 2 slices) and 16 K steps: the gate/up GEMM
+    splits K over four workgroups per tile, the last adds the four sums in
+    order; against the oracle, and bitwise repeatable."""
+    c = small_case(kind, T=20, E=8, k=2, K=2048, I=256, tag="gpu-kw")
+    out, _, _ = check(c, bm, 1, label="k split over workgroups")
+    again, _ = moe.run_case(c, block_m=bm, split=1)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+
+
+def test_k_split_over_workgroups_reused_workspace():
+    """One workspace for two calls in a row, the second smaller: the tile
+    tickets are cleared by each call."""
+    a = small_case("mxfp8", T=24, E=8, k=2, K=2048, I=256, tag="gpu-kw-a")
+    b = small_case("mxfp8", T=5, E=8, k=2, K=2048, I=256, tag="gpu-kw-b")
+    need = moe.moe_workspace_size("mxfp8", 24, 2048, 512, 8, 2, 16, split=1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for c in (a, b, a):
+        out, _ = moe.run_case(c, block_m=16, split=1, workspace=ws)
+        torch.cuda.synchronize()
+        ref, _ = moe.run_case(c, block_m=16, split=1)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    check(b, 16, 1, label="k split over workgroups, second call")
