@@ -22,7 +22,8 @@ Per token count the sweep also holds per-call distributions (median, p10,
 p90 of event pairs around each call): the whole call and the forward alone
 (planner outputs reused), back to back ("warm"), and the whole call with a
 1 GiB read before each call outside its events ("cold": L2 and the 256 MB
-MALL hold other, clean lines).  The line records the GPU clocks (from sysfs) and two
+MALL hold other, clean lines), and the whole call captured once in a HIP
+graph and replayed ("graph_warm": launch gaps gone, as in a decode loop).  The line records the GPU clocks (from sysfs) and two
 measured reference ceilings beside the spec peaks: a plain device copy, a
 read-only sum, and a large e4m3 GEMM through the vendor BLAS.
 
@@ -327,6 +328,26 @@ def per_call(torch, fn, n, stream, flush=None):
     return percentiles([a.elapsed_time(b) * 1e3 for a, b in evs])
 
 
+def graph_leg(torch, step, calls, stream):
+    """The whole call (planner + forward) captured once in a HIP graph
+    (torch.cuda.CUDAGraph over the same C ABI calls, which allocate nothing
+    and never synchronize) and replayed: per-replay event pairs.  What a
+    decode loop that replays a captured step pays per call."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    res = per_call(torch, g.replay, calls, stream)
+    del g
+    return res
+
+
 def gpu_clocks():
     """Current shader and memory clocks from the amdgpu sysfs DPM tables (the
     level marked with '*'); None where the files are absent.  Read directly:
@@ -537,6 +558,7 @@ def main():
         if args.calls:
             prot["full_warm"] = per_call(torch, step, args.calls, stream)
             prot["op_warm"] = per_call(torch, op_only, args.calls, stream)
+            prot["graph_warm"] = graph_leg(torch, step, args.calls, stream)
         if args.cold_calls:
             # a read, not a write: written scratch would leave the caches
             # dirty, and the call would pay for writing it back
