@@ -27,6 +27,11 @@
  *   device and never copies between host and device.
  * - The caller allocates and owns every buffer, including the workspace.  The
  *   library allocates no device memory and keeps no state between calls.
+ * - So a planner + forward sequence can be captured into a HIP graph on a
+ *   capturing stream and replayed: every clear the library does is a kernel,
+ *   not a memset node.  A replay reads whatever the captured buffers hold at
+ *   that time (new routing, new tokens); it keeps the captured sizes
+ *   (T, block_m, mode) and pointers.
  * - Return value: MOE_OK (0) or a negative moe_status.  All argument checks
  *   run on the host BEFORE anything is enqueued, so on an error nothing has
  *   been launched.  moe_last_error() returns a message for the last failing
