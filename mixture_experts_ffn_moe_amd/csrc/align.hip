@@ -14,8 +14,9 @@
 //   2. per expert: total count, block-padded count, exclusive prefix sum over
 //      experts (expert order ascending), and each wave's starting position
 //      inside the expert's segment (earlier waves first);
-//   3. padding slots of each segment and the tail up to the capacity get -1,
-//      expert_ids gets the owner of each block (-1 past the last block);
+//   3. expert_ids gets the owner of each block (-1 past the last block); every
+//      slot of sorted_token_ids was set to -1 with the histogram clear, so
+//      the padding needs no pass of its own;
 //   4. each wave walks its share in order, 64 ids at a time; lanes holding
 //      the same expert find each other with ballots over the expert id's
 //      bits, take consecutive slots in lane order, and the last of them
@@ -61,18 +62,25 @@ __device__ __forceinline__ void align_body(const int32_t* __restrict__ ids, int 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   for (int i = tid; i < kWaves * E; i += kThreads) cnt[i] = 0;
+  // every slot starts as padding; the scatter below (after several barriers)
+  // overwrites the slots that hold a route
+  for (int q = tid; q < sorted_cap; q += kThreads) sorted[q] = -1;
   __syncthreads();
 
   const int seg = (R + kWaves - 1) / kWaves;
   const int lo = min(R, w * seg), hi = min(R, lo + seg);
   // ids are read kBatch chunks of 64 at a time so that the global loads
-  // overlap instead of costing one memory latency per chunk
+  // overlap instead of costing one memory latency per chunk; a wave whose
+  // share is one batch keeps it in registers for the scatter
+  const bool one = hi - lo <= 64 * kBatch;
+  int keep[kBatch];
   for (int base = lo; base < hi; base += 64 * kBatch) {
     int eb[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = base + u * 64 + lane;
       eb[u] = i < hi ? expert_of(i) : -1;
+      keep[u] = eb[u];
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
@@ -119,12 +127,10 @@ __device__ __forceinline__ void align_body(const int32_t* __restrict__ ids, int 
       cnt[v * E + e] = run;
       run += c;
     }
-    // padding inside the segment and the expert of each block
+    // the expert of each block (the padding slots were filled at the start)
     const int pend = off[e] + (tot[e] + bm - 1) / bm * bm;
-    for (int q = off[e] + tot[e]; q < pend; ++q) sorted[q] = -1;
     for (int q = off[e] / bm; q < pend / bm; ++q) expert_ids[q] = e;
   }
-  for (int q = ntp + tid; q < sorted_cap; q += kThreads) sorted[q] = -1;
   for (int q = ntp / bm + tid; q < blocks_cap; q += kThreads) expert_ids[q] = -1;
   if (tid == 0) *ntp_out = ntp;
   __syncthreads();
@@ -136,7 +142,7 @@ __device__ __forceinline__ void align_body(const int32_t* __restrict__ ids, int 
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = base0 + u * 64 + lane;
-      eb[u] = i < hi ? expert_of(i) : -1;
+      eb[u] = one ? keep[u] : i < hi ? expert_of(i) : -1;
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
