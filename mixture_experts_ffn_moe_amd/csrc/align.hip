@@ -180,7 +180,8 @@ k_align(const int32_t* __restrict__ ids, int R, int E, int bm, int32_t* __restri
 // kChunk consecutive route ids (one workgroup runs the steps above in
 // 8.8 us for 1,536 routes but 165 us for 65,536): per-chunk expert counts;
 // one workgroup turns them into per-chunk cursors (segment start plus the
-// counts of earlier chunks) and writes the padding; one wave per chunk then
+// counts of earlier chunks) and the block owners (the count launch has set
+// every slot to -1); one wave per chunk then
 // scatters its ids in order.  Chunks are contiguous and taken in order, so
 // the result is the one-workgroup plan, bit for bit.  counts: C * ET ints
 // of workspace, C = ceil(routes / kChunk).
@@ -188,11 +189,16 @@ k_align(const int32_t* __restrict__ ids, int R, int E, int bm, int32_t* __restri
 
 constexpr int kChunk = 1024;
 
+// Also sets its share of sorted_token_ids to -1 (the padding; the scatter
+// overwrites the slots that hold a route).
 __global__ void __launch_bounds__(256)
 k_align_count(const int32_t* __restrict__ ids, int R_routed, int E_routed, int T, int S,
-              int* __restrict__ counts) {
+              int* __restrict__ counts, int32_t* __restrict__ sorted, int sorted_cap) {
   extern __shared__ int h[];
   const int ET = E_routed + S, R = R_routed + T * S;
+  const int share = (sorted_cap + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int f_lo = (int)blockIdx.x * share, f_hi = min(sorted_cap, f_lo + share);
+  for (int q = f_lo + (int)threadIdx.x; q < f_hi; q += 256) sorted[q] = -1;
   for (int e = threadIdx.x; e < ET; e += 256) h[e] = 0;
   __syncthreads();
   const int lo = blockIdx.x * kChunk, hi = min(R, lo + kChunk);
@@ -265,12 +271,13 @@ k_align_plan(int ET, int C, int bm, int* __restrict__ counts, int32_t* __restric
       counts[(size_t)c * ET + e] = run;
       run += t;
     }
-    // run is now the end of the expert's routes; pad to the block
+    // run is now the end of the expert's routes; its blocks (the padding
+    // slots were set to -1 by the count launch)
     const int pend = off[e] + (run - off[e] + bm - 1) / bm * bm;
-    for (int q = run; q < pend; ++q) sorted[q] = -1;
     for (int q = off[e] / bm; q < pend / bm; ++q) expert_ids[q] = e;
   }
-  for (int q = ntp + tid; q < sorted_cap; q += kThreads) sorted[q] = -1;
+  if (C == 0)  // no count launch ran
+    for (int q = tid; q < sorted_cap; q += kThreads) sorted[q] = -1;
   for (int q = ntp / bm + tid; q < blocks_cap; q += kThreads) expert_ids[q] = -1;
   if (tid == 0) *ntp_out = ntp;
 }
@@ -506,7 +513,7 @@ hipError_t launch_align_chunked(const int32_t* topk_ids, int R, int E, int block
   const size_t hsm = (size_t)ET * sizeof(int);
   if (C > 0)
     hipLaunchKernelGGL(k_align_count, dim3(C), dim3(256), hsm, stream, topk_ids, R, E, T,
-                       n_shared, counts);
+                       n_shared, counts, sorted, sorted_cap);
   hipLaunchKernelGGL(k_align_plan, dim3(1), dim3(kThreads), hsm, stream, ET, C, block_m, counts,
                      sorted, expert_ids, ntp, sorted_cap, blocks_cap);
   if (C > 0)
