@@ -145,15 +145,16 @@ int moe_route_align(const float* logits, int64_t T, int32_t E, int32_t top_k, in
  * The planner of moe_align / moe_align_shared (n_shared = 0 for the former)
  * for many routes.  One workgroup plans the whole call in moe_align, which
  * keeps every dependency a workgroup barrier; past 16,384 routes
- * (T * (top_k + n_shared)) moe_align_ws instead plans over chunks of 1,024
- * route ids in three launches: per-chunk expert counts, one workgroup
- * turning them into per-chunk cursors and the padding, one wave per chunk
+ * (T * (top_k + n_shared)) moe_align_ws instead plans over chunks of 512
+ * route ids in three launches: per-chunk expert counts (which also set the
+ * output to -1), one workgroup turning them into per-chunk cursors and the
+ * block owners, one wave per chunk
  * scattering its ids in order ([hpc-ops RFC] "Design": histogram, prefix
  * sums, row-to-token mapping).  The outputs are those of moe_align(_shared),
  * bit for bit.
  *   moe_align_ws_size: *bytes (host out) = workspace bytes the call needs:
  *     0 at or below 16,384 routes (workspace unused, may be NULL), else
- *     4 * ceil(routes / 1024) * (E + n_shared).
+ *     4 * ceil(routes / 512) * (E + n_shared).
  *   workspace: device memory, 16-byte aligned, contents undefined on return;
  *     concurrent calls need separate workspaces.
  * Errors: as moe_align / moe_align_shared, plus MOE_ERR_WORKSPACE.

@@ -187,7 +187,7 @@ k_align(const int32_t* __restrict__ ids, int R, int E, int bm, int32_t* __restri
 // of workspace, C = ceil(routes / kChunk).
 // ---------------------------------------------------------------------------
 
-constexpr int kChunk = 1024;
+constexpr int kChunk = 512;
 
 // Also sets its share of sorted_token_ids to -1 (the padding; the scatter
 // overwrites the slots that hold a route).

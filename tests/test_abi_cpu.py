@@ -173,8 +173,8 @@ def test_routed_heuristic():
 def test_align_ws_sizes_and_errors():
     assert moe.moe_align_ws_size(256, 6, 256) == 0                 # 1,536 routes: one workgroup
     assert moe.moe_align_ws_size(2048, 8, 288) == 0                # 16,384: still one
-    assert moe.moe_align_ws_size(2049, 8, 288) == 4 * 17 * 288     # 16,392 routes, 17 chunks
-    assert moe.moe_align_ws_size(8192, 8, 288, 1) == 4 * 72 * 289  # 73,728 routes with a shared expert
+    assert moe.moe_align_ws_size(2049, 8, 288) == 4 * 33 * 288     # 16,392 routes, 33 chunks of 512
+    assert moe.moe_align_ws_size(8192, 8, 288, 1) == 4 * 144 * 289  # 73,728 routes with a shared expert
     L = moe.lib()
     P = ctypes.c_void_p
     args = (P(FAKE), 8192, 8, 288, 0, 128, P(FAKE), P(FAKE), P(FAKE))
