@@ -19,8 +19,9 @@ import torch
 
 import datagen
 from oracle import codecs
-from oracle.moe import (ABS_BAND, REL_BAND, moe_ref, requant_blockwise, requant_bf16, requant_mx,
-                        tolerance_check)
+from oracle.moe import (LAMBDA, _flip_prob, _requant_blockwise, _requant_mx, _silu, gemm_sigma,
+                        moe_ref, requant_blockwise, requant_bf16, requant_mx, route_flip_bound,
+                        swiglu_band, tolerance_check)
 
 HERE = os.path.dirname(__file__)
 
@@ -297,8 +298,62 @@ def test_token_subset_matches_full():
 
 
 # ---------------------------------------------------------------------------
-# near-tie allowance
+# arithmetic model and near-tie allowance
 # ---------------------------------------------------------------------------
+
+def test_gemm_sigma_closed_form():
+    """sigma_G = sqrt(KAPPA^2 Q + (u sqrt(steps + 2) (|G| + 3 sqrt Q))^2),
+    worked by hand for all-ones operands: Q = K, G = K."""
+    u = 2.0 ** -24
+    for kind, K, kappa, block in (("fp8_blockwise", 256, 2.0 ** -15, 128),
+                                  ("mxfp8", 4096, 2.0 ** -15, 128),
+                                  ("bf16", 512, 2.0 ** -24, 32)):
+        a = np.ones((1, K))
+        b = np.ones((1, K))
+        got = gemm_sigma(kind, a, b, a @ b.T)[0, 0]
+        chain = u * math.sqrt(K / block + 2) * (K + 3 * math.sqrt(K))
+        want = math.sqrt((kappa * math.sqrt(K)) ** 2 + chain ** 2)
+        assert got == pytest.approx(want, rel=1e-12), kind
+
+
+def test_gemm_sigma_grows_like_sqrt_k():
+    """Random operands: the instruction term scales with sqrt(K) (the 2-norm
+    of the K products), so quadrupling K doubles it."""
+    rng = np.random.default_rng(3)
+    a = rng.normal(size=(4, 4096))
+    b = rng.normal(size=(3, 4096))
+    s1 = gemm_sigma("fp8_blockwise", a[:, :1024], b[:, :1024], a[:, :1024] @ b[:, :1024].T)
+    s4 = gemm_sigma("fp8_blockwise", a, b, a @ b.T)
+    assert 1.7 < np.median(s4 / s1) < 2.3
+
+
+def test_swiglu_band_first_order():
+    """With a tiny GEMM deviation the band is LAMBDA times the propagated
+    standard deviation: silu'(g) |up| sigma_g and silu(g) sigma_u add in
+    quadrature (silu' checked against a centred difference of silu), plus
+    the fp32 evaluation term (|g| + 6) u |h|."""
+    g = np.array([[-6.0, -1.3, 0.0, 0.7, 2.4, 9.0]])
+    v = np.array([[1.5, -2.0, 0.5, 3.0, -0.25, 1.0]])
+    G = np.concatenate([g, v], axis=1)
+    eps = 1e-9
+    sG = np.full(G.shape, eps)
+    h, band = swiglu_band(G, sG, g.shape[1])
+    d = 1e-6
+    dsilu = (_silu(g + d) - _silu(g - d)) / (2 * d)
+    want = LAMBDA * np.sqrt((dsilu * v * eps) ** 2 + (_silu(g) * eps) ** 2) + \
+        (np.abs(g) + 6) * 2.0 ** -24 * np.abs(h)
+    np.testing.assert_allclose(h, _silu(g) * v, rtol=1e-15)
+    np.testing.assert_allclose(band, want, rtol=1e-6)
+
+
+def test_flip_prob_closed_forms():
+    """A boundary at the kernel value's own position is crossed half the
+    time; one at LAMBDA standard deviations with the Gaussian tail
+    Phi(-LAMBDA) = erfc(LAMBDA / sqrt 2) / 2."""
+    assert _flip_prob(0.0, 1.0) == pytest.approx(0.5)
+    assert _flip_prob(1.0, 1.0) == pytest.approx(0.5 * math.erfc(LAMBDA / math.sqrt(2)), rel=1e-9)
+    assert _flip_prob(0.5, 1.0) == pytest.approx(0.5 * math.erfc(LAMBDA / 2 / math.sqrt(2)), rel=1e-9)
+
 
 def test_near_tie_alt_blockwise():
     """h = 2 sets sf_inv = 224 - 2^-16 (see the blockwise golden); an element
@@ -309,69 +364,136 @@ def test_near_tie_alt_blockwise():
     h[0, 0] = 2.0
     h[0, 1] = 368.0 / sf_inv * (1 + 1e-7)       # a hair above the midpoint
     h[0, 2] = (352.0 + 0.3 * 32) / sf_inv       # 30% into the step: clear
-    q, s, hd, alt = requant_blockwise(h)
+    band = np.full(h.shape, 1e-6)
+    q, s, hd, alt = requant_blockwise(h, band)
     sf = float(s[0, 0])
     assert q[0, 1] == 0x7C                      # 384: rounds up
     assert alt[0, 1] == pytest.approx(32 * sf)
     assert alt[0, 2] == 0.0
     assert alt[0, 0] == 0.0                     # the amax element is 448, exact
-    # near zero the absolute band (448 * 2^-16 in scaled units) reaches the
-    # smallest subnormal codes: the allowance there is about that band
-    assert 0 <= alt[0, 100] <= (448.0 * ABS_BAND + 2.0 ** -9) * sf
+    # with no GEMM deviation the fp32 roundings of sf, 1/sf and the product
+    # (4 u relative) still reach a boundary 1e-7 away, but not 0.3 steps
+    alt0 = requant_blockwise(h)[3]
+    assert alt0[0, 1] == pytest.approx(32 * sf) and alt0[0, 2] == 0.0
+    # the probability of the near-tie element is close to one half (the
+    # boundary lies a small fraction of the band away)
+    *_, prob, _, _ = _requant_blockwise(h, band)
+    assert 0.3 < prob[0, 1] < 0.5 and prob[0, 2] == 0.0
 
 
 def test_near_tie_alt_mx_scale():
-    """amax a hair below a power of two: the shared exponent itself is a
-    near-tie and the allowance covers the other exponent's result."""
-    h = np.zeros((1, 32))
-    h[0, 0] = 4.0 * (1 - 1e-6)
+    """amax a hair below a power of two, band reaching past it: the shared
+    exponent is a near-tie; the group's move under the other exponent is the
+    exact difference of the two dequantized groups."""
+    h = np.zeros((1, 64))
+    h[0, 0] = 4.0 * (1 - 1e-7)
     h[0, 1] = 1.3
-    q, s, hd, alt = requant_mx(h)
-    assert s[0, 0] == 127 + 1 - 8               # floor(log2 3.999996) = 1
-    # with exponent -7 the amax element saturates (511.99 -> 448, 3.5) while
-    # exponent -6 gives 256 (4.0): the allowance covers that 0.5
-    assert alt[0, 0] == pytest.approx(0.5)
-    # a normal element lands on the same value under either exponent (the
-    # e4m3 grid is invariant under power-of-two scaling), so no allowance
-    assert alt[0, 1] == 0.0
-    h[0, 0] = 3.0
-    q, s, hd, alt = requant_mx(h)
-    assert alt[0, 0] == 0.0
+    h[0, 33] = 3.0                              # second group: exponent clear
+    band = np.full(h.shape, 1e-5)
+    q, s, hd, alt, prob, _, (moved, dhd, alt2, gprob) = _requant_mx(h, band)
+    assert s[0, 0] == 127 + 1 - 8               # floor(log2 3.9999996) = 1
+    assert moved[0, 0] and not moved[0, 1]
+    # exponent -6 (amax 4 reaches 2^2): 3.9999996 * 64 -> 256, 1.3 * 64 = 83.2 -> 80
+    assert dhd[0, 0] == pytest.approx(4.0 - 448.0 / 128.0)  # 4 against 3.5 (saturated)
+    assert dhd[0, 1] == pytest.approx(80.0 / 64.0 - 1.25)   # 1.25 under both
+    assert np.all(dhd[0, 32:] == 0)
+    assert 0.0 < gprob[0, 0] <= 0.5 and gprob[0, 1] == 0.0
+    # public wrapper: the move is part of alt
+    assert requant_mx(h, band)[3][0, 0] == pytest.approx(0.5)
 
 
 def test_near_tie_alt_bf16():
     h = np.zeros((1, 128))
     h[0, 0] = 1.0
     h[0, 1] = 0.5 + 2.0 ** -9                   # midpoint (bf16 spacing at 0.5 is 2^-8)
-    h[0, 2] = 0.5 + 2.0 ** -10                  # 2^-10 from the midpoint, band ~2^-14
-    _, _, hd, alt = requant_bf16(h)
+    h[0, 2] = 0.5 + 2.0 ** -10                  # 2^-10 from the midpoint, band 2^-14
+    band = np.full(h.shape, 2.0 ** -14)
+    _, _, hd, alt = requant_bf16(h, band)
     assert alt[0, 1] == pytest.approx(2.0 ** -8)
     assert alt[0, 2] == 0.0
 
 
+def test_route_flip_bound_closed_forms():
+    """One near-tie: its effect alt |w2_ci| exactly.  Two: min(sum, max + 3
+    sqrt(p1 e1^2 + p2 e2^2)), worked by hand.  400 equal decisions taken with
+    certainty: max + 3 * sqrt(400) = 61 times one effect (a random walk), below
+    their sum (400)."""
+    w2 = np.array([[1.0, -2.0, 0.5], [0.25, 4.0, -1.0]])   # K = 2, I = 3
+    alt = np.array([[0.0, 0.1, 0.0]])
+    prob = np.array([[0.0, 0.4, 0.0]])
+    np.testing.assert_allclose(route_flip_bound(alt, prob, w2)[0], [0.2, 0.4])
+    alt = np.array([[0.3, 0.1, 0.0]])
+    prob = np.array([[0.5, 0.02, 0.0]])
+    e = np.array([[0.3 * 1.0, 0.1 * 2.0], [0.3 * 0.25, 0.1 * 4.0]])  # [col][decision]
+    want = [min(e[c].sum(), e[c].max() + 3 * math.sqrt(0.5 * e[c, 0] ** 2 + 0.02 * e[c, 1] ** 2))
+            for c in range(2)]
+    np.testing.assert_allclose(route_flip_bound(alt, prob, w2)[0], want)
+    w2 = np.ones((1, 400))
+    alt = np.full((1, 400), 0.01)
+    got = route_flip_bound(alt, np.ones((1, 400)), w2)[0, 0]
+    assert got == pytest.approx(0.61)
+
+
+def test_route_flip_bound_mx_group_exact():
+    """An MX group whose exponent is a near-tie is one decision: the kernel
+    taking the other exponent (its amax nudged across the power of two,
+    within the band) changes the down GEMM's outputs by at most the bound;
+    the group term is what covers it (the element near-ties alone do not)."""
+    rng = np.random.default_rng(8)
+    h = rng.normal(0, 0.6, (1, 64))
+    h[0, 5] = 4.0 * (1 - 1e-7)                  # group 0: amax just below 4
+    band = np.full(h.shape, 1e-6)
+    w2 = rng.normal(0, 1, (48, 64))
+    q, s, hd, alt, prob, _, groups = _requant_mx(h, band)
+    assert groups[0][0, 0]
+    bound = route_flip_bound(alt, prob, w2, groups)[0]
+    hk = h.copy()
+    hk[0, 5] = 4.0 * (1 + 1e-7)                 # the kernel's h: across 4
+    hd_k = requant_mx(hk)[2]
+    moved = np.abs((hd_k - hd) @ w2.T)[0]
+    assert np.max(moved) > 0.05
+    assert np.all(moved <= bound + 1e-12)
+    no_group = route_flip_bound(alt, prob, w2, None)[0]
+    assert np.any(moved > no_group)
+
+
 @pytest.mark.parametrize("kind,K,I,T", [("fp8_blockwise", 512, 384, 600), ("mxfp8", 256, 256, 300),
                                         ("bf16", 256, 256, 300)])
-def test_flip_bound_covers_fp32_deviation(kind, K, I, T):
-    """Soundness of the allowance: perturb h by relative noise of the size a
-    kernel's fp32 summation leaves (4e-5, twice the deviations measured on the
-    GPU) and requantize.  The perturbed outputs pass the gate with the
-    allowance; for the blockwise case the strict bound alone fails (so the
-    near-ties are real and the allowance is what covers them)."""
+def test_allowance_covers_model_deviation(kind, K, I, T):
+    """Soundness of the allowance: move h by a deviation of the model's size
+    (normal, standard deviation band / LAMBDA) and requantize.  The moved
+    outputs pass the gate with the allowance; for the blockwise case some
+    codes flip and the strict bound alone fails (so the near-ties are real
+    and the allowance is what covers them)."""
     d = small_case(kind, T, K, I, 8, 4, routing="uniform", seed="tie")
     base = run(d)
     rng = np.random.default_rng(1)
 
-    def perturb(h):
-        return h * (1 + rng.uniform(-1, 1, h.shape) * 4e-5)
+    def perturb(h, band):
+        return h + rng.normal(size=h.shape) * band / LAMBDA
 
     moved = run(d, h_perturb=perturb)
     tol = 2e-2 if kind != "bf16" else 5e-3
     got = codecs.bf16_encode(moved["out64"])
-    ok, stats = tolerance_check(got, base["out64"], tol, base["flip_bound"])
+    ok, stats = tolerance_check(got, base["out64"], tol, base["allowance"])
     assert ok, stats
     if kind == "fp8_blockwise":
         _, strict = tolerance_check(got, base["out64"], tol, None)
         assert strict["n_over_bound"] > 0
+
+
+def test_allowance_covers_band_edge_deviation():
+    """Harder than the model: every element of h moved by up to its whole
+    band (uniform in [-band, band]), so a large share of the flagged
+    decisions flip; the gate still accepts."""
+    for kind in ("fp8_blockwise", "mxfp8"):
+        d = small_case(kind, 200, 512, 256, 8, 4, routing="uniform", seed="edge")
+        base = run(d)
+        rng = np.random.default_rng(2)
+        moved = run(d, h_perturb=lambda h, band: h + rng.uniform(-1, 1, h.shape) * band)
+        ok, stats = tolerance_check(codecs.bf16_encode(moved["out64"]), base["out64"], 2e-2,
+                                    base["allowance"])
+        assert ok, (kind, stats)
 
 
 def test_mxfp4_equals_mxfp8_on_exact_reencoding():
