@@ -1,22 +1,29 @@
 """Benchmark of the fused MoE expert-FFN forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME[:T1/T2],...]
                     [--tokens 8,64,256] [--no-cpu-baseline]
 
 A step is one whole forward on one batch: the planner (moe_align) and the
 fused expert FFN (gather, gate/up GEMM, SwiGLU + requantization, down GEMM,
 top-k weighted combine), inputs resident in HBM, on synthetic seeded data of
 the workload's shapes (random-init weights; no trained checkpoint exists
-here).  Every token count of the workload is timed; the JSON line's ``value``
-is the largest one's throughput and ``sweep`` lists all of them.
+here).  By default two workloads run: blockwise FP8 K=4096, I=2048, E=256,
+top-6 at T = 8, 64 and 256 (the weight-stream-bound decode sizes), then
+blockwise FP8 K=4096, I=2048, E=288, top-8 at T = 8192, the largest
+single-GPU configuration, whose throughput, configuration and roofline make
+the JSON line's headline (``value``, ``config``, ``roofline``); ``sweep``
+lists every point.
 
 Throughput: algorithmic FLOPs 6 * R * K * I per step (R = routes to local
-experts; padding rows do not count) over the step time.  Roofline: the
-dominant kernel (the fused kernel in fused mode, the gate/up kernel in split
-mode, the persistent kernel in ring mode, ``--split 2``) is timed with HIP
-events recorded around it on its own stream, and its
-algorithmic HBM bytes (weights and scales of the experts it reads once, the
-token rows, its outputs) are divided by that time.
+experts; padding rows do not count) over the step time.  Roofline, per point
+and for the headline: the dominant kernel (the gate/up kernel in split mode,
+``k_up`` streaming or ``k_up_t`` LDS-tiled; the fused kernel in fused mode;
+the persistent kernel in ring mode) is timed with HIP events recorded around
+it on its own stream; its algorithmic FLOPs (4 * R * K * I for the gate/up
+GEMM) and HBM bytes (weights and scales of the experts it reads once, the
+token rows, its outputs) give its binding roof max(F / MFMA peak, B / HBM
+peak), and t_roof / t_measured is the fraction of that roof reached.  The
+whole step gets the same figure from its own FLOPs and bytes.
 
 Per token count the sweep also holds per-call distributions (median, p10,
 p90 of event pairs around each call): the whole call and the forward alone
@@ -27,8 +34,8 @@ graph and replayed ("graph_warm": launch gaps gone, as in a decode loop).  The l
 measured reference ceilings beside the spec peaks: a plain device copy, a
 read-only sum, and a large e4m3 GEMM through the vendor BLAS.
 
-The CPU baseline runs the fp64 oracle on a bounded sample of the same
-workload (a few tokens of the largest token count) on the host cores.
+The CPU baseline runs the fp64 oracle on a bounded sample of the headline
+workload (a few tokens of its batch) on the host cores.
 """
 
 import argparse
@@ -47,8 +54,9 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8_blockwise": 5000.0, "mxfp8": 5000.0, "m
 DTYPE_NAME = {"bf16": "bf16", "fp8_blockwise": "e4m3/fp32-blockwise", "mxfp8": "e4m3/e8m0-mx",
               "mxfp4": "e2m1/e8m0-mx weights x e4m3/e8m0-mx activations"}
 METRIC = ("fused MoE fwd µs and TFLOP/s (% FP8 MFMA / % HBM roofline) vs tokens T")
-KERNEL_SOURCES = ["mixture_experts_ffn_moe_amd/csrc/moe_kernels.hip",
-                  "mixture_experts_ffn_moe_amd/csrc/device.h"]
+CSRC = "mixture_experts_ffn_moe_amd/csrc"
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(os.path.join(ROOT, CSRC))
+                        if f.endswith((".hip", ".h")))
 
 
 class HipEvents:
@@ -144,6 +152,7 @@ COUNTER_RUNS = [
     ("up", "fp8-k4096-i2048-e256-top6", 256, ("k_up", "k_down")),
     ("fused", "fp8-k4096-i2048-e256-top6", 8, ("k_fused",)),
     ("up4", "mxfp4-k4096-i2048-e256-top6", 256, ("k_up", "k_down")),
+    ("tiled", "fp8-k4096-i2048-e288-top8", 8192, ("k_up_t", "k_down_t")),
 ]
 
 
@@ -423,77 +432,62 @@ def measured_ceilings(torch):
     return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="fp8-k4096-i2048-e256-top6")
-    ap.add_argument("--tokens", default=None, help="comma list; default: the workload's")
-    ap.add_argument("--block-m", type=int, default=None)
-    ap.add_argument("--split", type=int, default=-1)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=40)
-    ap.add_argument("--calls", type=int, default=200,
-                    help="per-call timed calls (warm) for the median / p10 / p90")
-    ap.add_argument("--cold-calls", type=int, default=50,
-                    help="per-call timed calls with a 1 GiB read before each (cold caches)")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
-                    help="only run 5 plain device copies of MIB MiB (counter calibration)")
-    ap.add_argument("--summarize-counters", default=None, metavar="DIR",
-                    help="only write profiles/hbm_traffic.json from the counter runs under DIR")
-    args = ap.parse_args()
+DEFAULT_WORKLOADS = "fp8-k4096-i2048-e256-top6,fp8-k4096-i2048-e288-top8:8192"
 
-    if args.summarize_counters:
-        summarize_counters(args.summarize_counters)
-        return
 
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the fused MoE forward here runs on one GPU's local "
-              "experts with no collectives; --gpus must be 1.", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    if args.calibrate_copy:
-        # a plain copy of known size: each launch reads and writes exactly
-        # MIB MiB, which calibrates the HBM byte counters of a profiler
-        n = args.calibrate_copy << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
-        return
-
+def parse_workloads(arg, tokens):
+    """'name[:T1/T2..],..' -> [(name, [T..])]; --tokens overrides every list."""
     import datagen
-    import mixture_experts_ffn_moe_amd as moe
+    out = []
+    for part in arg.split(","):
+        name, _, ts = part.partition(":")
+        if tokens:
+            ts_list = [int(t) for t in tokens.split(",")]
+        elif ts:
+            ts_list = [int(t) for t in ts.split("/")]
+        else:
+            ts_list = list(datagen.WORKLOADS[name]["tokens"])
+        out.append((name, ts_list))
+    return out
 
-    spec = datagen.WORKLOADS[args.workload]
+
+def dominant(kind, bm, split, K, I):
+    """Name and kind of the kernel that streams the gate/up weights."""
+    if split == 0:
+        return "k_fused"
+    if split == 2:
+        return "k_ring"
+    tiled = kind in ("fp8_blockwise", "mxfp8") and bm >= 64 and K % 256 == 0 and I % 128 == 0
+    return "k_up_t" if tiled else "k_up"
+
+
+def roof(flops, nbytes, us, kind):
+    """Binding roof of a kernel or step: (bound, t_roof us, frac = t_roof / t)."""
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[kind] * 1e12) * 1e6
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9) * 1e6
+    bound = "mfma" if t_mfma > t_hbm else "hbm"
+    t = max(t_mfma, t_hbm)
+    return bound, t, t / us
+
+
+def run_workload(args, torch, moe, datagen, name, tokens, dev, stream):
+    spec = datagen.WORKLOADS[name]
     kind, K, I, E, k = spec["kind"], spec["K"], spec["I"], spec["E"], spec["top_k"]
     N = 2 * I
-    tokens = ([int(t) for t in args.tokens.split(",")] if args.tokens else list(spec["tokens"]))
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    moe.lib()
-    print(f"[bench] generating {args.workload} weights on the GPU", file=sys.stderr, flush=True)
-    weights = datagen.make_weights(kind, K, I, E, device=dev, tag=args.workload,
-                                   w_std=spec.get("w_std"))
+    print(f"[bench] generating {name} weights on the GPU", file=sys.stderr, flush=True)
+    weights = datagen.make_weights(kind, K, I, E, device=dev, tag=name, w_std=spec.get("w_std"))
     torch.cuda.synchronize()
     # one shared expert of the same format, stored after the routed ones
     shared_w = None
     if args.calls:
-        sw = datagen.make_weights(kind, K, I, 1, device=dev, tag=args.workload + "/shared",
+        sw = datagen.make_weights(kind, K, I, 1, device=dev, tag=name + "/shared",
                                   w_std=spec.get("w_std"))
         shared_w = (sw, [None if a is None else torch.cat([a, b]) for a, b in zip(weights, sw)])
         torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
     sweep = []
-    last_case = None
+    case = None
     for T in tokens:
-        case = datagen.make_workload_case(args.workload, T, device=dev, weights=weights)
+        case = datagen.make_workload_case(name, T, device=dev, weights=weights)
         ids = case.topk_ids
         valid = (ids >= 0) & (ids < E)
         R = int(valid.sum().item())
@@ -531,23 +525,30 @@ def main():
         hev.close()
         flops = 6.0 * R * K * I
         step_bytes, dom_bytes = byte_model(kind, K, I, E_act, T, R, split)
-        kname = {0: "k_fused", 1: "k_up", 2: "k_ring"}[split]
+        kname = dominant(kind, bm, split, K, I)
+        dom_flops = flops if split != 1 else 4.0 * R * K * I    # gate/up GEMM alone
         mode = {0: "fused", 1: "split", 2: "ring"}[split]
+        s_bound, s_troof, s_frac = roof(flops, step_bytes, ms * 1e3, kind)
+        d_bound, d_troof, d_frac = roof(dom_flops, dom_bytes, kms * 1e3, kind)
         sweep.append({
-            "T": T, "routes": R, "active_experts": E_act, "block_m": bm,
+            "workload": name, "T": T, "routes": R, "active_experts": E_act, "block_m": bm,
             "mode": mode,
             "us_per_step": ms * 1e3, "tflops": flops / (ms * 1e-3) / 1e12,
             "pct_mfma_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS[kind],
             "step_gbs": step_bytes / (ms * 1e-3) / 1e9,
             "pct_hbm_peak": 100.0 * step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "step_roof": {"bound": s_bound, "t_roof_us": s_troof, "t_roof_over_t": s_frac},
             "dominant_kernel": kname, "dominant_us": kms * 1e3,
-            "dominant_bytes": dom_bytes, "dominant_gbs": dom_bytes / (kms * 1e-3) / 1e9,
+            "dominant_bytes": dom_bytes, "dominant_flops": dom_flops,
+            "dominant_gbs": dom_bytes / (kms * 1e-3) / 1e9,
+            "dominant_tflops": dom_flops / (kms * 1e-3) / 1e12,
+            "dominant_roof": {"bound": d_bound, "t_roof_us": d_troof, "t_roof_over_t": d_frac},
         })
-        print(f"[bench] T={T} bm={bm} {mode}: {ms*1e3:.1f} us/step, "
-              f"{kname} {kms*1e3:.1f} us = {dom_bytes/(kms*1e-3)/1e9:.0f} GB/s",
-              file=sys.stderr, flush=True)
+        print(f"[bench] {name} T={T} bm={bm} {mode}: {ms*1e3:.1f} us/step "
+              f"({100 * s_frac:.0f}% of its {s_bound} roof), {kname} {kms*1e3:.1f} us "
+              f"({100 * d_frac:.0f}% of its {d_bound} roof)", file=sys.stderr, flush=True)
         # per-call distributions: the whole call (planner + forward) and the
-        # forward alone, warm (back to back), then cold (1 GiB written before
+        # forward alone, warm (back to back), then cold (a 1 GiB read before
         # each call, outside its event pair: evicts L2 and the 256 MB MALL)
         prot = {}
 
@@ -569,28 +570,102 @@ def main():
             del scratch, sink
         sweep[-1]["per_call"] = prot
         if args.calls:
-            sweep[-1]["router"] = router_leg(torch, moe, datagen, spec, args.workload, T, bm,
+            sweep[-1]["router"] = router_leg(torch, moe, datagen, spec, name, T, bm,
                                              args.calls, stream)
             sweep[-1]["shared"] = shared_leg(torch, moe, datagen, case, shared_w, args.calls,
                                              stream)
-        last_case = case
         del ws
+    del weights, shared_w
+    return sweep, case
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOADS,
+                    help="comma list of name[:T1/T2..]; the last token count of the last "
+                         "workload is the headline")
+    ap.add_argument("--tokens", default=None, help="comma list for every workload")
+    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--split", type=int, default=-1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--calls", type=int, default=200,
+                    help="per-call timed calls (warm) for the median / p10 / p90")
+    ap.add_argument("--cold-calls", type=int, default=50,
+                    help="per-call timed calls with a 1 GiB read before each (cold caches)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--summarize-counters", default=None, metavar="DIR",
+                    help="only write profiles/hbm_traffic.json from the counter runs under DIR")
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the fused MoE forward here runs on one GPU's local "
+              "experts with no collectives; --gpus must be 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if args.calibrate_copy:
+        # a plain copy of known size: each launch reads and writes exactly
+        # MIB MiB, which calibrates the HBM byte counters of a profiler
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+        return
+
+    import datagen
+    import mixture_experts_ffn_moe_amd as moe
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    moe.lib()
+    stream = torch.cuda.current_stream()
+    sweep = []
+    last_case = None
+    for name, tokens in parse_workloads(args.workload, args.tokens):
+        part, last_case = run_workload(args, torch, moe, datagen, name, tokens, dev, stream)
+        sweep += part
+        torch.cuda.empty_cache()
 
     head = sweep[-1]
-    roof = {"bound": "hbm", "achieved": head["dominant_gbs"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": head["dominant_gbs"] / HBM_PEAK_GBS,
-            "traffic": load_traffic(args.workload, head["T"], head["dominant_kernel"]),
-            "kernel": head["dominant_kernel"], "bytes_per_launch": head["dominant_bytes"],
-            "us_per_launch": head["dominant_us"]}
+    spec = datagen.WORKLOADS[head["workload"]]
+    kind, K, I, E, k = spec["kind"], spec["K"], spec["I"], spec["E"], spec["top_k"]
+    dr = head["dominant_roof"]
+    if dr["bound"] == "hbm":
+        achieved, peak, unit = head["dominant_gbs"], HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = head["dominant_tflops"], MFMA_PEAK_TFLOPS[kind], "TFLOP/s"
+    roof_line = {"bound": dr["bound"], "achieved": achieved, "peak": peak, "unit": unit,
+                 "frac": achieved / peak,
+                 "traffic": load_traffic(head["workload"], head["T"], head["dominant_kernel"]),
+                 "kernel": head["dominant_kernel"], "bytes_per_launch": head["dominant_bytes"],
+                 "flops_per_launch": head["dominant_flops"], "us_per_launch": head["dominant_us"],
+                 "t_roof_us": dr["t_roof_us"],
+                 "mfma_frac": head["dominant_tflops"] / MFMA_PEAK_TFLOPS[kind],
+                 "hbm_frac": head["dominant_gbs"] / HBM_PEAK_GBS}
     result = {
         "metric": METRIC, "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["us_per_step"] / 1e3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": DTYPE_NAME[kind], "data": "synthetic (seeded random weights, tokens, routing)",
-        "config": {"workload": args.workload, "tokens": head["T"], "hidden": K,
+        "config": {"workload": head["workload"], "tokens": head["T"], "hidden": K,
                    "intermediate": I, "experts": E, "top_k": k, "block_m": head["block_m"],
                    "mode": head["mode"], "parallelism": "single GPU, all experts local"},
-        "roofline": roof,
+        "roofline": roof_line,
+        "step_roofline": head["step_roof"],
         "sweep": sweep,
         "kernel_source_hash": kernel_source_hash(),
     }

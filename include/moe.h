@@ -66,12 +66,45 @@ typedef enum {
   MOE_MXFP4 = 3          /* weights e2m1 + e8m0 per 32; activations as MOE_MXFP8 */
 } moe_dtype;
 
-/* Message describing the last error of the calling thread ("" if none). */
+/*
+ * Overrides of the kernel schedule for tuning sweeps ([prime-flash] "Tuning"
+ * and "Constraints": its block_n / warp_n / stages knobs are exposed to the
+ * caller rather than chosen inside; the gfx950 kernels here have knobs of
+ * their own).  Pass NULL, or leave a field 0, for the library's choice.  A
+ * set field must be a value the call's kernels support, else the call
+ * fails with MOE_ERR_UNSUPPORTED before anything is launched; the result
+ * does not depend on the knobs beyond fp32 summation order.
+ *   k_groups  streaming gate/up kernels (block_m 16 or 32, split 0 or 1): K
+ *             groups per workgroup, 1 or 2 (2 needs K >= 256); each group
+ *             of 4 waves walks part of K and the groups' sums are added in
+ *             a fixed order.
+ *   k_split   split mode, block_m 16 or 32: gate/up workgroups per (block,
+ *             128-wide slice) tile, 1 or 4 (4 needs K / 128 a multiple of 8
+ *             and at least 16, two K groups, and workspace for the partial
+ *             sums: moe_workspace_size with the same tune).
+ *   prefetch  streaming kernels (block_m 16 or 32, split 0 or 1, k_split 1):
+ *             K steps each wave keeps in flight, 1, 2 or 4.
+ *   stages    LDS-tiled kernels (e4m3 dtypes, split mode, block_m 64 or
+ *             128): pipeline stages, 2 or 3.
+ */
+typedef struct moe_tune {
+  int32_t k_groups;
+  int32_t k_split;
+  int32_t prefetch;
+  int32_t stages;
+} moe_tune;
+
+/* Message describing the last error of the calling thread ("" if none).
+ * Every entry point returns a status ([prime-flash] "Constraints": the
+ * shape and alignment rules a call must meet are checked, and a violation
+ * is reported, before any work is done); this is its text. */
 const char* moe_last_error(void);
 
 /*
  * Capacities of the planner outputs for any routing of T tokens with top_k
- * routes each over E experts:
+ * routes each over E experts ([prime-flash] "Shapes": sorted_token_ids and
+ * expert_ids are sized for the worst-case padding; "API": moe_align pads
+ * each expert's rows to a multiple of block_m):
  *   *sorted_cap = T*top_k + min(E, T*top_k) * (block_m - 1)
  *   *blocks_cap = ceil(*sorted_cap / block_m)
  * (each non-empty expert pads fewer than block_m rows).  Host out-params.
@@ -104,7 +137,23 @@ int moe_align_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m,
  */
 int moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
               int32_t block_m, int32_t* sorted_token_ids, int32_t* expert_ids,
-              int32_t* num_tokens_post_padded, void* stream);
+              int32_t* num_tokens_post_padded, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Workspace of moe_align: *bytes (host out) = 0 at or below 16,384 routes
+ * (T * top_k), else 4 * ceil(T * top_k / 512) * E.  With at least that
+ * many bytes at `ws` (device, 16-byte aligned, contents undefined on
+ * return; concurrent calls need separate workspaces) moe_align plans over
+ * chunks of 512 route ids in three launches (per-chunk expert counts, which
+ * also set the outputs to -1; one workgroup turning them into per-chunk
+ * cursors and the block owners; one wave per chunk scattering its ids in
+ * order: [hpc-ops RFC] "Design", histogram, prefix sums, row-to-token
+ * mapping, with the grid-wide dependencies at kernel boundaries).  With no
+ * workspace (ws NULL or ws_bytes smaller) one workgroup plans every call.
+ * The outputs are the same bits either way.  Errors: MOE_ERR_NULL,
+ * MOE_ERR_SHAPE.
+ */
+int moe_align_workspace_size(int64_t T, int32_t top_k, int32_t E, size_t* bytes);
 
 /*
  * Router and planner in one launch.  The gate's routing arrives at the
@@ -127,9 +176,14 @@ int moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E,
  *                            exactly moe_align's outputs for that topk_ids.
  *   ws, ws_bytes             device workspace of at least
  *                            moe_route_align_workspace_size bytes, 16-byte
- *                            aligned, all ZERO before the first call that
- *                            uses it; every call leaves it zero.  Calls that
- *                            may overlap need separate workspaces.
+ *                            aligned, its first 256 bytes all ZERO before
+ *                            the first call that uses it; every call leaves
+ *                            them zero.  Calls that may overlap need
+ *                            separate workspaces.  Past 16,384 routes, a
+ *                            workspace of 256 + moe_align_workspace_size(T,
+ *                            top_k, E) bytes or more makes the launch route
+ *                            only, and moe_align's chunked planner follow
+ *                            it (same outputs).
  * E <= 1024, 1 <= top_k <= min(16, E).  NaN logits are not supported.
  * Errors: as moe_align, plus MOE_ERR_UNSUPPORTED (top_k > 16 or > E),
  * MOE_ERR_WORKSPACE (ws_bytes too small).  T == 0 writes moe_align's T == 0
@@ -206,14 +260,17 @@ int moe_select_block_m_routed(int32_t dtype, int64_t T, int64_t K, int32_t top_k
                               int32_t active_experts, int32_t* block_m);
 
 /*
- * Workspace bytes a fused_moe_* call with these sizes needs (host out-param).
- * split = -1 means "as moe_select_split picks"; for split = 2 (ring mode)
- * the size with the default ring (see moe_ring_layout).  Errors: as the
- * fused calls' size checks.
+ * Workspace bytes a fused_moe_* call with these sizes and this tune (NULL:
+ * none) needs (host out-param; [prime-flash] introduction: split=True writes
+ * the H-wide activation to memory once, which here lives in the caller's
+ * workspace with the per-route down outputs; split=False accumulates into an
+ * fp32 buffer).  split = -1 means "as moe_select_split picks"; for split = 2
+ * (ring mode) the size with the default ring (see moe_ring_layout).
+ * Errors: as the fused calls' size and tune checks.
  */
 int moe_workspace_size(int32_t dtype, int64_t T, int64_t K, int64_t N,
                        int32_t E, int32_t top_k, int32_t block_m,
-                       int32_t split, size_t* bytes);
+                       int32_t split, const moe_tune* tune, size_t* bytes);
 
 /*
  * Ring-mode workspace ([DeepGEMM #88] "How it works": the intermediate pool
@@ -303,8 +360,10 @@ int moe_workspace_layout(int32_t dtype, int64_t T, int64_t K, int64_t N,
  *                    of the workspace is nonzero after a call in which one
  *                    gave up (a broken invariant; the output is then
  *                    invalid).
+ *   tune             NULL, or schedule overrides (moe_tune above).
  *   workspace, workspace_bytes
- *                    device scratch of at least moe_workspace_size bytes;
+ *                    device scratch of at least moe_workspace_size bytes
+ *                    (same sizes, split and tune);
  *                    contents undefined on return; concurrent calls need
  *                    separate workspaces.
  *   stream           hipStream_t as void*.
@@ -319,8 +378,8 @@ int fused_moe_bf16(const void* x, const void* w1, const void* w2,
                    const int32_t* num_tokens_post_padded,
                    const float* topk_weights, void* out, int64_t T, int64_t K,
                    int64_t N, int32_t E, int32_t top_k, int32_t block_m,
-                   int32_t split, void* workspace, size_t workspace_bytes,
-                   void* stream);
+                   int32_t split, const moe_tune* tune, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /* Blockwise FP8 W8A8 path ([hpc-ops RFC] "Background": blockwise FP8 MoE;
  * [DeepGEMM #88] "Before you merge": the intermediate is requantized per
@@ -337,8 +396,8 @@ int fused_moe_fp8_blockwise(const void* x, const float* x_scale,
                             const int32_t* num_tokens_post_padded,
                             const float* topk_weights, void* out, int64_t T,
                             int64_t K, int64_t N, int32_t E, int32_t top_k,
-                            int32_t block_m, int32_t split, void* workspace,
-                            size_t workspace_bytes, void* stream);
+                            int32_t block_m, int32_t split, const moe_tune* tune,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* MXFP8 path ([prime-flash] "Scale layout (mxfp8)": e4m3 values with e8m0
  * scales per 32 along K, activation scales row-major; the intermediate is
@@ -356,8 +415,8 @@ int fused_moe_mxfp8(const void* x, const uint8_t* x_scale, const void* w1,
                     const int32_t* num_tokens_post_padded,
                     const float* topk_weights, void* out, int64_t T, int64_t K,
                     int64_t N, int32_t E, int32_t top_k, int32_t block_m,
-                    int32_t split, void* workspace, size_t workspace_bytes,
-                    void* stream);
+                    int32_t split, const moe_tune* tune, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /* MXFP4 weights x MX FP8 activations ([DeepGEMM #411] "Summary": routed
  * weights stay packed MXFP4 in memory, E2M1 elements with one UE8M0 exponent
@@ -377,8 +436,8 @@ int fused_moe_mxfp4(const void* x, const uint8_t* x_scale, const void* w1,
                     const int32_t* num_tokens_post_padded,
                     const float* topk_weights, void* out, int64_t T, int64_t K,
                     int64_t N, int32_t E, int32_t top_k, int32_t block_m,
-                    int32_t split, void* workspace, size_t workspace_bytes,
-                    void* stream);
+                    int32_t split, const moe_tune* tune, void* workspace,
+                    size_t workspace_bytes, void* stream);
 
 /*
  * Shared experts.  [DeepGEMM #411] "Summary" runs the routed and the shared
@@ -417,8 +476,55 @@ int fused_moe_shared(int32_t dtype, const void* x, const void* x_scale, const vo
                      int32_t n_shared, const int32_t* sorted_token_ids,
                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                      const float* topk_weights, void* out, int64_t T, int64_t K, int64_t N,
-                     int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* workspace,
-                     size_t workspace_bytes, void* stream);
+                     int32_t E, int32_t top_k, int32_t block_m, int32_t split,
+                     const moe_tune* tune, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The split mode's second half alone, for testing the down GEMM and the
+ * combine apart from the gate/up GEMM and the requantization ([prime-flash]
+ * "Tests and benchmarks": the comparison isolates the kernel from the
+ * quantizer; [hpc-ops RFC] "Background" stages 4-5).  The caller places the
+ * requantized intermediate in the workspace, rows in sorted_token_ids order
+ * at moe_workspace_layout's offsets (values, then scales), and the call runs
+ * the down GEMM of every planner block and the top-k weighted combine into
+ * `out`, exactly as fused_moe_* in split mode (split = 1, no tune) would
+ * after its gate/up GEMM.  Arguments as fused_moe_* (w2 and its scales only;
+ * bf16 passes NULL scales); the workspace is moe_workspace_size(dtype, T, K,
+ * N, E, top_k, block_m, 1, NULL) bytes.  Rows of -1 positions may hold any
+ * bytes.  Errors as fused_moe_*.
+ */
+int fused_moe_down_combine(int32_t dtype, const void* w2, const void* w2_scale,
+                           const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                           const int32_t* num_tokens_post_padded, const float* topk_weights,
+                           void* out, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+                           int32_t block_m, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * Diagnostic, not a step of the forward: one 128-wide K step of the matrix
+ * instruction each dtype's kernels use, D = C + A . B^T, per 16 x 16 tile,
+ * through the kernels' own operand layout and instruction wrappers.  The
+ * parity tests accept outputs within an error model of these instructions
+ * (their sums are not correctly rounded: an e4m3 instruction keeps a limited
+ * number of bits of the products it aligns); a test measures the
+ * instructions against that model with this call.
+ *   a        (n_tiles, 16, 128) A rows: e4m3 bytes, or bf16 (256 bytes a row)
+ *   b        (n_tiles, 16, 128) B rows as a; MOE_MXFP4: (n_tiles, 16, 64)
+ *            packed e2m1 (element 2j in the low nibble of byte j)
+ *   a_scale, b_scale  MOE_MXFP8 / MOE_MXFP4: (n_tiles, 16, 4) e8m0 bytes, one
+ *            per 32-wide K block of each row; unused (may be NULL) otherwise
+ *   c        (n_tiles, 16, 16) fp32 accumulator input, or NULL for zeros
+ *   d [out]  (n_tiles, 16, 16) fp32: d[t][i][j] = c[t][i][j] + sum_k
+ *            A[t][i][k] B[t][j][k] (times the rows' block scales for MX)
+ * MOE_FP8_BLOCKWISE uses the unscaled e4m3 instruction (block scales are
+ * applied outside it by the kernels).  Device pointers, 16-byte aligned;
+ * asynchronous on `stream`.  Returns MOE_ERR_UNSUPPORTED (dtype),
+ * MOE_ERR_SHAPE (n_tiles outside [0, 2^24]), MOE_ERR_NULL, MOE_ERR_ALIGN or
+ * MOE_ERR_HIP; no message is recorded for this call.
+ */
+int moe_mfma_probe(int32_t dtype, const void* a, const void* b, const uint8_t* a_scale,
+                   const uint8_t* b_scale, const float* c, float* d, int64_t n_tiles,
+                   void* stream);
 
 /*
  * Profiling hook (changes no result): the next fused_moe_* calls made by the

@@ -33,6 +33,7 @@ __all__ = [
     "fused_moe_bf16",
     "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4", "EXPORTED_SYMBOLS",
     "moe_route_align", "moe_route_align_workspace_size", "moe_align_shared", "fused_moe_shared",
+    "moe_mfma_probe", "moe_align_workspace_size", "MoeTune", "fused_moe_down_combine",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -47,7 +48,8 @@ EXPORTED_SYMBOLS = (
     "fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4",
     "moe_set_timing_events", "moe_route_align_workspace_size", "moe_route_align",
     "moe_align_shared", "fused_moe_shared", "moe_ring_layout", "moe_ring_schedule",
-    "moe_select_block_m_routed", "moe_align_ws_size", "moe_align_ws",
+    "moe_select_block_m_routed", "moe_align_ws_size", "moe_align_ws", "moe_mfma_probe",
+    "moe_align_workspace_size", "fused_moe_down_combine",
 )
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
@@ -81,7 +83,8 @@ def lib():
     L.moe_last_error.argtypes = []
     L.moe_align_capacity.argtypes = [_I64, _I32, _I32, _I32, ctypes.POINTER(_I64),
                                      ctypes.POINTER(_I64)]
-    L.moe_align.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P]
+    L.moe_align.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
+    L.moe_align_workspace_size.argtypes = [_I64, _I32, _I32, ctypes.POINTER(_SZ)]
     L.moe_select_split.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32,
                                    ctypes.POINTER(_I32)]
     L.moe_select_block_m.argtypes = [_I32, _I64, _I64, _I32, _I32, ctypes.POINTER(_I32)]
@@ -89,19 +92,22 @@ def lib():
     L.moe_align_ws.argtypes = [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _SZ, _P]
     L.moe_select_block_m_routed.argtypes = [_I32, _I64, _I64, _I32, _I32, _I32,
                                             ctypes.POINTER(_I32)]
-    L.moe_workspace_size.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
+    L.moe_workspace_size.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P,
                                      ctypes.POINTER(_SZ)]
     L.moe_workspace_layout.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32,
                                        ctypes.POINTER(_SZ), ctypes.POINTER(_SZ)]
     L.moe_ring_schedule.argtypes = [_I32, _I32, _I32, _I32, _I64, _I64, _P, _P, _P]
     L.moe_ring_layout.argtypes = [_I32, _I64, _I64, _I64, _I32, _I32, _I32, ctypes.POINTER(_SZ),
                                   ctypes.POINTER(_SZ), ctypes.POINTER(_I64)]
-    tail = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _P]
+    tail = [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]
     L.fused_moe_bf16.argtypes = [_P, _P, _P] + tail
     L.fused_moe_fp8_blockwise.argtypes = [_P, _P, _P, _P, _P, _P] + tail
     L.fused_moe_mxfp8.argtypes = [_P, _P, _P, _P, _P, _P] + tail
     L.fused_moe_mxfp4.argtypes = [_P, _P, _P, _P, _P, _P] + tail
     L.moe_set_timing_events.argtypes = [_P, _P, _I32]
+    L.moe_mfma_probe.argtypes = [_I32, _P, _P, _P, _P, _P, _P, _I64, _P]
+    L.fused_moe_down_combine.argtypes = [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
+                                         _I32, _I32, _I32, _P, _SZ, _P]
     L.moe_route_align_workspace_size.argtypes = [ctypes.POINTER(_SZ)]
     L.moe_route_align.argtypes = [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]
     L.moe_align_shared.argtypes = [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P]
@@ -111,6 +117,22 @@ def lib():
             getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L
+
+
+class MoeTune(ctypes.Structure):
+    """Schedule overrides (struct moe_tune of the C ABI); 0 keeps the
+    library's choice: k_groups (1, 2), k_split (1, 4), prefetch (1, 2, 4),
+    stages (2, 3)."""
+    _fields_ = [("k_groups", _I32), ("k_split", _I32), ("prefetch", _I32), ("stages", _I32)]
+
+
+def _tune(tune):
+    """A MoeTune, a dict of its fields, or None -> pointer argument."""
+    if tune is None:
+        return None
+    if isinstance(tune, dict):
+        tune = MoeTune(**tune)
+    return ctypes.byref(tune)
 
 
 def _check(status):
@@ -146,10 +168,19 @@ def moe_set_timing_events(before, after, which=1):
     _check(lib().moe_set_timing_events(before, after, which))
 
 
-def moe_align(topk_ids, num_experts, block_m, stream=None, out=None):
+def moe_align_workspace_size(T, top_k, num_experts):
+    out = _SZ()
+    _check(lib().moe_align_workspace_size(T, top_k, num_experts, ctypes.byref(out)))
+    return out.value
+
+
+def moe_align(topk_ids, num_experts, block_m, stream=None, out=None, workspace=-1):
     """Planner: returns (sorted_token_ids, expert_ids, num_tokens_post_padded)
     as int32 device tensors (the last one of shape (1,)).  ``out`` may pass
-    preallocated tensors of the capacities moe_align_capacity gives."""
+    preallocated tensors of the capacities moe_align_capacity gives.
+    ``workspace``: a device tensor of moe_align_workspace_size bytes (the
+    chunked planner past 16,384 routes), None (one workgroup plans), or by
+    default one cached per device."""
     T, k = topk_ids.shape
     rows, blocks = moe_align_capacity(T, k, num_experts, block_m)
     dev = topk_ids.device
@@ -159,8 +190,13 @@ def moe_align(topk_ids, num_experts, block_m, stream=None, out=None):
         sorted_ids = torch.empty(max(rows, 1), dtype=torch.int32, device=dev)[:rows]
         expert_ids = torch.empty(max(blocks, 1), dtype=torch.int32, device=dev)[:blocks]
         ntp = torch.empty(1, dtype=torch.int32, device=dev)
+    if isinstance(workspace, int):
+        need = moe_align_workspace_size(T, k, num_experts)
+        workspace = _cached_align_ws(dev, need) if need else None
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().moe_align(_ptr(topk_ids.contiguous()), T, k, num_experts, block_m,
-                           _ptr(sorted_ids), _ptr(expert_ids), _ptr(ntp), _stream(stream)))
+                           _ptr(sorted_ids), _ptr(expert_ids), _ptr(ntp), _ptr(workspace), nbytes,
+                           _stream(stream)))
     return sorted_ids, expert_ids, ntp
 
 
@@ -173,13 +209,22 @@ def moe_route_align_workspace_size():
 _route_ws = {}
 
 
+def _cached_align_ws(dev, need):
+    ws = _ALIGN_WS.get(dev)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        _ALIGN_WS[dev] = ws
+    return ws
+
+
 def moe_route_align(logits, top_k, block_m, stream=None, out=None, workspace=None):
     """Router + planner in one launch: (T, E) fp32 logits -> (topk_ids,
     topk_weights, sorted_token_ids, expert_ids, num_tokens_post_padded).
-    ``out`` may pass those five preallocated.  ``workspace`` must hold zeros
-    before its first use (each call leaves it zero); by default one zeroed
-    buffer per device is kept and reused, so calls on several streams of one
-    device must pass their own."""
+    ``out`` may pass those five preallocated.  ``workspace``'s first 256
+    bytes must hold zeros before its first use (each call leaves them zero);
+    by default one zeroed buffer per device, large enough for the chunked
+    planner of this call, is kept and reused, so calls on several streams of
+    one device must pass their own."""
     T, E = logits.shape
     rows, blocks = moe_align_capacity(T, top_k, E, block_m)
     dev = logits.device
@@ -193,9 +238,9 @@ def moe_route_align(logits, top_k, block_m, stream=None, out=None, workspace=Non
         ntp = torch.empty(1, dtype=torch.int32, device=dev)
     if workspace is None:
         key = (dev.type, dev.index)
-        if key not in _route_ws:
-            _route_ws[key] = torch.zeros(moe_route_align_workspace_size(), dtype=torch.uint8,
-                                         device=dev)
+        need = moe_route_align_workspace_size() + moe_align_workspace_size(T, top_k, E)
+        if key not in _route_ws or _route_ws[key].numel() < need:
+            _route_ws[key] = torch.zeros(need, dtype=torch.uint8, device=dev)
         workspace = _route_ws[key]
     _check(lib().moe_route_align(_ptr(logits.contiguous()), T, E, top_k, block_m, _ptr(ids),
                                  _ptr(w), _ptr(sorted_ids), _ptr(expert_ids), _ptr(ntp),
@@ -247,11 +292,7 @@ def moe_align_ws(topk_ids, num_experts, block_m, n_shared=0, stream=None, out=No
         ntp = torch.empty(1, dtype=torch.int32, device=dev)
     need = moe_align_ws_size(T, k, num_experts, n_shared)
     if workspace is None and need:
-        ws = _ALIGN_WS.get(dev)
-        if ws is None or ws.numel() < need:
-            ws = torch.empty(need, dtype=torch.uint8, device=dev)
-            _ALIGN_WS[dev] = ws
-        workspace = ws
+        workspace = _cached_align_ws(dev, need)
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().moe_align_ws(_ptr(topk_ids.contiguous()), T, k, num_experts, n_shared, block_m,
                               _ptr(sorted_ids), _ptr(expert_ids), _ptr(ntp), _ptr(workspace),
@@ -261,7 +302,7 @@ def moe_align_ws(topk_ids, num_experts, block_m, n_shared=0, stream=None, out=No
 
 def fused_moe_shared(dtype, x, x_scale, w1, w1_scale, w2, w2_scale, n_shared, sorted_token_ids,
                      expert_ids, num_tokens_post_padded, topk_weights, top_k, block_m, split=-1,
-                     out=None, workspace=None, stream=None):
+                     out=None, workspace=None, stream=None, tune=None):
     """Forward with shared experts: w1 / w2 (and scales) hold the routed
     experts followed by ``n_shared`` shared ones; planner outputs from
     moe_align_shared."""
@@ -271,14 +312,14 @@ def fused_moe_shared(dtype, x, x_scale, w1, w1_scale, w2, w2_scale, n_shared, so
     dev = w1.device
     if out is None:
         out = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
-    need = moe_workspace_size(dtype, T, K, N, E_all, top_k + n_shared, block_m, split)
+    need = moe_workspace_size(dtype, T, K, N, E_all, top_k + n_shared, block_m, split, tune)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _check(lib().fused_moe_shared(_DTYPE_CODE.get(dtype, dtype), _ptr(x), _ptr(x_scale), _ptr(w1),
                                   _ptr(w1_scale), _ptr(w2), _ptr(w2_scale), n_shared,
                                   _ptr(sorted_token_ids), _ptr(expert_ids),
                                   _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(out), T,
-                                  K, N, E, top_k, block_m, split, _ptr(workspace),
+                                  K, N, E, top_k, block_m, split, _tune(tune), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
@@ -313,10 +354,10 @@ def active_experts(topk_ids, num_experts):
     return int(torch.unique(valid).numel())
 
 
-def moe_workspace_size(dtype, T, K, N, num_experts, top_k, block_m, split=-1):
+def moe_workspace_size(dtype, T, K, N, num_experts, top_k, block_m, split=-1, tune=None):
     out = _SZ()
     _check(lib().moe_workspace_size(_DTYPE_CODE.get(dtype, dtype), T, K, N, num_experts, top_k,
-                                    block_m, split, ctypes.byref(out)))
+                                    block_m, split, _tune(tune), ctypes.byref(out)))
     return out.value
 
 
@@ -351,66 +392,100 @@ def moe_ring_schedule(n_blocks, up_per_block, down_per_block, lag, first=0, coun
 
 
 def _run(fn, dtype, operands, w1, sorted_token_ids, expert_ids, num_tokens_post_padded,
-         topk_weights, top_k, block_m, split, out, workspace, stream, T, K):
+         topk_weights, top_k, block_m, split, out, workspace, stream, T, K, tune=None):
     E, N, _ = w1.shape
     dev = w1.device
     if out is None:
         out = torch.empty(T, K, dtype=torch.bfloat16, device=dev)
-    need = moe_workspace_size(dtype, T, K, N, E, top_k, block_m, split)
+    need = moe_workspace_size(dtype, T, K, N, E, top_k, block_m, split, tune)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _check(fn(*[_ptr(t) for t in operands], _ptr(sorted_token_ids), _ptr(expert_ids),
               _ptr(num_tokens_post_padded), _ptr(topk_weights), _ptr(out), T, K, N, E, top_k,
-              block_m, split, _ptr(workspace), workspace.numel() * workspace.element_size(),
-              _stream(stream)))
+              block_m, split, _tune(tune), _ptr(workspace),
+              workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 
 def fused_moe_bf16(x, w1, w2, sorted_token_ids, expert_ids, num_tokens_post_padded,
                    topk_weights, top_k, block_m, split=-1, out=None, workspace=None,
-                   stream=None):
+                   stream=None, tune=None):
     T, K = x.shape
     return _run(lib().fused_moe_bf16, MOE_BF16, [x, w1, w2], w1, sorted_token_ids, expert_ids,
                 num_tokens_post_padded, topk_weights, top_k, block_m, split, out, workspace,
-                stream, T, K)
+                stream, T, K, tune)
 
 
 def fused_moe_fp8_blockwise(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids,
                             expert_ids, num_tokens_post_padded, topk_weights, top_k, block_m,
-                            split=-1, out=None, workspace=None, stream=None):
+                            split=-1, out=None, workspace=None, stream=None, tune=None):
     T, K = x.shape
     return _run(lib().fused_moe_fp8_blockwise, MOE_FP8_BLOCKWISE,
                 [x, x_scale, w1, w1_scale, w2, w2_scale], w1, sorted_token_ids, expert_ids,
                 num_tokens_post_padded, topk_weights, top_k, block_m, split, out, workspace,
-                stream, T, K)
+                stream, T, K, tune)
 
 
 def fused_moe_mxfp8(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
                     num_tokens_post_padded, topk_weights, top_k, block_m, split=-1, out=None,
-                    workspace=None, stream=None):
+                    workspace=None, stream=None, tune=None):
     T, K = x.shape
     return _run(lib().fused_moe_mxfp8, MOE_MXFP8, [x, x_scale, w1, w1_scale, w2, w2_scale], w1,
                 sorted_token_ids, expert_ids, num_tokens_post_padded, topk_weights, top_k,
-                block_m, split, out, workspace, stream, T, K)
+                block_m, split, out, workspace, stream, T, K, tune)
 
 
 def fused_moe_mxfp4(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
                     num_tokens_post_padded, topk_weights, top_k, block_m, split=-1, out=None,
-                    workspace=None, stream=None):
+                    workspace=None, stream=None, tune=None):
     """w1 (E, N, K/2) and w2 (E, K, N/4) uint8: packed e2m1 pairs."""
     T, K = x.shape
     return _run(lib().fused_moe_mxfp4, MOE_MXFP4, [x, x_scale, w1, w1_scale, w2, w2_scale], w1,
                 sorted_token_ids, expert_ids, num_tokens_post_padded, topk_weights, top_k,
-                block_m, split, out, workspace, stream, T, K)
+                block_m, split, out, workspace, stream, T, K, tune)
+
+
+def fused_moe_down_combine(dtype, w2, w2_scale, sorted_token_ids, expert_ids,
+                           num_tokens_post_padded, topk_weights, top_k, block_m, workspace, T,
+                           out=None, stream=None):
+    """Down GEMM + combine of the split mode on the intermediate the caller
+    wrote into ``workspace`` (moe_workspace_layout offsets); returns out."""
+    E, K, I = w2.shape[0], w2.shape[1], w2.shape[2] * (2 if dtype == "mxfp4" else 1)
+    if out is None:
+        out = torch.empty(T, K, dtype=torch.bfloat16, device=w2.device)
+    _check(lib().fused_moe_down_combine(_DTYPE_CODE.get(dtype, dtype), _ptr(w2), _ptr(w2_scale),
+                                        _ptr(sorted_token_ids), _ptr(expert_ids),
+                                        _ptr(num_tokens_post_padded), _ptr(topk_weights),
+                                        _ptr(out), T, K, 2 * I, E, top_k, block_m,
+                                        _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream(stream)))
+    return out
+
+
+def moe_mfma_probe(dtype, a, b, a_scale=None, b_scale=None, c=None, stream=None, out=None):
+    """One 128-wide K step of the dtype's matrix instruction per 16 x 16 tile
+    (diagnostic): a, b are (n, 16, 128) uint8 / bf16 rows (MXFP4 b: (n, 16,
+    64) packed bytes), scales (n, 16, 4) uint8 for the MX dtypes, c an
+    optional (n, 16, 16) fp32 accumulator.  Returns d (n, 16, 16) fp32."""
+    n = a.shape[0]
+    if out is None:
+        out = torch.empty(n, 16, 16, dtype=torch.float32, device=a.device)
+    _check(lib().moe_mfma_probe(_DTYPE_CODE.get(dtype, dtype), _ptr(a), _ptr(b), _ptr(a_scale),
+                                _ptr(b_scale), _ptr(c), _ptr(out), n, _stream(stream)))
+    return out
 
 
 def run_case(case, block_m=None, split=-1, stream=None, workspace=None, out=None,
-             align_out=None, skip_align=False):
+             align_out=None, skip_align=False, tune=None):
     """Planner + forward for a ``datagen.Case``-like object (attributes kind,
     x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids, topk_weights, E, top_k).
     Returns (out, (sorted_token_ids, expert_ids, num_tokens_post_padded)).
     ``skip_align`` runs the fused forward alone on ``align_out`` as an earlier
-    call with the same routing and block_m filled it."""
+    call with the same routing and block_m filled it.  ``tune``: schedule
+    overrides (MoeTune or a dict of its fields).  Without ``block_m`` the
+    routed block-size choice needs the active-expert count, which this
+    helper counts on the host (a synchronization)."""
     T = case.x.shape[0]
     if block_m is None:
         block_m = moe_select_block_m_routed(T, case.top_k, case.E,
@@ -421,11 +496,13 @@ def run_case(case, block_m=None, split=-1, stream=None, workspace=None, out=None
         if align_out is None:
             raise ValueError("skip_align needs the align_out of an earlier call")
         align = tuple(align_out)
-    else:
+    elif S:
         align = moe_align_ws(case.topk_ids, case.E, block_m, n_shared=S, stream=stream,
                              out=align_out)
+    else:
+        align = moe_align(case.topk_ids, case.E, block_m, stream=stream, out=align_out)
     args = dict(top_k=case.top_k, block_m=block_m, split=split, out=out, workspace=workspace,
-                stream=stream)
+                stream=stream, tune=tune)
     if S:
         o = fused_moe_shared(case.kind, case.x, case.x_scale, case.w1, case.w1_scale, case.w2,
                              case.w2_scale, S, *align, case.topk_weights, **args)

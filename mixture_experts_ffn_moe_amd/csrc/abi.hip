@@ -98,14 +98,58 @@ int pick_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_
 // streaming blocks) where few (block, slice) tiles exist: at most 128 by the
 // even-spread estimate, K/128 a multiple of 8 and at least 16.  Measured
 // (MXFP8, K=4096, I=256, E=32, top-8): see the kernel.
+bool kw_supported(int64_t K, int32_t block_m, int split) {
+  const int64_t KS = K / 128;
+  return split == 1 && block_m <= 32 && KS % 8 == 0 && KS >= 16;
+}
+
 int pick_kw(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
-            int32_t block_m, int split) {
-  if (split != 1 || block_m > 32) return 1;
-  const int64_t KS = K / 128, R = T * top_k;
-  if (KS % 8 || KS < 16) return 1;
+            int32_t block_m, int split, const moe_tune* tune = nullptr) {
+  if (tune && tune->k_split) return tune->k_split;
+  if (!kw_supported(K, block_m, split)) return 1;
+  const int64_t R = T * top_k;
   const int64_t tiles = (R < E ? R : (int64_t)E) * ((N / 2) / 128);
   (void)dtype;
   return tiles <= 128 ? 4 : 1;
+}
+
+// Schedule overrides: every set field must name a variant the call's
+// kernels have (checked before anything is launched).
+int check_tune(int32_t dtype, int64_t K, int32_t block_m, int split, const moe_tune* t) {
+  if (!t) return MOE_OK;
+  const bool streaming = block_m <= 32 || dtype == MOE_BF16 || dtype == MOE_MXFP4;
+  if (t->k_groups) {
+    if (t->k_groups != 1 && t->k_groups != 2)
+      return fail(MOE_ERR_UNSUPPORTED, "tune.k_groups must be 0, 1 or 2 (got %d)", t->k_groups);
+    if (block_m > 32 || split == 2)
+      return fail(MOE_ERR_UNSUPPORTED, "tune.k_groups needs block_m 16 or 32 and split 0 or 1");
+    if (t->k_groups == 2 && K < 256)
+      return fail(MOE_ERR_UNSUPPORTED, "tune.k_groups = 2 needs K >= 256");
+  }
+  if (t->k_split) {
+    if (t->k_split != 1 && t->k_split != 4)
+      return fail(MOE_ERR_UNSUPPORTED, "tune.k_split must be 0, 1 or 4 (got %d)", t->k_split);
+    if (t->k_split == 4 && !kw_supported(K, block_m, split))
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "tune.k_split = 4 needs split 1, block_m 16 or 32, K/128 a multiple of 8 and >= 16");
+    if (t->k_split == 4 && t->k_groups == 1)
+      return fail(MOE_ERR_UNSUPPORTED, "tune.k_split = 4 runs two K groups per workgroup");
+  }
+  if (t->prefetch) {
+    if (t->prefetch != 1 && t->prefetch != 2 && t->prefetch != 4)
+      return fail(MOE_ERR_UNSUPPORTED, "tune.prefetch must be 0, 1, 2 or 4 (got %d)", t->prefetch);
+    if (block_m > 32 || split == 2 || t->k_split == 4)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "tune.prefetch needs block_m 16 or 32, split 0 or 1 and k_split 1");
+  }
+  if (t->stages) {
+    if (t->stages != 2 && t->stages != 3)
+      return fail(MOE_ERR_UNSUPPORTED, "tune.stages must be 0, 2 or 3 (got %d)", t->stages);
+    if (streaming || split != 1 || block_m > 128 || K % 256)
+      return fail(MOE_ERR_UNSUPPORTED,
+                  "tune.stages needs the LDS-tiled kernels: e4m3 dtypes, split 1, block_m 64 or 128");
+  }
+  return MOE_OK;
 }
 
 struct Layout {
@@ -121,7 +165,7 @@ size_t h_scale_bytes(int32_t dtype, int64_t I) {
 }
 
 Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
-              int32_t block_m, int split) {
+              int32_t block_m, int split, const moe_tune* tune = nullptr) {
   Layout L{};
   const int64_t I = N / 2;
   const size_t R = (size_t)T * top_k;
@@ -151,7 +195,7 @@ Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
   if (split) {
     L.flags = off;
     off = round_up(off + R * 4, 256);
-    const int kw = pick_kw(dtype, T, K, N, E, top_k, block_m, split);
+    const int kw = pick_kw(dtype, T, K, N, E, top_k, block_m, split, tune);
     if (kw > 1) {  // tile tickets right after the flags (one clear)
       L.tickets = off;
       off = round_up(off + (size_t)blocks * (I / 128) * 4, 256);
@@ -179,8 +223,9 @@ Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
 int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const void* w1s,
             const void* w2, const void* w2s, const int32_t* sorted, const int32_t* expert_ids,
             const int32_t* ntp, const float* topk_w, void* out, int64_t T, int64_t K, int64_t N,
-            int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* ws, size_t ws_bytes,
-            void* stream, int32_t n_shared = 0) {
+            int32_t E, int32_t top_k, int32_t block_m, int32_t split, const moe_tune* tune,
+            void* ws, size_t ws_bytes, void* stream, int32_t n_shared = 0,
+            bool down_only = false) {
   // E routed experts, then n_shared shared ones in the weights; every token
   // adds one route per shared expert.  Capacities and workspace follow the
   // totals.
@@ -193,7 +238,15 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
     return fail(MOE_ERR_UNSUPPORTED, "block_m 256 runs the split mode only");
   if (split == 2 && block_m > 32)
     return fail(MOE_ERR_UNSUPPORTED, "the ring mode runs block_m 16 or 32 (got %d)", block_m);
+  const int sp = split < 0 ? pick_split(dtype, T, K, N, E_all, k_all, block_m) : split;
+  rc = check_tune(dtype, K, block_m, sp, tune);
+  if (rc) return rc;
   if (T == 0) return ok();
+  if (down_only) {
+    // only w2 is read; the checks below see it in place of x and w1
+    x = w1 = w2;
+    xs = w1s = w2s;
+  }
   if (!x || !w1 || !w2 || !sorted || !expert_ids || !ntp || !topk_w || !out)
     return fail(MOE_ERR_NULL, "a required pointer is NULL");
   if (dtype != MOE_BF16 && (!xs || !w1s || !w2s))
@@ -204,8 +257,7 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
   if (dtype == MOE_FP8_BLOCKWISE && (!aligned(xs, 4) || !aligned(w1s, 4) || !aligned(w2s, 4)))
     return fail(MOE_ERR_ALIGN, "fp32 scales must be 4-byte aligned");
   if (!aligned(ntp, 4)) return fail(MOE_ERR_ALIGN, "num_tokens_post_padded must be 4-byte aligned");
-  const int sp = split < 0 ? pick_split(dtype, T, K, N, E_all, k_all, block_m) : split;
-  Layout L = layout(dtype, T, K, N, E_all, k_all, block_m, sp);
+  Layout L = layout(dtype, T, K, N, E_all, k_all, block_m, sp, tune);
   int64_t rows, blocks;
   capacity(T, k_all, E_all, block_m, &rows, &blocks);
   if (sp == 2) {
@@ -244,7 +296,7 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
     a.hs = w + L.hs;
     a.yr = reinterpret_cast<float*>(w + L.yr);
     a.h_rows = (int)(blocks * block_m);
-    a.kw = pick_kw(dtype, T, K, N, E_all, k_all, block_m, sp);
+    a.kw = pick_kw(dtype, T, K, N, E_all, k_all, block_m, sp, tune);
     if (a.kw > 1) {
       a.tickets = reinterpret_cast<int*>(w + L.tickets);
       a.part = reinterpret_cast<float*>(w + L.part);
@@ -264,11 +316,18 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
   a.top_k = top_k;
   a.n_shared = n_shared;
   a.blocks_cap = (int)blocks;
+  if (tune) {
+    a.ksplit = tune->k_groups;
+    a.depth = tune->prefetch;
+    a.stages = tune->stages;
+  }
   static_assert(MOE_BF16 == KIND_BF16 && MOE_FP8_BLOCKWISE == KIND_FP8B && MOE_MXFP8 == KIND_MX &&
                     MOE_MXFP4 == KIND_MX4,
                 "the moe_dtype values are the kernel kinds");
   const int kind = dtype;
-  hipError_t e = launch_moe(kind, block_m, sp, a, static_cast<hipStream_t>(stream), g_hook);
+  hipError_t e = down_only
+                     ? launch_down_combine(kind, block_m, a, static_cast<hipStream_t>(stream))
+                     : launch_moe(kind, block_m, sp, a, static_cast<hipStream_t>(stream), g_hook);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -290,9 +349,24 @@ int moe_align_capacity(int64_t T, int32_t top_k, int32_t E, int32_t block_m, int
   return ok();
 }
 
+// Route counts from which the planner runs over chunks in three launches
+// when the caller provides the workspace (measured, K=4096 I=2048 E=288
+// top-8: the one-workgroup planner takes 165 us for 65,536 routes, 11 us for
+// 1,536; the chunked one 29 us for 65,536).
+constexpr int64_t kChunkedRoutes = 16384;
+
+int moe_align_workspace_size(int64_t T, int32_t top_k, int32_t E, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
+  int rc = check_routes(T, top_k, E);
+  if (rc) return rc;
+  const int64_t routes = T * (int64_t)top_k;
+  *bytes = routes > kChunkedRoutes ? align_chunked_ws(routes, E) : 0;
+  return ok();
+}
+
 int moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int32_t block_m,
               int32_t* sorted_token_ids, int32_t* expert_ids, int32_t* num_tokens_post_padded,
-              void* stream) {
+              void* ws, size_t ws_bytes, void* stream) {
   int64_t rows, blocks;
   int rc = moe_align_capacity(T, top_k, E, block_m, &rows, &blocks);
   if (rc) return rc;
@@ -300,14 +374,23 @@ int moe_align(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, int3
   if (!num_tokens_post_padded || (rows > 0 && (!sorted_token_ids || !expert_ids)) ||
       (T > 0 && !topk_ids))
     return fail(MOE_ERR_NULL, "a required pointer is NULL");
-  const void* ps[] = {topk_ids, sorted_token_ids, expert_ids};
+  const void* ps[] = {topk_ids, sorted_token_ids, expert_ids, ws};
   for (const void* p : ps)
     if (p && !aligned(p, 16)) return fail(MOE_ERR_ALIGN, "tensors must be 16-byte aligned");
   if (!aligned(num_tokens_post_padded, 4))
     return fail(MOE_ERR_ALIGN, "num_tokens_post_padded must be 4-byte aligned");
-  hipError_t e = launch_align(topk_ids, (int)(T * top_k), E, block_m, sorted_token_ids, expert_ids,
-                              num_tokens_post_padded, (int)rows, (int)blocks,
-                              static_cast<hipStream_t>(stream));
+  size_t need = 0;
+  rc = moe_align_workspace_size(T, top_k, E, &need);
+  if (rc) return rc;
+  hipError_t e;
+  if (need > 0 && ws && ws_bytes >= need)
+    e = launch_align_chunked(topk_ids, (int)(T * top_k), E, block_m, sorted_token_ids, expert_ids,
+                             num_tokens_post_padded, (int)rows, (int)blocks,
+                             static_cast<hipStream_t>(stream), (int)T, 0, static_cast<int*>(ws));
+  else
+    e = launch_align(topk_ids, (int)(T * top_k), E, block_m, sorted_token_ids, expert_ids,
+                     num_tokens_post_padded, (int)rows, (int)blocks,
+                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -342,18 +425,14 @@ int fused_moe_shared(int32_t dtype, const void* x, const void* x_scale, const vo
                      int32_t n_shared, const int32_t* sorted_token_ids,
                      const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                      const float* topk_weights, void* out, int64_t T, int64_t K, int64_t N,
-                     int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     int32_t E, int32_t top_k, int32_t block_m, int32_t split,
+                     const moe_tune* tune, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   if (dtype < MOE_BF16 || dtype > MOE_MXFP4) return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
   return run_ffn(dtype, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
                  num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m, split,
-                 workspace, workspace_bytes, stream, n_shared);
+                 tune, workspace, workspace_bytes, stream, n_shared);
 }
-
-// Route counts from which moe_align_ws plans over chunks in three launches
-// (measured, K=4096 I=2048 E=288 top-8: the one-workgroup planner takes
-// 165 us for 65,536 routes, 11 us for 1,536).
-constexpr int64_t kChunkedRoutes = 16384;
 
 int moe_align_ws_size(int64_t T, int32_t top_k, int32_t E, int32_t n_shared, size_t* bytes) {
   if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
@@ -375,7 +454,7 @@ int moe_align_ws(const int32_t* topk_ids, int64_t T, int32_t top_k, int32_t E, i
     return n_shared ? moe_align_shared(topk_ids, T, top_k, E, n_shared, block_m, sorted_token_ids,
                                        expert_ids, num_tokens_post_padded, stream)
                     : moe_align(topk_ids, T, top_k, E, block_m, sorted_token_ids, expert_ids,
-                                num_tokens_post_padded, stream);
+                                num_tokens_post_padded, nullptr, 0, stream);
   int64_t rows, blocks;
   rc = moe_align_capacity(T, top_k + n_shared, E + n_shared, block_m, &rows, &blocks);
   if (rc) return rc;
@@ -427,12 +506,32 @@ int moe_route_align(const float* logits, int64_t T, int32_t E, int32_t top_k, in
   if (!aligned(num_tokens_post_padded, 4) || !aligned(ws, 16))
     return fail(MOE_ERR_ALIGN, "num_tokens_post_padded must be 4-byte and ws 16-byte aligned");
   if (ws_bytes < 256) return fail(MOE_ERR_WORKSPACE, "workspace too small: %zu < 256 bytes", ws_bytes);
+  // past 16,384 routes, with room for the chunk counts after the ticket: the
+  // router alone, then the chunked planner
+  size_t chunk = 0;
+  rc = moe_align_workspace_size(T, top_k, E, &chunk);
+  if (rc) return rc;
+  int* counts = (chunk > 0 && ws_bytes >= 256 + chunk)
+                    ? reinterpret_cast<int*>(static_cast<uint8_t*>(ws) + 256) : nullptr;
   hipError_t e = launch_route_align(logits, (int)T, E, top_k, block_m, topk_ids, topk_weights,
                                     sorted_token_ids, expert_ids, num_tokens_post_padded,
                                     (int)rows, (int)blocks, static_cast<int*>(ws),
-                                    static_cast<hipStream_t>(stream));
+                                    static_cast<hipStream_t>(stream), counts);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int fused_moe_down_combine(int32_t dtype, const void* w2, const void* w2_scale,
+                           const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                           const int32_t* num_tokens_post_padded, const float* topk_weights,
+                           void* out, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
+                           int32_t block_m, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (dtype < MOE_BF16 || dtype > MOE_MXFP4) return fail(MOE_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  // the split mode's layout without schedule overrides: moe_workspace_layout's offsets
+  return run_ffn(dtype, nullptr, nullptr, nullptr, nullptr, w2, w2_scale, sorted_token_ids,
+                 expert_ids, num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m,
+                 1, nullptr, workspace, workspace_bytes, stream, 0, true);
 }
 
 int moe_set_timing_events(void* before, void* after, int32_t which) {
@@ -497,7 +596,7 @@ int moe_select_block_m(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32
 }
 
 int moe_workspace_size(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
-                       int32_t block_m, int32_t split, size_t* bytes) {
+                       int32_t block_m, int32_t split, const moe_tune* tune, size_t* bytes) {
   if (!bytes) return fail(MOE_ERR_NULL, "bytes is NULL");
   int rc = check_ffn(dtype, T, K, N, E, top_k, block_m);
   if (rc) return rc;
@@ -505,7 +604,9 @@ int moe_workspace_size(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E
   if (split == 2 && block_m > 32)
     return fail(MOE_ERR_UNSUPPORTED, "the ring mode runs block_m 16 or 32 (got %d)", block_m);
   const int sp = split < 0 ? pick_split(dtype, T, K, N, E, top_k, block_m) : split;
-  *bytes = layout(dtype, T, K, N, E, top_k, block_m, sp).total;
+  rc = check_tune(dtype, K, block_m, sp, tune);
+  if (rc) return rc;
+  *bytes = layout(dtype, T, K, N, E, top_k, block_m, sp, tune).total;
   return ok();
 }
 
@@ -558,11 +659,11 @@ int moe_workspace_layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t
 int fused_moe_bf16(const void* x, const void* w1, const void* w2, const int32_t* sorted_token_ids,
                    const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                    const float* topk_weights, void* out, int64_t T, int64_t K, int64_t N, int32_t E,
-                   int32_t top_k, int32_t block_m, int32_t split, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   int32_t top_k, int32_t block_m, int32_t split, const moe_tune* tune,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   return run_ffn(MOE_BF16, x, nullptr, w1, nullptr, w2, nullptr, sorted_token_ids, expert_ids,
                  num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m, split,
-                 workspace, workspace_bytes, stream);
+                 tune, workspace, workspace_bytes, stream);
 }
 
 int fused_moe_fp8_blockwise(const void* x, const float* x_scale, const void* w1,
@@ -570,33 +671,33 @@ int fused_moe_fp8_blockwise(const void* x, const float* x_scale, const void* w1,
                             const int32_t* sorted_token_ids, const int32_t* expert_ids,
                             const int32_t* num_tokens_post_padded, const float* topk_weights,
                             void* out, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
-                            int32_t block_m, int32_t split, void* workspace,
+                            int32_t block_m, int32_t split, const moe_tune* tune, void* workspace,
                             size_t workspace_bytes, void* stream) {
   return run_ffn(MOE_FP8_BLOCKWISE, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids,
                  expert_ids, num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m,
-                 split, workspace, workspace_bytes, stream);
+                 split, tune, workspace, workspace_bytes, stream);
 }
 
 int fused_moe_mxfp8(const void* x, const uint8_t* x_scale, const void* w1, const uint8_t* w1_scale,
                     const void* w2, const uint8_t* w2_scale, const int32_t* sorted_token_ids,
                     const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                     const float* topk_weights, void* out, int64_t T, int64_t K, int64_t N,
-                    int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    int32_t E, int32_t top_k, int32_t block_m, int32_t split,
+                    const moe_tune* tune, void* workspace, size_t workspace_bytes, void* stream) {
   return run_ffn(MOE_MXFP8, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
                  num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m, split,
-                 workspace, workspace_bytes, stream);
+                 tune, workspace, workspace_bytes, stream);
 }
 
 int fused_moe_mxfp4(const void* x, const uint8_t* x_scale, const void* w1, const uint8_t* w1_scale,
                     const void* w2, const uint8_t* w2_scale, const int32_t* sorted_token_ids,
                     const int32_t* expert_ids, const int32_t* num_tokens_post_padded,
                     const float* topk_weights, void* out, int64_t T, int64_t K, int64_t N,
-                    int32_t E, int32_t top_k, int32_t block_m, int32_t split, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    int32_t E, int32_t top_k, int32_t block_m, int32_t split,
+                    const moe_tune* tune, void* workspace, size_t workspace_bytes, void* stream) {
   return run_ffn(MOE_MXFP4, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,
                  num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m, split,
-                 workspace, workspace_bytes, stream);
+                 tune, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -433,7 +433,7 @@ k_route_align(const float* __restrict__ logits, int T, int E, int top_k, int bm,
               int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
               int32_t* __restrict__ sorted, int32_t* __restrict__ expert_ids,
               int32_t* __restrict__ ntp_out, int sorted_cap, int blocks_cap,
-              int* __restrict__ ticket, int tokens_per_wg) {
+              int* __restrict__ ticket, int tokens_per_wg, int plan) {
   extern __shared__ int smem[];
   __shared__ int is_last;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -453,6 +453,7 @@ k_route_align(const float* __restrict__ logits, int T, int E, int top_k, int bm,
                          topk_w + (size_t)tb * top_k, lane);
     }
   }
+  if (!plan) return;  // the chunked planner runs in launches of its own
   if (gridDim.x == 1) {
     // one workgroup routed every token: a workgroup barrier publishes them
     __syncthreads();
@@ -478,7 +479,7 @@ k_route_align(const float* __restrict__ logits, int T, int E, int top_k, int bm,
 hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int block_m,
                               int32_t* topk_ids, float* topk_w, int32_t* sorted,
                               int32_t* expert_ids, int32_t* ntp, int sorted_cap, int blocks_cap,
-                              int* ticket, hipStream_t stream) {
+                              int* ticket, hipStream_t stream, int* chunk_counts) {
   const size_t smem = (size_t)(kWaves * E + 2 * E + kWaves + 1) * sizeof(int);
   // one token per wave up to 256 workgroups, then more tokens per wave
   const int want = (T + kWaves - 1) / kWaves;
@@ -488,13 +489,16 @@ hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int 
 #define MOE_ROUTE(N)                                                                          \
   hipLaunchKernelGGL(k_route_align<N>, dim3(groups), dim3(kThreads), smem, stream, logits, T, E, \
                      top_k, block_m, topk_ids, topk_w, sorted, expert_ids, ntp, sorted_cap,   \
-                     blocks_cap, ticket, per)
+                     blocks_cap, ticket, per, chunk_counts ? 0 : 1)
   if (epl <= 1) MOE_ROUTE(1);
   else if (epl <= 2) MOE_ROUTE(2);
   else if (epl <= 4) MOE_ROUTE(4);
   else if (epl <= 8) MOE_ROUTE(8);
   else MOE_ROUTE(16);
 #undef MOE_ROUTE
+  if (chunk_counts)
+    return launch_align_chunked(topk_ids, T * top_k, E, block_m, sorted, expert_ids, ntp,
+                                sorted_cap, blocks_cap, stream, T, 0, chunk_counts);
   return hipGetLastError();
 }
 

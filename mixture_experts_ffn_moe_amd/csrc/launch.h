@@ -38,6 +38,9 @@ struct MoeArgs {
   int kw;
   int* tickets;
   float* part;
+  // schedule overrides (0: the library's choice): K groups of the streaming
+  // gate/up kernels, their prefetch depth, the tiled kernels' stages
+  int ksplit, depth, stages;
 };
 
 // Ring mode sizing ([DeepGEMM #88] "How it works": the lag follows from the
@@ -118,11 +121,13 @@ hipError_t launch_align_chunked(const int32_t* topk_ids, int R, int E, int block
                                 int n_shared, int* counts);
 
 // Router (softmax, top-k, renormalized weights) and planner in one launch;
-// `ticket` is one int of workspace, zero before the call and after it.
+// `ticket` is one int of workspace, zero before the call and after it.  With
+// `chunk_counts` (align_chunked_ws(T * top_k, E) bytes) the launch only
+// routes, and the chunked planner follows.
 hipError_t launch_route_align(const float* logits, int T, int E, int top_k, int block_m,
                               int32_t* topk_ids, float* topk_w, int32_t* sorted,
                               int32_t* expert_ids, int32_t* ntp, int sorted_cap, int blocks_cap,
-                              int* ticket, hipStream_t stream);
+                              int* ticket, hipStream_t stream, int* chunk_counts = nullptr);
 
 // Events recorded around one kernel of a launch_moe sequence (profiling).
 struct TimingHook {
@@ -133,7 +138,12 @@ struct TimingHook {
 hipError_t launch_moe(int kind, int block_m, int split, const MoeArgs& a,
                       hipStream_t stream, const TimingHook& hook);
 
+// The split mode's down GEMM and combine alone, on the intermediate the
+// workspace already holds.
+hipError_t launch_down_combine(int kind, int block_m, const MoeArgs& a, hipStream_t stream);
+
 // LDS-tiled split-mode kernels (moe_tiled.hip) for many rows per expert.
 bool tiled_supported(int kind, int block_m, int K, int I);
 hipError_t launch_tiled(int kind, int block_m, const MoeArgs& a, hipStream_t stream,
                         const TimingHook& hook);
+hipError_t launch_tiled_down(int kind, int block_m, const MoeArgs& a, hipStream_t stream);

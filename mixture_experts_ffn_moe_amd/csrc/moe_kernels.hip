@@ -1128,16 +1128,55 @@ inline void mark(const TimingHook& h, int which, bool after, hipStream_t st) {
   if (h.which == which && h.before && h.after) (void)hipEventRecord(after ? h.after : h.before, st);
 }
 
-// Launch of the up-GEMM kernel (k_up or k_fused) with KSPLIT K groups.
-template <int KIND, int BM, int KSPLIT>
-void launch_up(int split, const MoeArgs& a, unsigned grid, hipStream_t st) {
+// Launch of the up-GEMM kernel (k_up or k_fused) with KSPLIT K groups and a
+// prefetch depth of D K steps.
+template <int KIND, int BM, int KSPLIT, int D>
+void launch_up_d(int split, const MoeArgs& a, unsigned grid, hipStream_t st) {
   constexpr int TH = BlockShape<BM, KSPLIT>::THREADS;
-  constexpr int D = prefetch_depth<KIND, BM, KSPLIT>();
   constexpr int MI = BlockShape<BM, KSPLIT>::MI, W = TH / 64;
   const size_t lds = is_mx(KIND) && scale_run<D>() == 4
                          ? (size_t)W * up_stage_bytes(a.K, MI, KSPLIT, W) : 0;
   if (split) hipLaunchKernelGGL((k_up<KIND, BM, D, KSPLIT>), dim3(grid), dim3(TH), lds, st, a);
   else hipLaunchKernelGGL((k_fused<KIND, BM, D, KSPLIT>), dim3(grid), dim3(TH), lds, st, a);
+}
+
+// The depth from the register budget, or the caller's (1, 2 or 4; the host
+// checks that it asked only at block_m 16 or 32).
+template <int KIND, int BM, int KSPLIT>
+void launch_up(int split, const MoeArgs& a, unsigned grid, hipStream_t st) {
+  if constexpr (BM <= 32) {
+    switch (a.depth) {
+      case 1: return launch_up_d<KIND, BM, KSPLIT, 1>(split, a, grid, st);
+      case 2: return launch_up_d<KIND, BM, KSPLIT, 2>(split, a, grid, st);
+      case 4: return launch_up_d<KIND, BM, KSPLIT, 4>(split, a, grid, st);
+      default: break;
+    }
+  }
+  launch_up_d<KIND, BM, KSPLIT, prefetch_depth<KIND, BM, KSPLIT>()>(split, a, grid, st);
+}
+
+// Down GEMM of the split mode (streaming kernel) at depth D.
+template <int KIND, int BM, int D>
+void launch_down_d(const MoeArgs& a, hipStream_t st) {
+  constexpr int THREADS = BlockShape<BM>::THREADS, W = THREADS / 64;
+  const int NT = (a.K + 255) / 256;
+  const size_t lds = is_mx(KIND) && scale_run<D>() == 4
+                         ? (size_t)W * stage_bytes(a.I / 128, BlockShape<BM>::MI, W) : 0;
+  hipLaunchKernelGGL((k_down<KIND, BM, D>), dim3((unsigned)a.blocks_cap * NT), dim3(THREADS), lds,
+                     st, a);
+}
+
+template <int KIND, int BM>
+void launch_down(const MoeArgs& a, hipStream_t st) {
+  if constexpr (BM <= 32) {
+    switch (a.depth) {
+      case 1: return launch_down_d<KIND, BM, 1>(a, st);
+      case 2: return launch_down_d<KIND, BM, 2>(a, st);
+      case 4: return launch_down_d<KIND, BM, 4>(a, st);
+      default: break;
+    }
+  }
+  launch_down_d<KIND, BM, prefetch_depth<KIND, BM>()>(a, st);
 }
 
 // K groups for the up GEMM: with few (block, slice) tiles (a narrow
@@ -1175,7 +1214,8 @@ void launch_up_sk(const MoeArgs& a, hipStream_t st) {
 template <int KIND, int BM>
 void launch_up_any(int split, const MoeArgs& a, unsigned grid, hipStream_t st) {
   if constexpr (BM <= 32) {
-    if (pick_ksplit<BM>(a) == 2) return launch_up<KIND, BM, 2>(split, a, grid, st);
+    const int ks = a.ksplit ? a.ksplit : pick_ksplit<BM>(a);
+    if (ks == 2) return launch_up<KIND, BM, 2>(split, a, grid, st);
   }
   launch_up<KIND, BM, 1>(split, a, grid, st);
 }
@@ -1284,13 +1324,8 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
       launch_up_any<KIND, BM>(1, a, (unsigned)a.blocks_cap * S, st);
     }
     mark(hk, 1, true, st);
-    const int NT = (a.K + 255) / 256;
     mark(hk, 2, false, st);
-    constexpr int W = THREADS / 64;
-    const size_t lds = is_mx(KIND) && scale_run<D>() == 4
-                           ? (size_t)W * stage_bytes(a.I / 128, BlockShape<BM>::MI, W) : 0;
-    hipLaunchKernelGGL((k_down<KIND, BM, D>), dim3((unsigned)a.blocks_cap * NT), dim3(THREADS), lds,
-                       st, a);
+    launch_down<KIND, BM>(a, st);
     mark(hk, 2, true, st);
     const int CT = (a.K + 1023) / 1024;
     hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
@@ -1304,6 +1339,50 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
     hipLaunchKernelGGL(k_finalize, dim3(grid_for((size_t)a.T * a.K / 4, 256)), dim3(256), 0, st, a);
   }
   return hipGetLastError();
+}
+
+// Flags of the routes a plan placed (what the gate/up kernels set), for a
+// down GEMM that runs without them.
+__global__ void __launch_bounds__(256) k_flag_routes(MoeArgs p) {
+  const int n = *p.ntp;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const int id = p.sorted[i];
+    if (id >= 0) p.flags[id] = 1;
+  }
+}
+
+// The split mode's down GEMM and combine alone, on the intermediate already
+// in the workspace.
+template <int KIND, int BM>
+hipError_t launch_down_combine_bm(const MoeArgs& a, hipStream_t st) {
+  const size_t fbytes = (total_routes(a) * 4 + 15) / 16;
+  hipLaunchKernelGGL(k_zero, dim3(grid_for(fbytes, 256)), dim3(256), 0, st,
+                     reinterpret_cast<uint4*>(a.flags), fbytes);
+  hipLaunchKernelGGL(k_flag_routes, dim3(grid_for((size_t)a.blocks_cap * BM, 256)), dim3(256), 0,
+                     st, a);
+  if (tiled_supported(KIND, BM, a.K, a.I)) {
+    hipError_t e = launch_tiled_down(KIND, BM, a, st);
+    if (e != hipSuccess) return e;
+  } else if constexpr (BM <= 128) {
+    launch_down<KIND, BM>(a, st);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  const int CT = (a.K + 1023) / 1024;
+  hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_down_combine_kind(int block_m, const MoeArgs& a, hipStream_t st) {
+  switch (block_m) {
+    case 16: return launch_down_combine_bm<KIND, 16>(a, st);
+    case 32: return launch_down_combine_bm<KIND, 32>(a, st);
+    case 64: return launch_down_combine_bm<KIND, 64>(a, st);
+    case 128: return launch_down_combine_bm<KIND, 128>(a, st);
+    case 256: return launch_down_combine_bm<KIND, 256>(a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 // block_m 256 exists only as the LDS-tiled split mode (e4m3, K % 256 == 0)
@@ -1335,6 +1414,16 @@ hipError_t launch_kind(int block_m, int split, const MoeArgs& a, hipStream_t st,
 }
 
 }  // namespace
+
+hipError_t launch_down_combine(int kind, int block_m, const MoeArgs& a, hipStream_t st) {
+  switch (kind) {
+    case KIND_BF16: return launch_down_combine_kind<KIND_BF16>(block_m, a, st);
+    case KIND_FP8B: return launch_down_combine_kind<KIND_FP8B>(block_m, a, st);
+    case KIND_MX: return launch_down_combine_kind<KIND_MX>(block_m, a, st);
+    case KIND_MX4: return launch_down_combine_kind<KIND_MX4>(block_m, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_moe(int kind, int block_m, int split, const MoeArgs& a, hipStream_t st,
                       const TimingHook& hk) {

@@ -519,9 +519,8 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
     }
 }
 
-template <int KIND, int BM>
-hipError_t launch_tiled_kind(const MoeArgs& a, hipStream_t st, const TimingHook& hk) {
-  constexpr int NS = BM == 256 ? 2 : 3;
+template <int KIND, int BM, int NS>
+hipError_t launch_tiled_ns(const MoeArgs& a, hipStream_t st, const TimingHook& hk) {
   constexpr int TH = TileCfg<KIND, BM, 256, NS>::THREADS;
   const int S = a.I / 128;
   const unsigned g_up = (unsigned)(((size_t)a.blocks_cap * S + 7) / 8 * 8);
@@ -535,11 +534,43 @@ hipError_t launch_tiled_kind(const MoeArgs& a, hipStream_t st, const TimingHook&
   return hipGetLastError();
 }
 
+template <int KIND, int BM>
+hipError_t launch_tiled_down_kind(const MoeArgs& a, hipStream_t st) {
+  constexpr int NS = BM == 256 ? 2 : 3;
+  constexpr int TH = TileCfg<KIND, BM, 256, NS>::THREADS;
+  const unsigned g_dn = (unsigned)(((size_t)a.blocks_cap * (a.K / 256) + 7) / 8 * 8);
+  hipLaunchKernelGGL((k_down_t<KIND, BM, NS>), dim3(g_dn), dim3(TH), 0, st, a);
+  return hipGetLastError();
+}
+
+// Stages: two for 256-row tiles (the LDS holds no third), three otherwise,
+// or the caller's two for 64- and 128-row tiles.
+template <int KIND, int BM>
+hipError_t launch_tiled_kind(const MoeArgs& a, hipStream_t st, const TimingHook& hk) {
+  if constexpr (BM == 256) {
+    return launch_tiled_ns<KIND, BM, 2>(a, st, hk);
+  } else {
+    if (a.stages == 2) return launch_tiled_ns<KIND, BM, 2>(a, st, hk);
+    return launch_tiled_ns<KIND, BM, 3>(a, st, hk);
+  }
+}
+
 }  // namespace
 
 bool tiled_supported(int kind, int block_m, int K, int I) {
   return (kind == KIND_FP8B || kind == KIND_MX) &&
          (block_m == 64 || block_m == 128 || block_m == 256) && K % 256 == 0 && I % 128 == 0;
+}
+
+hipError_t launch_tiled_down(int kind, int block_m, const MoeArgs& a, hipStream_t st) {
+  if (kind == KIND_FP8B) {
+    if (block_m == 256) return launch_tiled_down_kind<KIND_FP8B, 256>(a, st);
+    if (block_m == 128) return launch_tiled_down_kind<KIND_FP8B, 128>(a, st);
+    return launch_tiled_down_kind<KIND_FP8B, 64>(a, st);
+  }
+  if (block_m == 256) return launch_tiled_down_kind<KIND_MX, 256>(a, st);
+  if (block_m == 128) return launch_tiled_down_kind<KIND_MX, 128>(a, st);
+  return launch_tiled_down_kind<KIND_MX, 64>(a, st);
 }
 
 hipError_t launch_tiled(int kind, int block_m, const MoeArgs& a, hipStream_t st,

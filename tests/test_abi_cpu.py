@@ -50,12 +50,28 @@ def test_align_errors_before_launch():
     L = moe.lib()
     P = ctypes.c_void_p
     # E > 1024
-    assert L.moe_align(P(FAKE), 4, 2, 2000, 16, P(FAKE), P(FAKE), P(FAKE), None) == -3
+    assert L.moe_align(P(FAKE), 4, 2, 2000, 16, P(FAKE), P(FAKE), P(FAKE), None, 0, None) == -3
     # null outputs
-    assert L.moe_align(P(FAKE), 4, 2, 8, 16, None, P(FAKE), P(FAKE), None) == -1
+    assert L.moe_align(P(FAKE), 4, 2, 8, 16, None, P(FAKE), P(FAKE), None, 0, None) == -1
     # misaligned
-    assert L.moe_align(P(FAKE + 4), 4, 2, 8, 16, P(FAKE), P(FAKE), P(FAKE), None) == -4
+    assert L.moe_align(P(FAKE + 4), 4, 2, 8, 16, P(FAKE), P(FAKE), P(FAKE), None, 0,
+                       None) == -4
     assert b"aligned" in L.moe_last_error()
+    # misaligned workspace
+    assert L.moe_align(P(FAKE), 4096, 8, 8, 16, P(FAKE), P(FAKE), P(FAKE), P(FAKE + 4), 1 << 20,
+                       None) == -4
+
+
+def test_align_workspace_size():
+    """0 up to 16,384 routes (one workgroup plans), then 4 bytes per expert
+    and chunk of 512 routes (the chunked planner)."""
+    assert moe.moe_align_workspace_size(2048, 8, 288) == 0
+    assert moe.moe_align_workspace_size(2049, 8, 288) == 4 * 33 * 288
+    assert moe.moe_align_workspace_size(8192, 8, 288) == 4 * 128 * 288
+    for bad in ((-1, 8, 288), (8, 0, 288), (8, 8, 0)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_align_workspace_size(*bad)
+        assert ei.value.status == -2
 
 
 def test_route_align_errors_before_launch():
@@ -81,9 +97,10 @@ def test_route_align_errors_before_launch():
 
 
 def _ffn(L, fn, K=4096, N=4096, T=8, E=16, k=2, bm=16, split=-1, ws=FAKE, ws_bytes=1 << 40,
-         x=FAKE, sorted_ids=FAKE, scales=True):
+         x=FAKE, sorted_ids=FAKE, scales=True, tune=None):
     P = ctypes.c_void_p
     tail = [P(sorted_ids), P(FAKE), P(FAKE), P(FAKE), P(FAKE), T, K, N, E, k, bm, split,
+            None if tune is None else ctypes.byref(moe.MoeTune(**tune)),
             P(ws) if ws else None, ws_bytes, None]
     if fn == "fused_moe_bf16":
         return getattr(L, fn)(P(x), P(FAKE), P(FAKE), *tail)
@@ -119,6 +136,52 @@ def test_ffn_errors_before_launch(fn):
         assert _ffn(L, fn, scales=False) == -1
     # T == 0 is a successful no-op (no launch)
     assert _ffn(L, fn, T=0) == 0
+
+
+@pytest.mark.parametrize("fn", ["fused_moe_bf16", "fused_moe_fp8_blockwise", "fused_moe_mxfp8",
+                                "fused_moe_mxfp4"])
+def test_tune_errors_before_launch(fn):
+    """Every set field of moe_tune must name a variant the call's kernels
+    have; otherwise MOE_ERR_UNSUPPORTED before any launch."""
+    L = moe.lib()
+    tiled = fn in ("fused_moe_fp8_blockwise", "fused_moe_mxfp8")
+    for field, bad in (("k_groups", 3), ("k_split", 2), ("prefetch", 3), ("stages", 4),
+                       ("k_groups", -1)):
+        assert _ffn(L, fn, split=1, tune={field: bad}) == -3, (field, bad)
+        assert b"tune." + field.encode() in L.moe_last_error()
+    # a field for kernels the call does not run
+    assert _ffn(L, fn, bm=64, split=1, tune={"k_groups": 2}) == -3
+    assert _ffn(L, fn, bm=64, split=1, tune={"prefetch": 2}) == -3
+    assert _ffn(L, fn, bm=16, split=2, tune={"prefetch": 2}) == -3     # ring mode
+    assert _ffn(L, fn, bm=16, split=1, tune={"stages": 2}) == -3       # streaming kernels
+    assert _ffn(L, fn, bm=64, split=0, tune={"stages": 2}) == -3       # fused mode
+    if not tiled:
+        assert _ffn(L, fn, bm=64, split=1, tune={"stages": 2}) == -3   # no tiled kernels
+    assert _ffn(L, fn, K=1024, bm=16, split=1, tune={"k_split": 4}) == -3   # K / 128 < 16
+    assert _ffn(L, fn, K=2176, bm=16, split=1, tune={"k_split": 4}) == -3   # not a multiple of 8
+    assert _ffn(L, fn, bm=16, split=0, tune={"k_split": 4}) == -3
+    assert _ffn(L, fn, bm=16, split=1, tune={"k_split": 4, "k_groups": 1}) == -3
+    assert _ffn(L, fn, bm=16, split=1, tune={"k_split": 4, "prefetch": 2}) == -3
+    assert _ffn(L, fn, K=128, bm=16, split=1, tune={"k_groups": 2}) == -3   # one K step
+    # supported overrides pass the checks (the call then stops at T == 0)
+    ok = [{"k_groups": 1}, {"k_groups": 2}, {"k_split": 4}, {"k_split": 1, "prefetch": 1},
+          {"prefetch": 2}, {"prefetch": 4}, {"k_groups": 2, "prefetch": 4}]
+    for t in ok:
+        assert _ffn(L, fn, T=0, bm=16, split=1, tune=t) == 0, t
+        assert _ffn(L, fn, T=0, bm=32, split=0, tune={k: v for k, v in t.items()
+                                                         if k != "k_split"}) == 0, t
+    if tiled:
+        for st in (2, 3):
+            assert _ffn(L, fn, T=0, bm=128, split=1, tune={"stages": st}) == 0
+        assert _ffn(L, fn, bm=256, split=1, tune={"stages": 3}) == -3  # 256 rows: two stages
+    # the same checks in moe_workspace_size, which also sizes the K-split sums
+    dt = {"fused_moe_bf16": "bf16", "fused_moe_fp8_blockwise": "fp8_blockwise",
+          "fused_moe_mxfp8": "mxfp8", "fused_moe_mxfp4": "mxfp4"}[fn]
+    plain = moe.moe_workspace_size(dt, 2048, 4096, 4096, 256, 6, 16, 1, {"k_split": 1})
+    split4 = moe.moe_workspace_size(dt, 2048, 4096, 4096, 256, 6, 16, 1, {"k_split": 4})
+    assert split4 > plain
+    with pytest.raises(moe.MoeError):
+        moe.moe_workspace_size(dt, 8, 4096, 4096, 256, 6, 16, 1, {"prefetch": 3})
 
 
 def test_workspace_sizes_grow_with_tokens():

@@ -40,13 +40,25 @@ CASES = [
 ]
 
 
+SENTINEL = 0x7F7F7F7F
+
+
+def _outputs(T, k, E, bm, S=0):
+    """Planner outputs pre-filled with a sentinel: the planner must write
+    every element of the capacity (ids, -1 padding and the count)."""
+    rows, blocks = moe.moe_align_capacity(T, k + S, E + S, bm)
+    return (torch.full((max(rows, 1),), SENTINEL, dtype=torch.int32, device="cuda")[:rows],
+            torch.full((max(blocks, 1),), SENTINEL, dtype=torch.int32, device="cuda")[:blocks],
+            torch.full((1,), SENTINEL, dtype=torch.int32, device="cuda"))
+
+
 @pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("kind,T,E,k", CASES)
 def test_align_bit_exact(kind, T, E, k, bm):
     say(f"[gpu] align kind={kind} T={T} E={E} k={k} bm={bm}")
     ids = _routing(kind, T, E, k, T * 7 + E)
     s_ref, e_ref, n_ref = align_ref(ids.numpy(), E, bm)
-    s, e, n = moe.moe_align(ids.cuda(), E, bm)
+    s, e, n = moe.moe_align(ids.cuda(), E, bm, out=_outputs(T, k, E, bm), workspace=None)
     torch.cuda.synchronize()
     assert int(n.item()) == n_ref
     assert np.array_equal(s.cpu().numpy(), s_ref)
@@ -83,11 +95,16 @@ def test_align_chunked_bit_exact(kind, T, E, k, bm):
     s_ref, e_ref, n_ref = align_ref(ids.numpy(), E, bm)
     # a workspace full of garbage: the chunk counts must not depend on it
     ws = torch.full((moe.moe_align_ws_size(T, k, E),), 0x5A, dtype=torch.uint8, device="cuda")
-    s, e, n = moe.moe_align_ws(ids.cuda(), E, bm, workspace=ws)
+    s, e, n = moe.moe_align_ws(ids.cuda(), E, bm, workspace=ws, out=_outputs(T, k, E, bm))
     torch.cuda.synchronize()
     assert int(n.item()) == n_ref
     assert np.array_equal(s.cpu().numpy(), s_ref)
     assert np.array_equal(e.cpu().numpy(), e_ref)
+    # moe_align with its workspace runs the same chunked plan
+    assert moe.moe_align_workspace_size(T, k, E) == ws.numel()
+    s2, e2, n2 = moe.moe_align(ids.cuda(), E, bm, workspace=ws, out=_outputs(T, k, E, bm))
+    torch.cuda.synchronize()
+    assert torch.equal(s2, s) and torch.equal(e2, e) and torch.equal(n2, n)
 
 
 @pytest.mark.parametrize("S", [1, 2])
@@ -112,3 +129,24 @@ def test_align_ws_small_is_moe_align():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("T,E,k,bm", [(4096, 288, 8, 128), (8192, 288, 8, 256), (3000, 64, 6, 64)])
+def test_route_align_chunked_planner(T, E, k, bm):
+    """Past 16,384 routes with room for the chunk counts, moe_route_align
+    routes in one launch and plans with the chunked planner: the outputs
+    equal the router oracle's ids and moe_align's plan of them."""
+    from oracle.router import route_ref
+    g = torch.Generator().manual_seed(T + E)
+    logits = torch.randn(T, E, generator=g)
+    need = moe.moe_route_align_workspace_size() + moe.moe_align_workspace_size(T, k, E)
+    assert need > 256 or T * k <= 16384
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ids, w, s, e, n = moe.moe_route_align(logits.cuda(), k, bm, workspace=ws)
+    torch.cuda.synchronize()
+    ids_ref, _ = route_ref(logits.numpy(), k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    s_ref, e_ref, n_ref = align_ref(ids_ref, E, bm)
+    assert int(n.item()) == n_ref
+    assert np.array_equal(s.cpu().numpy(), s_ref) and np.array_equal(e.cpu().numpy(), e_ref)
+    assert not bool(ws[:256].any())      # the ticket is back at zero

@@ -95,7 +95,7 @@ def test_graph_replay_matches_eager(kind, T, E, k, bm, split, shp):
         say(f"      replay {r}: {diff} of {got.size} outputs differ from the eager call")
         if split == 0:
             ref = oracle(c)
-            ok, stats = tolerance_check(got, ref["out64"], TOL[kind], ref["flip_bound"])
+            ok, stats = tolerance_check(got, ref["out64"], TOL[kind], ref["allowance"])
             say(f"      oracle {stats}")
             assert ok, stats
         else:

@@ -86,11 +86,14 @@ def _adjacent(a, b, sign):
 @pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
 def test_split_intermediate_matches_oracle(kind):
     """The requantized intermediate the split mode writes (values and scales)
-    against the oracle's: scales equal up to fp32 summation noise, every code
-    equal or one rounding step away, and such one-step flips rare.  A flip
-    happens where the GPU's fp32 h (its own summation order) and the oracle's
-    sit on either side of a rounding boundary; with |dh|/h ~ 3e-5 and e4m3's
-    2^-3 relative spacing that is a few per thousand codes."""
+    against the oracle's.  Every code equals the oracle's, except where the
+    oracle flags the decision as a near-tie (alt > 0: the GPU's fp32 h, with
+    its own summation order, may lie on the other side of the rounding
+    boundary), and then it is the neighbouring code.  Blockwise scales lie
+    within the oracle's bound on their deviation; an MX shared exponent
+    differs only in a group the oracle flags, whose codes are then the other
+    exponent's.  The number of flipped decisions stays within what the
+    oracle's model expects (the sum of its flip probabilities)."""
     c = small_case(kind, T=40, E=4, k=2)
     bm = 16
     K, I, E, k = c.K, c.I, c.E, c.top_k
@@ -105,31 +108,44 @@ def test_split_intermediate_matches_oracle(kind):
     n = int(ntp.item())
     wsn = ws.cpu().numpy()
     es = 2 if kind == "bf16" else 1
+    sign = 0x8000 if es == 2 else 0x80
     flips = total = scale_flips = 0
+    expected = 0.0
     for pos in range(n):
         rid = int(sid[pos])
         if rid < 0:
             continue
-        q_ref, s_ref, _ = ref[rid]
+        q_ref, s_ref, _, alt, info = ref[rid]
         row = wsn[h_off + pos * I * es: h_off + (pos + 1) * I * es]
         if kind == "bf16":
             row = row.view(np.uint16)
         keep = np.ones(I, bool)
         if kind == "fp8_blockwise":
             srow = wsn[hs_off + pos * (I // 128) * 4: hs_off + (pos + 1) * (I // 128) * 4]
-            np.testing.assert_allclose(srow.view(np.float32), s_ref, rtol=1e-4)
+            rel = np.abs(srow.view(np.float32).astype(np.float64) / s_ref - 1.0)
+            assert np.all(rel <= info["scale_rel"] + 2.0 ** -23), (pos, rel, info["scale_rel"])
         if kind in ("mxfp8", "mxfp4"):
             srow = wsn[hs_off + pos * (I // 32): hs_off + (pos + 1) * (I // 32)]
             moved = srow != s_ref          # power-of-two scale decided the other way
-            assert np.all(np.abs(srow.astype(int) - s_ref.astype(int)) <= 1)
+            assert np.all(info["moved"][moved]), (pos, np.nonzero(moved))
             scale_flips += int(moved.sum())
+            for gi in np.nonzero(moved)[0]:
+                sl = slice(32 * gi, 32 * gi + 32)
+                s_alt = int(srow[gi]) - 127
+                q_alt = codecs.e4m3_encode((codecs.e4m3_decode(q_ref[sl]) * 2.0 ** (int(s_ref[gi]) - 127)
+                                            + info["dhd"][sl]) * 2.0 ** -s_alt)
+                same = row[sl] == q_alt
+                assert np.all(same | ((info["alt2"][sl] > 0) & _adjacent(row[sl], q_alt, sign))), pos
             keep = ~np.repeat(moved, 32)
-        assert np.all(_adjacent(row[keep], q_ref[keep], 0x8000 if es == 2 else 0x80)), pos
-        flips += int(np.sum(row[keep] != q_ref[keep]))
+        diff = row[keep] != q_ref[keep]
+        assert np.all(alt[keep][diff] > 0), (pos, np.nonzero(diff))
+        assert np.all(_adjacent(row[keep][diff], q_ref[keep][diff], sign)), pos
+        flips += int(diff.sum())
         total += int(keep.sum())
-    say(f"      intermediate code flips {flips}/{total}, scale flips {scale_flips}")
-    assert flips <= max(2, total // 100)
-    assert scale_flips <= max(1, n * (I // 32) // 100)
+        expected += float(np.sum(info["prob"]))
+    say(f"      intermediate code flips {flips}/{total} (model expects {expected:.1f}), "
+        f"scale flips {scale_flips}")
+    assert flips <= expected + 5 * np.sqrt(expected) + 3
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])

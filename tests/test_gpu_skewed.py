@@ -36,9 +36,7 @@ def block_rows(align, bm):
 @pytest.mark.parametrize("kind,bm", [("fp8_blockwise", 64), ("fp8_blockwise", 128),
                                      ("fp8_blockwise", 256), ("mxfp8", 64), ("mxfp8", 128)])
 def test_skewed_plan(kind, bm):
-    # (the MX seed avoids one whose requantization near-ties exceed the strict
-    # share of the oracle gate on every path, 16-row streaming included)
-    c = skewed_case(kind, 300, 24, 4, 512, 256, f"mixed-{kind}-{bm}" + ("-b" if kind == "mxfp8" else ""))
+    c = skewed_case(kind, 300, 24, 4, 512, 256, f"mixed-{kind}-{bm}")
     out, align, ref = check(c, bm, 1, label="skewed")
     rows = block_rows(align, bm)
     small = int(((rows[:, 16:] >= 0).sum(axis=1) == 0).sum())
@@ -72,7 +70,7 @@ def test_routes_behind_padding(bm):
     torch.cuda.synchronize()
     got = out_bits(out)
     ref = oracle(c)
-    ok, stats = tolerance_check(got, ref["out64"], TOL[kind], ref["flip_bound"])
+    ok, stats = tolerance_check(got, ref["out64"], TOL[kind], ref["allowance"])
     say(f"      stats {stats}")
     assert ok, stats
     # the same routes in other rows of the tiles: equal up to summation order
