@@ -399,6 +399,31 @@ int fused_moe_fp8_blockwise(const void* x, const float* x_scale,
                             int32_t block_m, int32_t split, const moe_tune* tune,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * blockwise FP8 path of fused_moe_fp8_blockwise with no workspace argument
+ * and no tune.  The workspace is a static array of 64 MiB that the library
+ * holds on every GPU it runs on until the process ends (enough for the
+ * decode sizes at K = 4096, I = 2048, e.g. T = 256 with top-6 over 256
+ * experts and block_m 16, split mode).  A call whose moe_workspace_size(.., NULL)
+ * exceeds 64 MiB fails with MOE_ERR_WORKSPACE before anything is launched.
+ * Nothing is allocated: the array's address on the current device is looked
+ * up once (hipGetSymbolAddress) on that device's first call.  Every call on
+ * one GPU shares that GPU's array, so calls that may overlap on one GPU (two
+ * streams, two threads) race and must be serialized by the caller; the
+ * kernels clear what they count on, so the contents a previous call left do
+ * not matter.  Otherwise exactly fused_moe_fp8_blockwise (same arguments,
+ * results and errors). */
+int fused_moe_fp8_blockwise_noalloc(const void* x, const float* x_scale,
+                                    const void* w1, const float* w1_scale,
+                                    const void* w2, const float* w2_scale,
+                                    const int32_t* sorted_token_ids,
+                                    const int32_t* expert_ids,
+                                    const int32_t* num_tokens_post_padded,
+                                    const float* topk_weights, void* out, int64_t T,
+                                    int64_t K, int64_t N, int32_t E, int32_t top_k,
+                                    int32_t block_m, int32_t split, void* stream);
+
 /* MXFP8 path ([prime-flash] "Scale layout (mxfp8)": e4m3 values with e8m0
  * scales per 32 along K, activation scales row-major; the intermediate is
  * requantized to mxfp8 on chip before the down GEMM, shared exponent

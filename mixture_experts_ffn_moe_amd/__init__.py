@@ -34,6 +34,7 @@ __all__ = [
     "fused_moe_fp8_blockwise", "fused_moe_mxfp8", "fused_moe_mxfp4", "EXPORTED_SYMBOLS",
     "moe_route_align", "moe_route_align_workspace_size", "moe_align_shared", "fused_moe_shared",
     "moe_mfma_probe", "moe_align_workspace_size", "MoeTune", "fused_moe_down_combine",
+    "fused_moe_fp8_blockwise_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
@@ -49,7 +50,7 @@ EXPORTED_SYMBOLS = (
     "moe_set_timing_events", "moe_route_align_workspace_size", "moe_route_align",
     "moe_align_shared", "fused_moe_shared", "moe_ring_layout", "moe_ring_schedule",
     "moe_select_block_m_routed", "moe_align_ws_size", "moe_align_ws", "moe_mfma_probe",
-    "moe_align_workspace_size", "fused_moe_down_combine",
+    "moe_align_workspace_size", "fused_moe_down_combine", "fused_moe_fp8_blockwise_noalloc",
 )
 
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_UNSUPPORTED",
@@ -104,6 +105,8 @@ def lib():
     L.fused_moe_fp8_blockwise.argtypes = [_P, _P, _P, _P, _P, _P] + tail
     L.fused_moe_mxfp8.argtypes = [_P, _P, _P, _P, _P, _P] + tail
     L.fused_moe_mxfp4.argtypes = [_P, _P, _P, _P, _P, _P] + tail
+    L.fused_moe_fp8_blockwise_noalloc.argtypes = [_P] * 11 + [_I64, _I64, _I64, _I32, _I32,
+                                                              _I32, _I32, _P]
     L.moe_set_timing_events.argtypes = [_P, _P, _I32]
     L.moe_mfma_probe.argtypes = [_I32, _P, _P, _P, _P, _P, _P, _I64, _P]
     L.fused_moe_down_combine.argtypes = [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64,
@@ -424,6 +427,23 @@ def fused_moe_fp8_blockwise(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token
                 [x, x_scale, w1, w1_scale, w2, w2_scale], w1, sorted_token_ids, expert_ids,
                 num_tokens_post_padded, topk_weights, top_k, block_m, split, out, workspace,
                 stream, T, K, tune)
+
+
+def fused_moe_fp8_blockwise_noalloc(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids,
+                                    expert_ids, num_tokens_post_padded, topk_weights, top_k,
+                                    block_m, split=-1, out=None, stream=None):
+    """fused_moe_fp8_blockwise with the library's static workspace (no
+    workspace argument; the caller provides ``out``, or it is allocated here
+    by torch before the call)."""
+    T, K = x.shape
+    E, N, _ = w1.shape
+    if out is None:
+        out = torch.empty(T, K, dtype=torch.bfloat16, device=x.device)
+    _check(lib().fused_moe_fp8_blockwise_noalloc(
+        _ptr(x), _ptr(x_scale), _ptr(w1), _ptr(w1_scale), _ptr(w2), _ptr(w2_scale),
+        _ptr(sorted_token_ids), _ptr(expert_ids), _ptr(num_tokens_post_padded),
+        _ptr(topk_weights), _ptr(out), T, K, N, E, top_k, block_m, split, _stream(stream)))
+    return out
 
 
 def fused_moe_mxfp8(x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids, expert_ids,

@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "device.h"
@@ -330,6 +331,39 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
                      : launch_moe(kind, block_m, sp, a, static_cast<hipStream_t>(stream), g_hook);
   if (e != hipSuccess) return fail(MOE_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+// Workspace of fused_moe_fp8_blockwise_noalloc: device memory the library
+// holds on every GPU it runs on until the process ends.  Host code never
+// uses this name as an address (on the host it is a stand-in, not device
+// memory): each device's address comes from hipGetSymbolAddress, taken once
+// with that device current.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch`, looked up on the first call made with the
+// device current.
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the %d this library tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -676,6 +710,31 @@ int fused_moe_fp8_blockwise(const void* x, const float* x_scale, const void* w1,
   return run_ffn(MOE_FP8_BLOCKWISE, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids,
                  expert_ids, num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m,
                  split, tune, workspace, workspace_bytes, stream);
+}
+
+int fused_moe_fp8_blockwise_noalloc(const void* x, const float* x_scale, const void* w1,
+                                    const float* w1_scale, const void* w2, const float* w2_scale,
+                                    const int32_t* sorted_token_ids, const int32_t* expert_ids,
+                                    const int32_t* num_tokens_post_padded,
+                                    const float* topk_weights, void* out, int64_t T, int64_t K,
+                                    int64_t N, int32_t E, int32_t top_k, int32_t block_m,
+                                    int32_t split, void* stream) {
+  size_t need = 0;
+  int rc = moe_workspace_size(MOE_FP8_BLOCKWISE, T, K, N, E, top_k, block_m, split, nullptr,
+                              &need);
+  if (rc) return rc;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_WORKSPACE,
+                "the call needs %zu workspace bytes, beyond the %zu of the library's static "
+                "scratch; use fused_moe_fp8_blockwise with a workspace",
+                need, kScratchBytes);
+  if (T == 0) return ok();
+  void* ws = nullptr;
+  rc = scratch_for_current_device(&ws);
+  if (rc) return rc;
+  return run_ffn(MOE_FP8_BLOCKWISE, x, x_scale, w1, w1_scale, w2, w2_scale, sorted_token_ids,
+                 expert_ids, num_tokens_post_padded, topk_weights, out, T, K, N, E, top_k, block_m,
+                 split, nullptr, ws, kScratchBytes, stream);
 }
 
 int fused_moe_mxfp8(const void* x, const uint8_t* x_scale, const void* w1, const uint8_t* w1_scale,

@@ -249,3 +249,18 @@ def test_align_ws_sizes_and_errors():
                           1 << 30, None) == -3                     # E > 1024
     with pytest.raises(moe.MoeError):
         moe.moe_align_ws_size(8, 6, 256, -1)
+
+
+def test_noalloc_rejects_before_launch():
+    """The static-workspace entry point: a call needing more than its 64 MiB
+    fails before any HIP call; so do the ordinary argument checks."""
+    L = moe.lib()
+    P = ctypes.c_void_p
+    f = P(FAKE)
+    assert L.fused_moe_fp8_blockwise_noalloc(*([f] * 11), 4096, 4096, 4096, 256, 6, 64, 1,
+                                             None) == -5
+    assert b"static scratch" in L.moe_last_error()
+    assert L.fused_moe_fp8_blockwise_noalloc(*([f] * 11), 8, 4000, 4096, 256, 6, 16, 1,
+                                             None) == -3   # K % 128
+    assert L.fused_moe_fp8_blockwise_noalloc(*([f] * 11), 0, 4096, 4096, 256, 6, 16, 1,
+                                             None) == 0    # T == 0: no-op
