@@ -591,7 +591,7 @@ def main():
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--split", type=int, default=-1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--cpu-tokens", type=int, default=24)
     ap.add_argument("--calls", type=int, default=200,
                     help="per-call timed calls (warm) for the median / p10 / p90")
     ap.add_argument("--cold-calls", type=int, default=50,
