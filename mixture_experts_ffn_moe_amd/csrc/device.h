@@ -190,11 +190,18 @@ __device__ __forceinline__ f32x4 mfma_step_scaled(const Frag<KIND>& a, const Fra
   }
 }
 
-// silu(g) * u in fp32: g / (1 + 2^(-g*log2 e)) with the hardware exp2 and an
-// IEEE division.
+// silu(g) * u in fp32: g / (1 + 2^(-g*log2 e)) with the hardware exp2 and a
+// refined hardware reciprocal in place of an IEEE division (about 10 VALU
+// instructions fewer per element; the result is within about one ulp).
 __device__ __forceinline__ float swiglu(float g, float u) {
-  float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
-  return g / (1.0f + e) * u;
+  // e^-g as 2^(-g log2 e), the exponent capped at 126 so that 1 + e and its
+  // reciprocal stay finite and normal (past the cap silu(g) is below 1e-36)
+  const float e = __builtin_amdgcn_exp2f(__builtin_fminf(-g * 1.4426950408889634f, 126.0f));
+  const float d = 1.0f + e;
+  // 1 / d: the hardware reciprocal (1 ulp) refined by one Newton step
+  float r = __builtin_amdgcn_rcpf(d);
+  r = __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+  return g * r * u;
 }
 
 // fp32 -> e4m3 code, round to nearest even, saturating at +-448.  The

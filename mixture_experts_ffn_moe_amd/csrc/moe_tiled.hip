@@ -100,13 +100,16 @@ struct TileSrc {
 
 // Issue the DMA loads of K step `ks` into stage slot `st` of the pipeline
 // area at LDS address `lds` (a wave-uniform byte address).
-//  a_off[t] / b_off[t]: this lane's byte offsets of its A / B chunks (t-th load)
+//  a_off[t]           : this lane's byte offset of its A chunk (t-th load)
+//  b_off + b_soff[t]  : the same for B, a lane offset plus a wave-uniform
+//                       offset per load (the weight rows of one tile are
+//                       contiguous, so only the lane part varies)
 //  sa_off / sb_off    : this lane's scale row offsets; sa_step bytes per step
 template <int KIND, int BM, int BN, int NS>
 __device__ __forceinline__ void tile_load(const TileSrc& src, uint32_t lds, int st, int ks,
                                           const uint32_t (&a_off)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
-                                          uint32_t sa_off, uint32_t sa_step,
-                                          const uint32_t (&b_off)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
+                                          uint32_t sa_off, uint32_t sa_step, uint32_t b_off,
+                                          const uint32_t (&b_soff)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
                                           uint32_t sb_off) {
   using C = TileCfg<KIND, BM, BN, NS>;
   const uint32_t w = (uint32_t)wave_id();
@@ -116,7 +119,7 @@ __device__ __forceinline__ void tile_load(const TileSrc& src, uint32_t lds, int 
   for (int t = 0; t < C::A_INSTR; ++t) dma16(src.ra, stage + (w + C::NW * t) * 1024, a_off[t], soff);
 #pragma unroll
   for (int t = 0; t < C::B_INSTR; ++t)
-    dma16(src.rb, stage + C::A_BYTES + (w + C::NW * t) * 1024, b_off[t], soff);
+    dma16(src.rb, stage + C::A_BYTES + (w + C::NW * t) * 1024, b_off, soff + b_soff[t]);
   // row scales: wave w stages rows [w * SA_ROWS, (w + 1) * SA_ROWS) in its 64
   // slots.  All lanes load (lanes past SA_ROWS fill padding from an in-bounds
   // row): a lane-dependent branch around the asm would put its scalar
@@ -150,7 +153,7 @@ template <int ROWS>
 __device__ __forceinline__ int scale_slot(int row) { return (row / ROWS) * 64 + row % ROWS; }
 
 // Compute one staged K step (stage at `stage`, logical step ks).
-template <int KIND, int BM, int BN, int NS>
+template <int KIND, int BM, int BN, int NS, bool B_NEXT>
 __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const StepScales& sc1,
                                           const StepScales& sc2, int up_split,
                                           f32x4 (&acc)[4][TileCfg<KIND, BM, BN, NS>::NI]) {
@@ -217,7 +220,24 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
         for (int i4 = 0; i4 < 4; ++i4)
           acc[mi][ni][i4] += tt[mi][i4] * (sa[mi][i4] * (ni < up_split ? s1 : s2));
     };
-    if constexpr (C::NW == 8) {
+    if constexpr (C::NW == 8 && B_NEXT) {
+      // two waves share each SIMD and fill each other's MFMA gaps; column
+      // ni + 1's B fragment is read while column ni's MFMAs run (gate/up
+      // GEMM at K=4096, I=2048, E=288, top-8, T=8192, 256-row tiles: 1.70 ->
+      // 1.58 ms)
+      Frag<KIND_FP8B> fb2[2];
+      lds_frag(fb2[0], tb, brow_of(0), g);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        if (ni + 1 < NI) lds_frag(fb2[(ni + 1) & 1], tb, brow_of(ni + 1), g);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          t[0][mi] = mfma_step<KIND_FP8B>(fa[mi], fb2[ni & 1], z);
+        }
+        promote(ni, t[0]);
+      }
+    } else if constexpr (C::NW == 8) {
       // two waves share each SIMD and fill each other's MFMA gaps; no
       // lookahead, which keeps the wave within 256 registers
 #pragma unroll
@@ -259,11 +279,11 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
 
 // One workgroup tile: acc[mi][ni] over all K steps, visiting the steps from
 // a staggered start, NS stages in flight (stage slots in one LDS array).
-template <int KIND, int BM, int BN, int NS>
+template <int KIND, int BM, int BN, int NS, bool B_NEXT = false>
 __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, int ksteps,
                                           const uint32_t (&a_off)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
-                                          uint32_t sa_off, uint32_t sa_step,
-                                          const uint32_t (&b_off)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
+                                          uint32_t sa_off, uint32_t sa_step, uint32_t b_off,
+                                          const uint32_t (&b_soff)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
                                           uint32_t sb_off, int up_split, int group,
                                           f32x4 (&acc)[4][TileCfg<KIND, BM, BN, NS>::NI]) {
   using C = TileCfg<KIND, BM, BN, NS>;
@@ -292,7 +312,8 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, int
   auto step_at = [&](int i) { const int k = i + rot; return k >= ksteps ? k - ksteps : k; };
   const uint32_t lbase = lds_addr(smem);
   auto load = [&](int slot, int i) {
-    tile_load<KIND, BM, BN, NS>(src, lbase, slot, step_at(i), a_off, sa_off, sa_step, b_off, sb_off);
+    tile_load<KIND, BM, BN, NS>(src, lbase, slot, step_at(i), a_off, sa_off, sa_step, b_off, b_soff,
+                                sb_off);
   };
 #pragma unroll
   for (int u = 0; u < NS - 1; ++u)
@@ -305,7 +326,8 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, int
     lds_barrier();
     const int ahead = slot + NS - 1;
     if (i + NS - 1 < ksteps) load(ahead >= NS ? ahead - NS : ahead, i + NS - 1);
-    tile_step<KIND, BM, BN, NS>(smem + slot * C::STAGE, step_at(i), sc1, sc2, up_split, acc);
+    tile_step<KIND, BM, BN, NS, B_NEXT>(smem + slot * C::STAGE, step_at(i), sc1, sc2, up_split,
+                                        acc);
     slot = slot + 1 == NS ? 0 : slot + 1;
   }
   __syncthreads();  // the caller reuses the LDS
@@ -337,19 +359,22 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   TileSrc src;
   src.ra = make_desc(p.x, (uint32_t)((size_t)p.T * K));
   src.rb = make_desc(p.w1 + (size_t)e * N * K, (uint32_t)((size_t)N * K));
-  uint32_t a_off[C::A_INSTR], b_off[C::B_INSTR];
+  uint32_t a_off[C::A_INSTR], b_soff[C::B_INSTR];
 #pragma unroll
   for (int t = 0; t < C::A_INSTR; ++t) {
     int row, q;
     dma_rows<C::NW>(t, row, q);
     a_off[t] = (uint32_t)route_token(p, ids[row]) * K + q * 16;
   }
+  // B rows [0,128): the gate slice's weight rows; [128,256): the up slice's.
+  // Load t's rows are load 0's plus NW * 8 * t, all on one side of 128.
+  int brow0, bq;
+  dma_rows<C::NW>(0, brow0, bq);
+  const uint32_t b_off = (uint32_t)(s * 128 + brow0) * K + bq * 16;
 #pragma unroll
   for (int t = 0; t < C::B_INSTR; ++t) {
-    int row, q;
-    dma_rows<C::NW>(t, row, q);  // rows [0,128): gate slice rows; [128,256): up slice rows
-    const int n = (row < 128 ? s * 128 + row : I + s * 128 + row - 128);
-    b_off[t] = (uint32_t)n * K + q * 16;
+    const int d = C::NW * 8 * t;
+    b_soff[t] = (uint32_t)(d < 128 ? d : I - 128 + d) * K;
   }
   const int srow = wid * C::SA_ROWS + lane;  // scale row this lane stages
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
@@ -370,8 +395,8 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
     src.bsc2 = nullptr;
   }
   f32x4 acc[MI][NI];
-  tile_gemm<KIND, BM, 256, NS>(src, smem, KS, a_off, sa_off, sa_step, b_off, sb_off, HALF,
-                               e, acc);
+  tile_gemm<KIND, BM, 256, NS, true>(src, smem, KS, a_off, sa_off, sa_step, b_off, b_soff, sb_off,
+                                     HALF, e, acc);
 
   // SwiGLU: gate subtile j pairs with up subtile HALF + j (same columns)
   float h[MI][HALF][4];
@@ -474,19 +499,18 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   TileSrc src;
   src.ra = make_desc(p.hq, (uint32_t)(rows_cap * I));
   src.rb = make_desc(p.w2 + (size_t)e * K * I, (uint32_t)((size_t)K * I));
-  uint32_t a_off[C::A_INSTR], b_off[C::B_INSTR];
+  uint32_t a_off[C::A_INSTR], b_soff[C::B_INSTR];
 #pragma unroll
   for (int t = 0; t < C::A_INSTR; ++t) {
     int row, q;
     dma_rows<C::NW>(t, row, q);
     a_off[t] = (uint32_t)((size_t)b * BM + row) * I + q * 16;
   }
+  int brow0, bq;
+  dma_rows<C::NW>(0, brow0, bq);
+  const uint32_t b_off = (uint32_t)(ct * 256 + brow0) * I + bq * 16;
 #pragma unroll
-  for (int t = 0; t < C::B_INSTR; ++t) {
-    int row, q;
-    dma_rows<C::NW>(t, row, q);
-    b_off[t] = (uint32_t)(ct * 256 + row) * I + q * 16;
-  }
+  for (int t = 0; t < C::B_INSTR; ++t) b_soff[t] = (uint32_t)(C::NW * 8 * t) * I;
   const int srow = wid * C::SA_ROWS + lane;
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
   const int c0 = ct * 256 + wn * (256 / C::WN);  // this wave's first output column
@@ -506,7 +530,7 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   }
   f32x4 acc[MI][NI];
   // all NI subtiles of a wave are contiguous output columns (no gate/up split)
-  tile_gemm<KIND, BM, 256, NS>(src, smem, IS, a_off, sa_off, sa_step, b_off, sb_off, NI,
+  tile_gemm<KIND, BM, 256, NS>(src, smem, IS, a_off, sa_off, sa_step, b_off, b_soff, sb_off, NI,
                                e, acc);
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
