@@ -36,7 +36,12 @@ For every token t and route j with expert e = topk_ids[t, j] in [0, E):
   6. top-k weighted combine: out[t] = sum_j topk_weights[t, j] * y_j, the
      weight applied after the down GEMM, summed in fp64; the bf16 output is
      one rounding of that sum ([hpc-ops RFC] stage 5; [prime-flash] intro:
-     "top-k weighted reduction").
+     "top-k weighted reduction").  Between the down GEMM and the combine a
+     kernel may hold each route's row y_j in bf16: the pages' combine buffer
+     takes two bytes per token, selected expert and hidden column ([DeepGEMM
+     #88] "The rest of the memory numbers": 512 MiB at 8192 tokens on
+     4096/2048/288/8).  The result here keeps y_j exact; ``dev_bound``
+     covers that rounding (below).
 
 Requantization decisions (rounding to e4m3 / bf16, the power-of-two MX scale)
 are taken on h rounded to binary32, the precision the kernels hold h in; the
@@ -70,8 +75,10 @@ two ways, both modelled per element and returned beside the result:
   evaluation of silu: exp2, one division, the products, about (|g| + 6) u
   relative).  The down GEMM's own deviation, the deviation of a blockwise
   group's scale (the kernel's amax lies within the band of its largest
-  element), and the fp32 combine of the top_k rows are added to
-  ``dev_bound`` per output element.
+  element), the fp32 combine of the top_k rows and the rounding of each
+  route's row to bf16 before the combine (half a bf16 spacing at the largest
+  magnitude the kernel's row can reach, times the route weight) are added
+  to ``dev_bound`` per output element.
 * Near-ties (``flip_bound``).  Where the kernel's h can lie on the other side
   of a requantization rounding boundary (within the band above), both
   neighbouring codes are correct roundings of h.  Each requantizer returns,
@@ -400,6 +407,12 @@ def _requantizer(kind):
             "mxfp4": _requant_mx}.get(kind)
 
 
+def _row_rounding(reach):
+    """Largest change of a route's row element of magnitude at most `reach`
+    when it is rounded to bf16 (round to nearest: half a spacing)."""
+    return codecs.bf16_half_ulp(reach)
+
+
 def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
             topk_weights, tokens=None, exact_h=False, keep_h=False, h_perturb=None,
             n_shared=0):
@@ -510,10 +523,16 @@ def moe_ref(kind, x, x_scale, w1, w1_scale, w2, w2_scale, topk_ids,
             # the fp32 sum of the routes' rows (split-K over 128-wide slices
             # of I in the fused mode): at most k * I / 128 + 1 roundings
             lin_dev[i] += abs(w) * (U32 * (k * (I // 128 + 1) + 1) * np.abs(y[r]))
+            # the row held in bf16 before the combine: the kernel's fp32 row
+            # lies within its deviation and near-tie effects of y
+            reach = np.abs(y[r]) + LAMBDA * sy[r]
             if sd is not None:
                 lin_dev[i] += abs(w) * sd[r]
+                reach = reach + sd[r]
             if fl is not None:
                 flip[i] += abs(w) * fl[r]
+                reach = reach + fl[r]
+            lin_dev[i] += abs(w) * _row_rounding(reach)
             if keep_h:
                 key = t * k_routed + j if j < k_routed else T * k_routed + t * n_shared + j - k_routed
                 info = {"prob": prob[r]}

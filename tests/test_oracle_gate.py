@@ -176,3 +176,56 @@ def test_gate_rejects_wrong_mx_exponent(kind, monkeypatch):
     assert state["done"] and int(d["topk_ids"][t, j]) == e
     ok, st = _gate(kind, mutated, ref)
     assert not ok, st
+
+
+# ---------------------------------------------------------------------------
+# per-route rows held in bf16 before the combine
+# ---------------------------------------------------------------------------
+
+def _rows_rounded(d, T, k, bits=8):
+    """Emulated kernel: each route's row y_j (the oracle's exact value)
+    rounded to `bits` significant bits (8: bf16, round to nearest even),
+    then the weighted sum in fp64."""
+    out = None
+    for t in range(T):
+        for j in range(k):
+            y = _one_route(d, t, j, w=1.0)
+            if bits == 8:
+                yr = codecs.bf16_decode(codecs.bf16_encode(y))
+            else:
+                m, e = np.frexp(y)
+                yr = np.ldexp(np.round(m * 2.0 ** bits) / 2.0 ** bits, e)
+            if out is None:
+                out = np.zeros((T, y.size))
+            out[t] += d["topk_weights"][t, j] * yr
+    return out
+
+
+@pytest.mark.parametrize("kind,K,I", CASES)
+def test_gate_accepts_bf16_route_rows(kind, K, I, monkeypatch):
+    """Rows rounded to bf16 before the combine (the pages' two-byte combine
+    buffer) pass the gate with no tolerance at all (tol 0: the allowance and
+    the output's half spacing only); without the row-rounding term of the
+    allowance the same output fails, so the term is what admits it."""
+    T, k = 4, 4
+    d = small_case(kind, T, K, I, 8, k, seed="rows")
+    ref = run(d)
+    emul = _rows_rounded(d, T, k)
+    ok, st = om.tolerance_check(codecs.bf16_encode(emul), ref["out64"], 0.0, ref["allowance"])
+    assert ok, st
+    monkeypatch.setattr(om, "_row_rounding", lambda reach: np.zeros_like(reach))
+    bare = run(d)
+    ok, st = om.tolerance_check(codecs.bf16_encode(emul), ref["out64"], 0.0, bare["allowance"])
+    assert not ok, st
+
+
+@pytest.mark.parametrize("kind,K,I", CASES)
+def test_gate_rejects_coarser_route_rows(kind, K, I):
+    """Rows rounded to 6 significant bits (a plausible wrong row format: up
+    to four times bf16's rounding error) fail the gate at tol 0."""
+    T, k = 4, 4
+    d = small_case(kind, T, K, I, 8, k, seed="rows")
+    ref = run(d)
+    emul = _rows_rounded(d, T, k, bits=6)
+    ok, st = om.tolerance_check(codecs.bf16_encode(emul), ref["out64"], 0.0, ref["allowance"])
+    assert not ok, st
