@@ -263,8 +263,8 @@ int moe_select_block_m_routed(int32_t dtype, int64_t T, int64_t K, int32_t top_k
  * Workspace bytes a fused_moe_* call with these sizes and this tune (NULL:
  * none) needs (host out-param; [prime-flash] introduction: split=True writes
  * the H-wide activation to memory once, which here lives in the caller's
- * workspace with the per-route down outputs; split=False accumulates into an
- * fp32 buffer).  split = -1 means "as moe_select_split picks"; for split = 2
+ * workspace with the per-route down outputs in bf16; split=False accumulates
+ * into an fp32 buffer).  split = -1 means "as moe_select_split picks"; for split = 2
  * (ring mode) the size with the default ring (see moe_ring_layout).
  * Errors: as the fused calls' size and tune checks.
  */
@@ -336,7 +336,11 @@ int moe_workspace_layout(int32_t dtype, int64_t T, int64_t K, int64_t N,
  *   out       [out]  (T, K) bf16.  EVERY element is written: a token whose
  *                    routes are all outside [0, E) gets zeros.  out is
  *                    sum_j topk_weights[t, j] * y_j summed in fp32 with one
- *                    rounding to bf16.
+ *                    rounding to bf16; in split and ring mode each route's
+ *                    row y_j is first held in bf16 in the workspace (the
+ *                    combine buffer of [DeepGEMM #88] "The rest of the
+ *                    memory numbers": two bytes per token, route and
+ *                    column).
  *   T, K, N, E, top_k, block_m
  *                    tokens, hidden size, fused gate+up width (N = 2I; rows
  *                    [0, I) of w1 are the gate, [I, N) the up projection),

@@ -183,7 +183,7 @@ Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
     L.flags = off;
     off = round_up(off + R * 4, 256);
     L.yr = off;
-    off = round_up(off + R * (size_t)K * 4, 256);
+    off = round_up(off + R * (size_t)K * 2, 256);
     L.ring_fixed = off;
     L.slot_bytes = (size_t)block_m * ((size_t)I * es + h_scale_bytes(dtype, I));
     L.slots = ring_default_slots(blocks, (int)(I / 128));
@@ -208,7 +208,7 @@ Layout layout(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t
     if (dtype == MOE_MXFP8 || dtype == MOE_MXFP4) off = round_up(off + (size_t)rows * (I / 32), 256);
     if (dtype == MOE_BF16) L.hs = L.hq;
     L.yr = off;
-    off = round_up(off + R * (size_t)K * 4, 256);
+    off = round_up(off + R * (size_t)K * 2, 256);
     if (kw > 1) {  // per tile and workgroup: block_m rows x 256 gate/up sums
       L.part = off;
       off = round_up(off + (size_t)blocks * (I / 128) * kw * block_m * 256 * 4, 256);
@@ -295,7 +295,7 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
     a.flags = reinterpret_cast<int32_t*>(w + L.flags);
     a.hq = w + L.hq;
     a.hs = w + L.hs;
-    a.yr = reinterpret_cast<float*>(w + L.yr);
+    a.yr = reinterpret_cast<uint16_t*>(w + L.yr);
     a.h_rows = (int)(blocks * block_m);
     a.kw = pick_kw(dtype, T, K, N, E_all, k_all, block_m, sp, tune);
     if (a.kw > 1) {

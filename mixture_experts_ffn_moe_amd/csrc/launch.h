@@ -20,7 +20,7 @@ struct MoeArgs {
   // workspace regions
   uint8_t* hq;     // split: (rows_cap, I) intermediate values
   uint8_t* hs;     // split: intermediate scales
-  float* yr;       // split: (T*top_k, K) per-route down outputs
+  uint16_t* yr;    // split: (T*top_k, K) per-route down outputs, bf16 bits
   int32_t* flags;  // split: (T*top_k) route placed flags
   float* acc;      // fused: (T, K) fp32 accumulator
   int T, K, I, E, top_k;

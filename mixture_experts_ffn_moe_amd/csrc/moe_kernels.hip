@@ -36,6 +36,7 @@
 namespace {
 
 constexpr int kSlice = 128;  // width of an I slice (= blockwise scale group)
+constexpr int kCombineCols = 2048;  // output columns per combine workgroup (8 per thread)
 
 // Operands of a wave's GEMM: A rows (l % 16 of each 16-row subtile) and B
 // rows (l % 16 of each 16-column subtile) as buffer resources plus per-lane
@@ -731,7 +732,7 @@ k_up_sk(MoeArgs p) {
 
 // Down GEMM of the tile (block b of expert e, output columns ct*256 ..
 // ct*256 + 255; tile index b * NT + ct) from intermediate rows hrow0 ..:
-// fp32 per-route rows of yr.
+// per-route rows of yr, rounded to bf16.
 // CPA: cache policy of the intermediate's loads.
 template <int KIND, int BM, int D, int CPA = 0>
 __device__ __forceinline__ void down_block(const MoeArgs& p, int e, int ct, uint32_t tile,
@@ -804,7 +805,7 @@ __device__ __forceinline__ void down_block(const MoeArgs& p, int e, int ct, uint
       const int id = ids[wm * 64 + mi * 16 + 4 * g + i];
       if (id < 0) continue;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) p.yr[(size_t)id * K + c0 + 16 * ni + r16] = acc[mi][ni][i];
+      for (int ni = 0; ni < 4; ++ni) p.yr[(size_t)id * K + c0 + 16 * ni + r16] = f32_to_bf16(acc[mi][ni][i]);
     }
 }
 
@@ -926,35 +927,38 @@ k_ring(MoeArgs p) {
 // j then s ascending.
 __global__ void __launch_bounds__(256) k_combine(MoeArgs p) {
   const int K = p.K;
-  const int CT = (K + 1023) / 1024;
+  const int CT = (K + kCombineCols - 1) / kCombineCols;
   const int t = blockIdx.x / CT;
-  const int c = (blockIdx.x % CT) * 1024 + threadIdx.x * 4;
+  const int c = (blockIdx.x % CT) * kCombineCols + threadIdx.x * 8;  // 8 columns per thread
   if (c >= K) return;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  float s[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) s[u] = 0.f;
+  // one route's 8 bf16 values, times w, added in route order
+  auto add = [&](size_t id, float w) {
+    const uint4 y = *reinterpret_cast<const uint4*>(p.yr + id * K + c);
+    const uint32_t v[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s[2 * u] += w * __uint_as_float(v[u] << 16);
+      s[2 * u + 1] += w * __uint_as_float(v[u] & 0xFFFF0000u);
+    }
+  };
   for (int j = 0; j < p.top_k; ++j) {
     const size_t id = (size_t)t * p.top_k + j;
-    if (!p.flags[id]) continue;
-    const float w = p.topk_w[id];
-    const float4 y = *reinterpret_cast<const float4*>(p.yr + id * K + c);
-    s.x += w * y.x;
-    s.y += w * y.y;
-    s.z += w * y.z;
-    s.w += w * y.w;
+    if (p.flags[id]) add(id, p.topk_w[id]);
   }
   // shared experts: every token, weight 1, after its routed experts
   for (int j = 0; j < p.n_shared; ++j) {
     const size_t id = (size_t)p.T * p.top_k + (size_t)t * p.n_shared + j;
-    if (!p.flags[id]) continue;
-    const float4 y = *reinterpret_cast<const float4*>(p.yr + id * K + c);
-    s.x += y.x;
-    s.y += y.y;
-    s.z += y.z;
-    s.w += y.w;
+    if (p.flags[id]) add(id, 1.0f);
   }
-  uint2 o;
-  o.x = (uint32_t)f32_to_bf16(s.x) | ((uint32_t)f32_to_bf16(s.y) << 16);
-  o.y = (uint32_t)f32_to_bf16(s.z) | ((uint32_t)f32_to_bf16(s.w) << 16);
-  *reinterpret_cast<uint2*>(p.out + (size_t)t * K + c) = o;
+  uint4 o;
+  o.x = (uint32_t)f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
+  o.y = (uint32_t)f32_to_bf16(s[2]) | ((uint32_t)f32_to_bf16(s[3]) << 16);
+  o.z = (uint32_t)f32_to_bf16(s[4]) | ((uint32_t)f32_to_bf16(s[5]) << 16);
+  o.w = (uint32_t)f32_to_bf16(s[6]) | ((uint32_t)f32_to_bf16(s[7]) << 16);
+  *reinterpret_cast<uint4*>(p.out + (size_t)t * K + c) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -1280,7 +1284,7 @@ hipError_t launch_ring(const MoeArgs& a0, hipStream_t st, const TimingHook& hk) 
   mark(hk, 1, false, st);
   hipLaunchKernelGGL((k_ring<KIND, BM, D>), dim3(grid), dim3(THREADS), lds, st, a);
   mark(hk, 1, true, st);
-  const int CT = (a.K + 1023) / 1024;
+  const int CT = (a.K + kCombineCols - 1) / kCombineCols;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -1312,7 +1316,7 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
     if (tiled_supported(KIND, BM, a.K, a.I)) {
       hipError_t e = launch_tiled(KIND, BM, a, st, hk);
       if (e != hipSuccess) return e;
-      const int CT = (a.K + 1023) / 1024;
+      const int CT = (a.K + kCombineCols - 1) / kCombineCols;
       hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
       return hipGetLastError();
     }
@@ -1327,7 +1331,7 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
     mark(hk, 2, false, st);
     launch_down<KIND, BM>(a, st);
     mark(hk, 2, true, st);
-    const int CT = (a.K + 1023) / 1024;
+    const int CT = (a.K + kCombineCols - 1) / kCombineCols;
     hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
   } else {
     const size_t n16 = (size_t)a.T * a.K * 4 / 16;
@@ -1368,7 +1372,7 @@ hipError_t launch_down_combine_bm(const MoeArgs& a, hipStream_t st) {
   } else {
     return hipErrorInvalidValue;
   }
-  const int CT = (a.K + 1023) / 1024;
+  const int CT = (a.K + kCombineCols - 1) / kCombineCols;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -1395,7 +1399,7 @@ hipError_t launch_tiled_only(const MoeArgs& a, hipStream_t st, const TimingHook&
                      reinterpret_cast<uint4*>(a.flags), fbytes);
   hipError_t e = launch_tiled(KIND, 256, a, st, hk);
   if (e != hipSuccess) return e;
-  const int CT = (a.K + 1023) / 1024;
+  const int CT = (a.K + kCombineCols - 1) / kCombineCols;
   hipLaunchKernelGGL(k_combine, dim3((unsigned)(a.T * CT)), dim3(256), 0, st, a);
   return hipGetLastError();
 }

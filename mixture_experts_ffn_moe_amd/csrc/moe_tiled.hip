@@ -475,7 +475,7 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   }
 }
 
-// down GEMM, one (block, 256 output columns) tile, fp32 per-route rows
+// down GEMM, one (block, 256 output columns) tile, bf16 per-route rows
 template <int KIND, int BM, int NS>
 __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(1, BM >= 128 ? 2 : 1))) k_down_t(MoeArgs p) {
   using C = TileCfg<KIND, BM, 256, NS>;
@@ -532,15 +532,27 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   // all NI subtiles of a wave are contiguous output columns (no gate/up split)
   tile_gemm<KIND, BM, 256, NS>(src, smem, IS, a_off, sa_off, sa_step, b_off, b_soff, sb_off, NI,
                                e, acc);
+  // the tile's rows rounded to bf16, staged in LDS (rows of 512 bytes plus
+  // 16 bytes of padding), then written out as whole 512-byte row pieces
+  constexpr int YROW = 256 * 2 + 16;
+  static_assert(BM * YROW <= NS * C::STAGE, "the bf16 tile fits the pipeline LDS");
+  const int cw = wn * (256 / C::WN);  // this wave's first column within the tile
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
-      const int id = ids[wm * 64 + mi * 16 + 4 * g + i4];
-      if (id < 0) continue;
+      uint16_t* yrow = reinterpret_cast<uint16_t*>(smem + (wm * 64 + mi * 16 + 4 * g + i4) * YROW);
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) p.yr[(size_t)id * K + c0 + ni * 16 + r16] = acc[mi][ni][i4];
+      for (int ni = 0; ni < NI; ++ni) yrow[cw + ni * 16 + r16] = f32_to_bf16(acc[mi][ni][i4]);
     }
+  __syncthreads();
+  for (int c = threadIdx.x; c < BM * 32; c += C::THREADS) {
+    const int row = c / 32, ch = c % 32;
+    const int id = ids[row];
+    if (id < 0) continue;
+    *reinterpret_cast<uint4*>(p.yr + (size_t)id * K + ct * 256 + ch * 8) =
+        *reinterpret_cast<const uint4*>(smem + row * YROW + ch * 16);
+  }
 }
 
 template <int KIND, int BM, int NS>

@@ -125,7 +125,7 @@ def test_ring_workspace(dtype, es, sb, T, bm):
     total = moe.moe_workspace_size(dtype, T, K, N, E, k, bm, split=2)
     assert total == -(-(fixed + slots * slot) // 256) * 256
     R = T * k
-    assert fixed >= R * K * 4 + R * 4          # per-route rows and flags come first
+    assert fixed >= R * K * 2 + R * 4          # per-route bf16 rows and flags come first
 
 
 def test_ring_layout_rejects_large_blocks():
