@@ -118,8 +118,8 @@ def byte_model(kind, K, I, E_act, T, R, split):
     step = E_act * (w1e + w2e) + x_b + out_b + route_b
     hs = 0 if kind == "bf16" else (R * (I // 128) * 4 if kind == "fp8_blockwise" else R * (I // 32))
     if split == 2:
-        # persistent ring kernel: both GEMMs, H written and read back, fp32 route rows
-        dom = E_act * (w1e + w2e) + x_b + 2 * (R * I * es + hs) + R * K * 4
+        # persistent ring kernel: both GEMMs, H written and read back, bf16 route rows
+        dom = E_act * (w1e + w2e) + x_b + 2 * (R * I * es + hs) + R * K * 2
     elif split:
         dom = E_act * w1e + x_b + R * I * es + hs          # gate/up kernel: w1, x, H write
     else:

@@ -222,9 +222,9 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
     };
     if constexpr (C::NW == 8 && B_NEXT) {
       // two waves share each SIMD and fill each other's MFMA gaps; column
-      // ni + 1's B fragment is read while column ni's MFMAs run (gate/up
-      // GEMM at K=4096, I=2048, E=288, top-8, T=8192, 256-row tiles: 1.70 ->
-      // 1.58 ms)
+      // ni + 1's B fragment is read while column ni's MFMAs run (K=4096,
+      // I=2048, E=288, top-8, T=8192, 256-row tiles: gate/up GEMM 1.70 ->
+      // 1.58 ms, down GEMM 0.96 -> 0.86 ms)
       Frag<KIND_FP8B> fb2[2];
       lds_frag(fb2[0], tb, brow_of(0), g);
 #pragma unroll
@@ -530,7 +530,7 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   }
   f32x4 acc[MI][NI];
   // all NI subtiles of a wave are contiguous output columns (no gate/up split)
-  tile_gemm<KIND, BM, 256, NS>(src, smem, IS, a_off, sa_off, sa_step, b_off, b_soff, sb_off, NI,
+  tile_gemm<KIND, BM, 256, NS, true>(src, smem, IS, a_off, sa_off, sa_step, b_off, b_soff, sb_off, NI,
                                e, acc);
   // the tile's rows rounded to bf16, staged in LDS (rows of 512 bytes plus
   // 16 bytes of padding), then written out as whole 512-byte row pieces
