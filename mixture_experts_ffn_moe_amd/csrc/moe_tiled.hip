@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kRowBytes = 128;  // one K step of e4m3
 constexpr int kChunks = 8;      // 16-byte chunks per row
+constexpr int kScaleRow = 128;  // K steps of a weight block-scale row in LDS (K, I <= 16384)
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
@@ -105,7 +106,10 @@ struct TileSrc {
 //                       offset per load (the weight rows of one tile are
 //                       contiguous, so only the lane part varies)
 //  sa_off / sb_off    : this lane's scale row offsets; sa_step bytes per step
-template <int KIND, int BM, int BN, int NS>
+// PART 0 issues the whole stage; 1 only the weight side (B and its MX
+// scales), 2 only the activation side (A and its row scales), so that a
+// tile can request its first weights before it knows its activation rows.
+template <int KIND, int BM, int BN, int NS, int PART = 0>
 __device__ __forceinline__ void tile_load(const TileSrc& src, uint32_t lds, int st, int ks,
                                           const uint32_t (&a_off)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
                                           uint32_t sa_off, uint32_t sa_step, uint32_t b_off,
@@ -115,17 +119,22 @@ __device__ __forceinline__ void tile_load(const TileSrc& src, uint32_t lds, int 
   const uint32_t w = (uint32_t)wave_id();
   const uint32_t stage = lds + (uint32_t)(st * C::STAGE);
   const uint32_t soff = (uint32_t)ks * kRowBytes;
+  if constexpr (PART != 1) {
 #pragma unroll
-  for (int t = 0; t < C::A_INSTR; ++t) dma16(src.ra, stage + (w + C::NW * t) * 1024, a_off[t], soff);
+    for (int t = 0; t < C::A_INSTR; ++t) dma16(src.ra, stage + (w + C::NW * t) * 1024, a_off[t], soff);
+  }
+  if constexpr (PART != 2) {
 #pragma unroll
-  for (int t = 0; t < C::B_INSTR; ++t)
-    dma16(src.rb, stage + C::A_BYTES + (w + C::NW * t) * 1024, b_off, soff + b_soff[t]);
+    for (int t = 0; t < C::B_INSTR; ++t)
+      dma16(src.rb, stage + C::A_BYTES + (w + C::NW * t) * 1024, b_off, soff + b_soff[t]);
+  }
   // row scales: wave w stages rows [w * SA_ROWS, (w + 1) * SA_ROWS) in its 64
   // slots.  All lanes load (lanes past SA_ROWS fill padding from an in-bounds
   // row): a lane-dependent branch around the asm would put its scalar
   // operands in vector registers.
-  dma4(src.rsa, stage + C::A_BYTES + C::B_BYTES + w * 256, sa_off, (uint32_t)ks * sa_step);
-  if constexpr (KIND == KIND_MX)
+  if constexpr (PART != 1)
+    dma4(src.rsa, stage + C::A_BYTES + C::B_BYTES + w * 256, sa_off, (uint32_t)ks * sa_step);
+  if constexpr (KIND == KIND_MX && PART != 2)
     dma4(src.rsb, stage + C::A_BYTES + C::B_BYTES + C::SA_BYTES + w * 256, sb_off, (uint32_t)ks * 4);
 }
 
@@ -152,10 +161,12 @@ __device__ __forceinline__ void lds_frag(Frag<KIND_FP8B>& f, const uint8_t* base
 template <int ROWS>
 __device__ __forceinline__ int scale_slot(int row) { return (row / ROWS) * 64 + row % ROWS; }
 
-// Compute one staged K step (stage at `stage`, logical step ks).
+// Compute one staged K step (stage at `stage`, logical step ks).  wsc: the
+// blockwise weight scales of the tile's two 128-row weight blocks in LDS,
+// step ks of the first at wsc[ks], of the second at wsc[kScaleRow + ks].
 template <int KIND, int BM, int BN, int NS, bool B_NEXT>
-__device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const StepScales& sc1,
-                                          const StepScales& sc2, int up_split,
+__device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const float* wsc,
+                                          int up_split,
                                           f32x4 (&acc)[4][TileCfg<KIND, BM, BN, NS>::NI]) {
   using C = TileCfg<KIND, BM, BN, NS>;
   constexpr int MI = C::MI, NI = C::NI;
@@ -194,8 +205,8 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
   };
   if constexpr (KIND == KIND_FP8B) {
     float sa[MI][4];
-    const float s1 = sc1.at(ks);
-    const float s2 = sc2.at(ks);
+    const float s1 = wsc[ks];
+    const float s2 = wsc[kScaleRow + ks];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -279,12 +290,22 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const St
 
 // One workgroup tile: acc[mi][ni] over all K steps, visiting the steps from
 // a staggered start, NS stages in flight (stage slots in one LDS array).
-template <int KIND, int BM, int BN, int NS, bool B_NEXT = false>
-__device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, int ksteps,
+// The tile's first requests go out before anything waits: the blockwise
+// weight-scale rows of the tile's two 128-row weight blocks (src.bsc and
+// src.bsc2, into `wsc`, 2 x kScaleRow floats of LDS; the wave reads them
+// from row wsc_row on) and the weight side of the first stage; then `activation_offsets()` runs (it may wait
+// for the tile's rows and fill a_off / sa_off, which are read only after
+// it), then the activation side of the first stage and the other stages.
+// Every load is a direct-to-LDS load issued from asm, so the K loop's
+// explicit waits are the only ones.
+template <int KIND, int BM, int BN, int NS, bool B_NEXT, typename F>
+__device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, float* wsc, int wsc_row,
+                                          int ksteps,
                                           const uint32_t (&a_off)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
-                                          uint32_t sa_off, uint32_t sa_step, uint32_t b_off,
+                                          const uint32_t& sa_off, uint32_t sa_step, uint32_t b_off,
                                           const uint32_t (&b_soff)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
                                           uint32_t sb_off, int up_split, int group,
+                                          F&& activation_offsets,
                                           f32x4 (&acc)[4][TileCfg<KIND, BM, BN, NS>::NI]) {
   using C = TileCfg<KIND, BM, BN, NS>;
   constexpr int MI = C::MI, NI = C::NI;
@@ -292,13 +313,18 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, int
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
-  StepScales sc1{0.f, 0.f}, sc2{0.f, 0.f};
   if constexpr (KIND == KIND_FP8B) {
-    sc1.load(src.bsc, ksteps);
-    sc2.load(src.bsc2 ? src.bsc2 : src.bsc, ksteps);
-    // wait here: the compiler would place this wait at the first use, inside
-    // the K loop, where it would also drain the pipeline's loads every pass
-    wait_vmcnt<0>();
+    // each row: lanes load steps lane and 64 + lane (past ksteps the
+    // descriptor's bound returns zeros)
+    const int lane = threadIdx.x & 63;
+    const uint32_t m0 = lds_addr(wsc);
+    const uint32_t bytes = (uint32_t)ksteps * 4;
+    const desc_t r1 = make_desc(src.bsc, bytes);
+    const desc_t r2 = make_desc(src.bsc2 ? src.bsc2 : src.bsc, bytes);
+    dma4(r1, m0, lane * 4, 0);
+    dma4(r1, m0 + 256, 256 + lane * 4, 0);
+    dma4(r2, m0 + kScaleRow * 4, lane * 4, 0);
+    dma4(r2, m0 + kScaleRow * 4 + 256, 256 + lane * 4, 0);
   }
   // All tiles of one expert start at the same step and walk K in step: the
   // slices (or column tiles) of one block then read its gathered activation
@@ -315,9 +341,17 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, int
     tile_load<KIND, BM, BN, NS>(src, lbase, slot, step_at(i), a_off, sa_off, sa_step, b_off, b_soff,
                                 sb_off);
   };
+  // stage 0 in two parts around the activation offsets (the wait counts
+  // below count whole stages issued after the one awaited: unchanged)
+  tile_load<KIND, BM, BN, NS, 1>(src, lbase, 0, step_at(0), a_off, sa_off, sa_step, b_off, b_soff,
+                                 sb_off);
+  activation_offsets();
+  tile_load<KIND, BM, BN, NS, 2>(src, lbase, 0, step_at(0), a_off, sa_off, sa_step, b_off, b_soff,
+                                 sb_off);
 #pragma unroll
-  for (int u = 0; u < NS - 1; ++u)
+  for (int u = 1; u < NS - 1; ++u)
     if (u < ksteps) load(u, u);
+  const float* wsc_r = wsc + wsc_row * kScaleRow;
   int slot = 0;
   for (int i = 0; i < ksteps; ++i) {
     // step i has landed once only the later steps' loads may be pending
@@ -326,8 +360,7 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, int
     lds_barrier();
     const int ahead = slot + NS - 1;
     if (i + NS - 1 < ksteps) load(ahead >= NS ? ahead - NS : ahead, i + NS - 1);
-    tile_step<KIND, BM, BN, NS, B_NEXT>(smem + slot * C::STAGE, step_at(i), sc1, sc2, up_split,
-                                        acc);
+    tile_step<KIND, BM, BN, NS, B_NEXT>(smem + slot * C::STAGE, step_at(i), wsc_r, up_split, acc);
     slot = slot + 1 == NS ? 0 : slot + 1;
   }
   __syncthreads();  // the caller reuses the LDS
@@ -340,8 +373,9 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   using C = TileCfg<KIND, BM, 256, NS>;
   constexpr int MI = C::MI, NI = C::NI, HALF = NI / 2;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE];
-  __shared__ int ids[BM];
+  __shared__ int ids[C::NW * 64];  // route id of row r at scale_slot<SA_ROWS>(r)
   __shared__ float lds_amax[C::WN * BM];
+  __shared__ float wsc[2 * kScaleRow];
   const int S = p.I / 128;
   const int logical = xcd_remap(blockIdx.x, (*p.ntp / BM) * S);
   if (logical < 0) return;
@@ -352,20 +386,18 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int wn = wid % C::WN, wm = wid / C::WN;
   const int g = lane >> 4, r16 = lane & 15;
-  if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
-  __syncthreads();
+  const int srow = wid * C::SA_ROWS + lane;  // row whose id and scales this lane stages
+  // the block's route ids, into LDS with the wave's scale-row layout; the
+  // weight loads go out before anything waits for them
+  dma4(make_desc(p.sorted, (uint32_t)((size_t)p.blocks_cap * BM * 4)), lds_addr(ids) + wid * 256,
+       (uint32_t)(b * BM + (srow < BM ? srow : 0)) * 4, 0);
+  auto id_of = [&](int r) { return ids[scale_slot<C::SA_ROWS>(r)]; };
   const int K = p.K, I = p.I, N = 2 * I, KS = K / 128;
 
   TileSrc src;
   src.ra = make_desc(p.x, (uint32_t)((size_t)p.T * K));
   src.rb = make_desc(p.w1 + (size_t)e * N * K, (uint32_t)((size_t)N * K));
   uint32_t a_off[C::A_INSTR], b_soff[C::B_INSTR];
-#pragma unroll
-  for (int t = 0; t < C::A_INSTR; ++t) {
-    int row, q;
-    dma_rows<C::NW>(t, row, q);
-    a_off[t] = (uint32_t)route_token(p, ids[row]) * K + q * 16;
-  }
   // B rows [0,128): the gate slice's weight rows; [128,256): the up slice's.
   // Load t's rows are load 0's plus NW * 8 * t, all on one side of 128.
   int brow0, bq;
@@ -376,16 +408,14 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
     const int d = C::NW * 8 * t;
     b_soff[t] = (uint32_t)(d < 128 ? d : I - 128 + d) * K;
   }
-  const int srow = wid * C::SA_ROWS + lane;  // scale row this lane stages
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
+  const uint32_t sa_row = KIND == KIND_FP8B ? KS * 4 : K / 32;  // bytes per activation scale row
   if constexpr (KIND == KIND_FP8B) {
     src.rsa = make_desc(p.xs, (uint32_t)((size_t)p.T * KS * 4));
-    sa_off = (uint32_t)route_token(p, ids[srow < BM ? srow : 0]) * KS * 4;
     src.bsc = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + s) * KS;
     src.bsc2 = reinterpret_cast<const float*>(p.w1s) + ((size_t)e * (N / 128) + S + s) * KS;
   } else {
     src.rsa = make_desc(p.xs, (uint32_t)((size_t)p.T * (K / 32)));
-    sa_off = (uint32_t)route_token(p, ids[srow < BM ? srow : 0]) * (K / 32);
     src.rsb = make_desc(reinterpret_cast<const uint8_t*>(p.w1s) + (size_t)e * N * (K / 32),
                         (uint32_t)((size_t)N * (K / 32)));
     const int brow = min(wid * C::SB_ROWS + lane, 255);  // B scale row this lane stages
@@ -394,9 +424,23 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
     src.bsc = nullptr;
     src.bsc2 = nullptr;
   }
+  // the gathered activation rows, once the route ids have arrived: issued
+  // after them, the weight-scale rows (blockwise: 4 loads) and the weight
+  // side of the first stage (B, and the MX weight scales) may be pending
+  auto activation_offsets = [&]() {
+    wait_vmcnt<(KIND == KIND_FP8B ? 4 : 0) + C::B_INSTR + (KIND == KIND_MX ? 1 : 0)>();
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < C::A_INSTR; ++t) {
+      int row, q;
+      dma_rows<C::NW>(t, row, q);
+      a_off[t] = (uint32_t)route_token(p, id_of(row)) * K + q * 16;
+    }
+    sa_off = (uint32_t)route_token(p, id_of(srow < BM ? srow : 0)) * sa_row;
+  };
   f32x4 acc[MI][NI];
-  tile_gemm<KIND, BM, 256, NS, true>(src, smem, KS, a_off, sa_off, sa_step, b_off, b_soff, sb_off,
-                                     HALF, e, acc);
+  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, 0, KS, a_off, sa_off, sa_step, b_off, b_soff,
+                                     sb_off, HALF, e, activation_offsets, acc);
 
   // SwiGLU: gate subtile j pairs with up subtile HALF + j (same columns)
   float h[MI][HALF][4];
@@ -470,7 +514,7 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
         *reinterpret_cast<const uint4*>(q + row * QROW + ch * 16);
   }
   if (s == 0 && threadIdx.x < BM) {
-    const int id = ids[threadIdx.x];
+    const int id = id_of(threadIdx.x);
     if (id >= 0) p.flags[id] = 1;
   }
 }
@@ -481,7 +525,8 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   using C = TileCfg<KIND, BM, 256, NS>;
   constexpr int MI = C::MI, NI = C::NI;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE];
-  __shared__ int ids[BM];
+  __shared__ int ids[C::NW * 64];  // route id of row r at scale_slot<SA_ROWS>(r)
+  __shared__ float wsc[2 * kScaleRow];
   const int K = p.K, I = p.I, IS = I / 128;
   const int NT = K / 256;
   const int logical = xcd_remap(blockIdx.x, (*p.ntp / BM) * NT);
@@ -493,8 +538,11 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int wn = wid % C::WN, wm = wid / C::WN;
   const int g = lane >> 4, r16 = lane & 15;
-  if (threadIdx.x < BM) ids[threadIdx.x] = p.sorted[b * BM + threadIdx.x];
-  __syncthreads();
+  const int srow = wid * C::SA_ROWS + lane;  // row whose id and scales this lane stages
+  // the block's route ids are needed only to store the result: loaded into
+  // LDS ahead of the K walk, whose last wait covers them
+  dma4(make_desc(p.sorted, (uint32_t)((size_t)p.blocks_cap * BM * 4)), lds_addr(ids) + wid * 256,
+       (uint32_t)(b * BM + (srow < BM ? srow : 0)) * 4, 0);
   const size_t rows_cap = (size_t)p.blocks_cap * BM;
   TileSrc src;
   src.ra = make_desc(p.hq, (uint32_t)(rows_cap * I));
@@ -511,14 +559,14 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   const uint32_t b_off = (uint32_t)(ct * 256 + brow0) * I + bq * 16;
 #pragma unroll
   for (int t = 0; t < C::B_INSTR; ++t) b_soff[t] = (uint32_t)(C::NW * 8 * t) * I;
-  const int srow = wid * C::SA_ROWS + lane;
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
   const int c0 = ct * 256 + wn * (256 / C::WN);  // this wave's first output column
   if constexpr (KIND == KIND_FP8B) {
     src.rsa = make_desc(p.hs, (uint32_t)(rows_cap * IS * 4));
     sa_off = (uint32_t)((size_t)b * BM + (srow < BM ? srow : 0)) * IS * 4;
-    src.bsc = reinterpret_cast<const float*>(p.w2s) + ((size_t)e * (K / 128) + c0 / 128) * IS;
-    src.bsc2 = nullptr;
+    // the tile's two 128-column weight blocks; the wave's is c0 / 128
+    src.bsc = reinterpret_cast<const float*>(p.w2s) + ((size_t)e * (K / 128) + 2 * ct) * IS;
+    src.bsc2 = src.bsc + IS;
   } else {
     src.rsa = make_desc(p.hs, (uint32_t)(rows_cap * (I / 32)));
     sa_off = (uint32_t)((size_t)b * BM + (srow < BM ? srow : 0)) * (I / 32);
@@ -530,8 +578,8 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   }
   f32x4 acc[MI][NI];
   // all NI subtiles of a wave are contiguous output columns (no gate/up split)
-  tile_gemm<KIND, BM, 256, NS, true>(src, smem, IS, a_off, sa_off, sa_step, b_off, b_soff, sb_off, NI,
-                               e, acc);
+  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, c0 / 128 - 2 * ct, IS, a_off, sa_off, sa_step,
+                                     b_off, b_soff, sb_off, NI, e, [] {}, acc);
   // the tile's rows rounded to bf16, staged in LDS (rows of 512 bytes plus
   // 16 bytes of padding), then written out as whole 512-byte row pieces
   constexpr int YROW = 256 * 2 + 16;
@@ -548,7 +596,7 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   __syncthreads();
   for (int c = threadIdx.x; c < BM * 32; c += C::THREADS) {
     const int row = c / 32, ch = c % 32;
-    const int id = ids[row];
+    const int id = ids[scale_slot<C::SA_ROWS>(row)];
     if (id < 0) continue;
     *reinterpret_cast<uint4*>(p.yr + (size_t)id * K + ct * 256 + ch * 8) =
         *reinterpret_cast<const uint4*>(smem + row * YROW + ch * 16);
