@@ -75,7 +75,7 @@ def test_align_repeatable():
 
 
 # moe_align_ws: chunked planning past 16,384 routes (three launches over
-# chunks of 1,024 route ids), bit for bit the one-workgroup plan
+# chunks of 512 route ids), bit for bit the one-workgroup plan
 CHUNKED = [
     ("uniform", 2049, 288, 8),      # 16,392 routes: just past the switch
     ("masked", 8192, 288, 8),       # 65,536 routes
