@@ -58,3 +58,14 @@ def test_tiled_stages(kind, bm):
     b = _bits(c, bm, 1, {"stages": 3})
     say(f"      stages 2 against 3: {int((a != b).sum())} outputs differ")
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("kind", ["fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("K,I", [(8448, 256), (512, 8448)])
+def test_tiled_long_k_walks(kind, K, I):
+    """More than 64 K steps in one tiled GEMM (66: the gate/up GEMM at
+    K = 8448, the down GEMM at I = 8448): the weight block-scale rows held
+    for the walk, and every later step's operands, past their first 64."""
+    c = small_case(kind, T=70, E=2, k=1, tag="gpu-tune-long", K=K, I=I)
+    for bm in (64, 128):
+        check(c, bm, 1, label="long K walk")
