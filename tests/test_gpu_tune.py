@@ -61,11 +61,12 @@ def test_tiled_stages(kind, bm):
 
 
 @pytest.mark.parametrize("kind", ["fp8_blockwise", "mxfp8"])
-@pytest.mark.parametrize("K,I", [(8448, 256), (512, 8448)])
+@pytest.mark.parametrize("K,I", [(8448, 256), (512, 8448), (16384, 256), (512, 16384)])
 def test_tiled_long_k_walks(kind, K, I):
     """More than 64 K steps in one tiled GEMM (66: the gate/up GEMM at
-    K = 8448, the down GEMM at I = 8448): the weight block-scale rows held
-    for the walk, and every later step's operands, past their first 64."""
+    K = 8448, the down GEMM at I = 8448; 128, the most the blockwise format
+    allows, at 16384): the weight block-scale rows held for the walk, and
+    every later step's operands, past their first 64."""
     c = small_case(kind, T=70, E=2, k=1, tag="gpu-tune-long", K=K, I=I)
     for bm in (64, 128):
         check(c, bm, 1, label="long K walk")
