@@ -212,6 +212,13 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
 }
 
+// The same for a value already within the range: h * (1 / (amax / 448))
+// with |h| <= amax is at most 448 plus a few ulp, far below the 464 midpoint,
+// so it rounds as the clamped value would.
+__device__ __forceinline__ uint32_t f32_to_e4m3_in_range(float v) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, 0.0f, 0, false) & 0xFFu;
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
 __device__ __forceinline__ uint16_t f32_to_bf16(float v) {
   uint32_t u = __float_as_uint(v);
@@ -230,12 +237,21 @@ __device__ __forceinline__ int mx_shared_exp(float a) {
   return s < -127 ? -127 : (s > 127 ? 127 : s);
 }
 
+// max of v and the value lane movement CTRL (a DPP control) brings in
+template <int CTRL>
+__device__ __forceinline__ float max_dpp(float v) {
+  const int u = __builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true);
+  return __builtin_fmaxf(v, __int_as_float(u));
+}
+
 __device__ __forceinline__ float wave_max16(float v) {
-  // max over the 16 lanes sharing l / 16 (xor offsets stay inside the group)
-  v = __builtin_fmaxf(v, __shfl_xor(v, 1));
-  v = __builtin_fmaxf(v, __shfl_xor(v, 2));
-  v = __builtin_fmaxf(v, __shfl_xor(v, 4));
-  v = __builtin_fmaxf(v, __shfl_xor(v, 8));
+  // max over the 16 lanes sharing l / 16, which form one DPP row: swap
+  // neighbours, then pairs (each quad holds its max), then rotate the row
+  // by 4 and by 8 (each lane meets every quad); no LDS traffic
+  v = max_dpp<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v = max_dpp<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v = max_dpp<0x124>(v);  // row_ror 4
+  v = max_dpp<0x128>(v);  // row_ror 8
   return v;
 }
 

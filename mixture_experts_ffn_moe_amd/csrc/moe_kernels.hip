@@ -549,7 +549,7 @@ __device__ __forceinline__ void requant_tile(const f32x4 (&h)[BlockShape<BM>::MI
           const float inv = 1.0f / f;
           sf[mi][i] = f;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) codes[mi][j][i] = f32_to_e4m3(h[mi][j][i] * inv);
+          for (int j = 0; j < 2; ++j) codes[mi][j][i] = f32_to_e4m3_in_range(h[mi][j][i] * inv);
         }
     } else {  // MX: this wave's 32 columns form one group
 #pragma unroll

@@ -483,7 +483,7 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
         const float inv = 1.0f / f;
 #pragma unroll
         for (int j = 0; j < HALF; ++j)
-          q[row * QROW + wn * HALF * 16 + j * 16 + r16] = (uint8_t)f32_to_e4m3(h[mi][j][i4] * inv);
+          q[row * QROW + wn * HALF * 16 + j * 16 + r16] = (uint8_t)f32_to_e4m3_in_range(h[mi][j][i4] * inv);
         if (wn == 0 && r16 == 0) reinterpret_cast<float*>(p.hs)[(pos0 + row) * (I / 128) + s] = f;
       }
   } else {  // MX: groups of 32 columns = subtile pairs (2j, 2j+1) of this wave
