@@ -248,8 +248,10 @@ int moe_select_block_m(int32_t dtype, int64_t T, int64_t K, int32_t top_k, int32
 
 /*
  * The same, with the number of experts that hold at least one route
- * (active_experts, in [0, E]; a caller that has the routing on the host
- * counts them).  A skewed routing concentrates the routes on few experts,
+ * (active_experts, in [0, E]).  The count is a host value: a caller that
+ * routes on the device takes it from an earlier step or from its own
+ * routing statistics, since reading it back would synchronize; inside a
+ * captured graph, moe_select_block_m needs no count.  A skewed routing concentrates the routes on few experts,
  * which then hold many rows each: blockwise FP8 at K=7168, I=3072, E=384,
  * T=256 under a zipf routing (59 active experts, 26 rows each) runs in
  * 961 us with 64-row tiles against 1389 us with the 16-row blocks the
