@@ -89,10 +89,15 @@ class HipEvents:
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources' code: comments removed and whitespace
+    collapsed, so that an edit of a comment keeps the counters current."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            t = re.sub(r"/\*.*?\*/", " ", fh.read(), flags=re.S)
+        t = re.sub(r"//[^\n]*", " ", t)
+        h.update(" ".join(t.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -95,8 +95,10 @@ struct TileCfg {
 // Operand sources of one tile GEMM.
 struct TileSrc {
   desc_t ra, rb, rsa, rsb;
-  const float* bsc;  // FP8B: weight block-scale row of the wave's n-block (index: step)
-  const float* bsc2; // FP8B k_up_t: the up half's block-scale row
+  // FP8B: block-scale rows (index: step) of the tile's two 128-row weight
+  // blocks: k_up_t's gate and up slices, k_down_t's two column blocks
+  const float* bsc;
+  const float* bsc2;
 };
 
 // Issue the DMA loads of K step `ks` into stage slot `st` of the pipeline
