@@ -194,6 +194,23 @@ def test_routes_outside_local_experts(split):
     assert torch.all(out[5].float() == 0)
 
 
+@pytest.mark.parametrize("kind", ["fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("bm,split", [(64, 1), (128, 1), (256, 1), (16, 2), (32, 2)])
+def test_routes_outside_local_experts_tiled_and_ring(kind, bm, split):
+    """The LDS-tiled kernels and the ring mode with non-local routes, ids
+    beyond E and tokens with no local route at all (their rows must be
+    zeros, written although no tile ever holds them)."""
+    c = small_case(kind, T=300, E=4, k=2, K=512, tag="gpu-oor-tiled")
+    ids = c.topk_ids.clone()
+    ids[::3, 1] = -1
+    ids[5, :] = -1
+    ids[299, :] = -1          # the last token too
+    ids[7, 0] = 9
+    c.topk_ids = ids
+    out, _, _ = check(c, bm, split, label="oor tiled/ring")
+    assert torch.all(out[5].float() == 0) and torch.all(out[299].float() == 0)
+
+
 @pytest.mark.parametrize("kind", ["bf16", "fp8_blockwise", "mxfp8", "mxfp4"])
 def test_single_token(kind):
     c = small_case(kind, T=1, E=8, k=2)
