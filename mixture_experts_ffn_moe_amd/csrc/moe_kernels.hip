@@ -9,9 +9,10 @@
 //                gather x rows, gate/up GEMM on MFMA, SwiGLU, requantize,
 //                write the intermediate slice (+ scales) to the workspace
 //     k_down     per (block_m rows, 256 output columns): intermediate . w2^T
-//                over all of I (no split-K), fp32 per-route result rows
-//     k_combine  out[t] = bf16(sum_j w[t,j] * y[t,j]) in route order
-//                (deterministic)
+//                over all of I (no split-K), per-route result rows in bf16
+//                (the pages' combine buffer)
+//     k_combine  out[t] = bf16(sum_j w[t,j] * y[t,j]) in route order, in
+//                fp32 (deterministic)
 //   fused mode ([prime-flash] introduction, split=False):
 //     k_zero     clear the fp32 (T, K) accumulator
 //     k_fused    per (block_m rows, 128-wide slice of I): k_up's work with
