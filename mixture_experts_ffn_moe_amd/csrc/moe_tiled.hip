@@ -583,7 +583,10 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, c0 / 128 - 2 * ct, IS, a_off, sa_off, sa_step,
                                      b_off, b_soff, sb_off, NI, e, [] {}, acc);
   // the tile's rows rounded to bf16, staged in LDS (rows of 512 bytes plus
-  // 16 bytes of padding), then written out as whole 512-byte row pieces
+  // 16 bytes of padding), then written out as whole 512-byte row pieces with
+  // non-temporal stores: the combine reads them once, much later, so they
+  // need not displace the weight stream in L2 (K=4096, I=2048, E=288,
+  // top-8: 1-2% of this kernel at T = 4096 and 8192)
   constexpr int YROW = 256 * 2 + 16;
   static_assert(BM * YROW <= NS * C::STAGE, "the bf16 tile fits the pipeline LDS");
   const int cw = wn * (256 / C::WN);  // this wave's first column within the tile
@@ -600,8 +603,9 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
     const int row = c / 32, ch = c % 32;
     const int id = ids[scale_slot<C::SA_ROWS>(row)];
     if (id < 0) continue;
-    *reinterpret_cast<uint4*>(p.yr + (size_t)id * K + ct * 256 + ch * 8) =
-        *reinterpret_cast<const uint4*>(smem + row * YROW + ch * 16);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(smem + row * YROW + ch * 16),
+                                reinterpret_cast<u32x4*>(p.yr + (size_t)id * K + ct * 256 + ch * 8));
   }
 }
 
