@@ -49,7 +49,7 @@ def test_noalloc_rejects_sizes_beyond_its_workspace():
     L = moe.lib()
     P = ctypes.c_void_p
     fake = P(1 << 20)
-    # T = 4096, K = 4096, I = 2048, 256 experts top-6, 64-row blocks: 140 MiB
+    # T = 4096, K = 4096, I = 2048, 256 experts top-6, 64-row blocks, split mode: 274 MiB
     rc = L.fused_moe_fp8_blockwise_noalloc(*([fake] * 11), 4096, 4096, 4096, 256, 6, 64, 1, None)
     assert rc == -5
     assert b"static scratch" in L.moe_last_error()
