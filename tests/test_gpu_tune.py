@@ -51,8 +51,12 @@ def test_k_split_over_workgroups(kind):
 
 @pytest.mark.parametrize("kind", ["fp8_blockwise", "mxfp8"])
 @pytest.mark.parametrize("bm", [64, 128])
-def test_tiled_stages(kind, bm):
-    c = small_case(kind, T=300, E=8, k=2, tag="gpu-tune-tiled", K=512)   # tiled: K % 256 == 0
+@pytest.mark.parametrize("K,I", [(512, 384), (256, 128), (768, 384)])
+def test_tiled_stages(kind, bm, K, I):
+    """Two and three LDS stages.  K and I give the two GEMMs walks of 4 and
+    3, 2 and 1, 6 and 3 steps: as long as the pipeline or shorter, and not
+    a whole number of rounds of its slots."""
+    c = small_case(kind, T=300, E=8, k=2, tag="gpu-tune-tiled", K=K, I=I)   # tiled: K % 256 == 0
     check(c, bm, 1, tune={"stages": 2}, label="tune")
     a = _bits(c, bm, 1, {"stages": 2})
     b = _bits(c, bm, 1, {"stages": 3})
