@@ -36,6 +36,9 @@ namespace {
 constexpr int kRowBytes = 128;  // one K step of e4m3
 constexpr int kChunks = 8;      // 16-byte chunks per row
 constexpr int kScaleRow = 128;  // K steps of a weight block-scale row in LDS (K, I <= 16384)
+#ifndef LOADER_WAVES_8
+#define LOADER_WAVES_8 4  // loading waves of an 8-wave tile
+#endif
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
@@ -75,19 +78,26 @@ struct TileCfg {
   static constexpr int WN = NW / WM;            // wave columns
   static constexpr int MI = 4;                  // 16-row subtiles per wave
   static constexpr int NI = BN / WN / 16;       // 16-column subtiles per wave
+  // Waves that issue the tile's DMA loads: with two waves per SIMD, only
+  // the first wave of each SIMD loads (twice the instructions), so the
+  // other never holds its MFMAs behind a queue of vector-memory issues
+  // (K=4096, I=2048, E=288, top-8, T=8192, 256-row tiles: gate/up GEMM 1.54
+  // -> 1.43 ms).
+  static constexpr int LW = NW == 8 ? LOADER_WAVES_8 : NW;
   static constexpr int A_BYTES = BM * kRowBytes;
   static constexpr int B_BYTES = BN * kRowBytes;
-  // Row scales (fp32, or 4 x e8m0 per row): each wave stages SA_ROWS rows in
-  // 64 four-byte slots (every lane loads; the slots past SA_ROWS are padding).
-  static constexpr int SA_BYTES = NW * 256;
-  static constexpr int SB_BYTES = (KIND == KIND_MX) ? NW * 256 : 0;  // MX weight scales
+  // Row scales (fp32, or 4 x e8m0 per row): each loading wave stages
+  // SA_ROWS rows in 64 four-byte slots (every lane loads; the slots past
+  // SA_ROWS are padding).
+  static constexpr int SA_BYTES = LW * 256;
+  static constexpr int SB_BYTES = (KIND == KIND_MX) ? LW * 256 : 0;  // MX weight scales
   static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-  static constexpr int A_INSTR = A_BYTES / 1024 / NW;  // 16-byte DMA instructions per wave
-  static constexpr int B_INSTR = B_BYTES / 1024 / NW;
-  static constexpr int SA_ROWS = BM / NW;              // scale rows staged per wave
-  static constexpr int SB_ROWS = BN / NW;
+  static constexpr int A_INSTR = A_BYTES / 1024 / LW;  // 16-byte DMA instructions per loading wave
+  static constexpr int B_INSTR = B_BYTES / 1024 / LW;
+  static constexpr int SA_ROWS = BM / LW;              // scale rows staged per loading wave
+  static constexpr int SB_ROWS = BN / LW;
   static constexpr int S_INSTR = 1 + ((KIND == KIND_MX) ? 1 : 0);
-  static constexpr int LOADS = A_INSTR + B_INSTR + S_INSTR;  // per wave per stage
+  static constexpr int LOADS = A_INSTR + B_INSTR + S_INSTR;  // per loading wave per stage
   static constexpr int THREADS = NW * 64;
   static_assert(SA_ROWS <= 64 && SB_ROWS <= 64, "one scale instruction per wave");
 };
@@ -103,7 +113,9 @@ struct TileSrc {
 
 // Issue the DMA loads of K step `ks` into stage slot `st` of the pipeline
 // area at LDS address `lds` (a wave-uniform byte address).
-//  a_off[t]           : this lane's byte offset of its A chunk (t-th load)
+//  a_off[t] + a_soff[t]: this lane's byte offset of its A chunk (t-th load),
+//                       a lane part and a wave-uniform part (zero where the
+//                       rows are gathered)
 //  b_off + b_soff[t]  : the same for B, a lane offset plus a wave-uniform
 //                       offset per load (the weight rows of one tile are
 //                       contiguous, so only the lane part varies)
@@ -114,21 +126,24 @@ struct TileSrc {
 template <int KIND, int BM, int BN, int NS, int PART = 0>
 __device__ __forceinline__ void tile_load(const TileSrc& src, uint32_t lds, int st, int ks,
                                           const uint32_t (&a_off)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
+                                          const uint32_t (&a_soff)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
                                           uint32_t sa_off, uint32_t sa_step, uint32_t b_off,
                                           const uint32_t (&b_soff)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
                                           uint32_t sb_off) {
   using C = TileCfg<KIND, BM, BN, NS>;
   const uint32_t w = (uint32_t)wave_id();
+  if (w >= (uint32_t)C::LW) return;
   const uint32_t stage = lds + (uint32_t)(st * C::STAGE);
   const uint32_t soff = (uint32_t)ks * kRowBytes;
   if constexpr (PART != 1) {
 #pragma unroll
-    for (int t = 0; t < C::A_INSTR; ++t) dma16(src.ra, stage + (w + C::NW * t) * 1024, a_off[t], soff);
+    for (int t = 0; t < C::A_INSTR; ++t)
+      dma16(src.ra, stage + (w + C::LW * t) * 1024, a_off[t], soff + a_soff[t]);
   }
   if constexpr (PART != 2) {
 #pragma unroll
     for (int t = 0; t < C::B_INSTR; ++t)
-      dma16(src.rb, stage + C::A_BYTES + (w + C::NW * t) * 1024, b_off, soff + b_soff[t]);
+      dma16(src.rb, stage + C::A_BYTES + (w + C::LW * t) * 1024, b_off, soff + b_soff[t]);
   }
   // row scales: wave w stages rows [w * SA_ROWS, (w + 1) * SA_ROWS) in its 64
   // slots.  All lanes load (lanes past SA_ROWS fill padding from an in-bounds
@@ -140,13 +155,13 @@ __device__ __forceinline__ void tile_load(const TileSrc& src, uint32_t lds, int 
     dma4(src.rsb, stage + C::A_BYTES + C::B_BYTES + C::SA_BYTES + w * 256, sb_off, (uint32_t)ks * 4);
 }
 
-// Per-lane DMA offsets of the A and B tiles: lane slot (w + 4t) * 64 + lane
-// holds row slot / 8, physical chunk slot % 8, which carries logical chunk
-// (slot % 8) ^ swz(row).
-template <int NW>
+// Per-lane DMA offsets of the A and B tiles, LW loading waves: lane slot
+// (w + LW t) * 64 + lane holds row slot / 8, physical chunk slot % 8, which
+// carries logical chunk (slot % 8) ^ swz(row).
+template <int LW>
 __device__ __forceinline__ void dma_rows(int t_idx, int& row, int& qchunk) {
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int slot = (w + NW * t_idx) * 64 + lane;
+  const int slot = (w + LW * t_idx) * 64 + lane;
   row = slot / kChunks;
   qchunk = (slot % kChunks) ^ swz(row);
 }
@@ -304,6 +319,7 @@ template <int KIND, int BM, int BN, int NS, bool B_NEXT, typename F>
 __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, float* wsc, int wsc_row,
                                           int ksteps,
                                           const uint32_t (&a_off)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
+                                          const uint32_t (&a_soff)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
                                           const uint32_t& sa_off, uint32_t sa_step, uint32_t b_off,
                                           const uint32_t (&b_soff)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
                                           uint32_t sb_off, int up_split, int group,
@@ -340,15 +356,15 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, flo
   auto step_at = [&](int i) { const int k = i + rot; return k >= ksteps ? k - ksteps : k; };
   const uint32_t lbase = lds_addr(smem);
   auto load = [&](int slot, int i) {
-    tile_load<KIND, BM, BN, NS>(src, lbase, slot, step_at(i), a_off, sa_off, sa_step, b_off, b_soff,
+    tile_load<KIND, BM, BN, NS>(src, lbase, slot, step_at(i), a_off, a_soff, sa_off, sa_step, b_off, b_soff,
                                 sb_off);
   };
   // stage 0 in two parts around the activation offsets (the wait counts
   // below count whole stages issued after the one awaited: unchanged)
-  tile_load<KIND, BM, BN, NS, 1>(src, lbase, 0, step_at(0), a_off, sa_off, sa_step, b_off, b_soff,
+  tile_load<KIND, BM, BN, NS, 1>(src, lbase, 0, step_at(0), a_off, a_soff, sa_off, sa_step, b_off, b_soff,
                                  sb_off);
   activation_offsets();
-  tile_load<KIND, BM, BN, NS, 2>(src, lbase, 0, step_at(0), a_off, sa_off, sa_step, b_off, b_soff,
+  tile_load<KIND, BM, BN, NS, 2>(src, lbase, 0, step_at(0), a_off, a_soff, sa_off, sa_step, b_off, b_soff,
                                  sb_off);
 #pragma unroll
   for (int u = 1; u < NS - 1; ++u)
@@ -399,15 +415,17 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   TileSrc src;
   src.ra = make_desc(p.x, (uint32_t)((size_t)p.T * K));
   src.rb = make_desc(p.w1 + (size_t)e * N * K, (uint32_t)((size_t)N * K));
-  uint32_t a_off[C::A_INSTR], b_soff[C::B_INSTR];
+  uint32_t a_off[C::A_INSTR], a_soff[C::A_INSTR], b_soff[C::B_INSTR];
+#pragma unroll
+  for (int t = 0; t < C::A_INSTR; ++t) a_soff[t] = 0;  // gathered rows: all in a_off
   // B rows [0,128): the gate slice's weight rows; [128,256): the up slice's.
-  // Load t's rows are load 0's plus NW * 8 * t, all on one side of 128.
+  // Load t's rows are load 0's plus LW * 8 * t, all on one side of 128.
   int brow0, bq;
-  dma_rows<C::NW>(0, brow0, bq);
+  dma_rows<C::LW>(0, brow0, bq);
   const uint32_t b_off = (uint32_t)(s * 128 + brow0) * K + bq * 16;
 #pragma unroll
   for (int t = 0; t < C::B_INSTR; ++t) {
-    const int d = C::NW * 8 * t;
+    const int d = C::LW * 8 * t;
     b_soff[t] = (uint32_t)(d < 128 ? d : I - 128 + d) * K;
   }
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
@@ -427,21 +445,23 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
     src.bsc2 = nullptr;
   }
   // the gathered activation rows, once the route ids have arrived: issued
-  // after them, the weight-scale rows (blockwise: 4 loads) and the weight
-  // side of the first stage (B, and the MX weight scales) may be pending
+  // after them, the weight-scale rows (blockwise: 4 loads) and, in a
+  // loading wave, the weight side of the first stage (B, and the MX weight
+  // scales) may be pending
   auto activation_offsets = [&]() {
-    wait_vmcnt<(KIND == KIND_FP8B ? 4 : 0) + C::B_INSTR + (KIND == KIND_MX ? 1 : 0)>();
+    if (wid < C::LW) wait_vmcnt<(KIND == KIND_FP8B ? 4 : 0) + C::B_INSTR + (KIND == KIND_MX ? 1 : 0)>();
+    else wait_vmcnt<(KIND == KIND_FP8B ? 4 : 0)>();
     lds_barrier();
 #pragma unroll
     for (int t = 0; t < C::A_INSTR; ++t) {
       int row, q;
-      dma_rows<C::NW>(t, row, q);
+      dma_rows<C::LW>(t, row, q);
       a_off[t] = (uint32_t)route_token(p, id_of(row)) * K + q * 16;
     }
     sa_off = (uint32_t)route_token(p, id_of(srow < BM ? srow : 0)) * sa_row;
   };
   f32x4 acc[MI][NI];
-  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, 0, KS, a_off, sa_off, sa_step, b_off, b_soff,
+  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, 0, KS, a_off, a_soff, sa_off, sa_step, b_off, b_soff,
                                      sb_off, HALF, e, activation_offsets, acc);
 
   // SwiGLU: gate subtile j pairs with up subtile HALF + j (same columns)
@@ -526,7 +546,9 @@ template <int KIND, int BM, int NS>
 __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(1, BM >= 128 ? 2 : 1))) k_down_t(MoeArgs p) {
   using C = TileCfg<KIND, BM, 256, NS>;
   constexpr int MI = C::MI, NI = C::NI;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * C::STAGE];
+  constexpr int YROW = 256 * 2 + 16;  // bytes per staged bf16 output row (epilogue)
+  constexpr int SMEM = NS * C::STAGE > BM * YROW ? NS * C::STAGE : BM * YROW;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   __shared__ int ids[C::NW * 64];  // route id of row r at scale_slot<SA_ROWS>(r)
   __shared__ float wsc[2 * kScaleRow];
   const int K = p.K, I = p.I, IS = I / 128;
@@ -549,18 +571,22 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   TileSrc src;
   src.ra = make_desc(p.hq, (uint32_t)(rows_cap * I));
   src.rb = make_desc(p.w2 + (size_t)e * K * I, (uint32_t)((size_t)K * I));
-  uint32_t a_off[C::A_INSTR], b_soff[C::B_INSTR];
+  // the block's H rows are contiguous: load t's rows are load 0's plus
+  // LW * 8 * t, a wave-uniform offset, as for the weight rows
+  uint32_t a_off[C::A_INSTR], a_soff[C::A_INSTR], b_soff[C::B_INSTR];
+  int arow0, aq;
+  dma_rows<C::LW>(0, arow0, aq);
+  const uint32_t a_off0 = (uint32_t)((size_t)b * BM + arow0) * I + aq * 16;
 #pragma unroll
   for (int t = 0; t < C::A_INSTR; ++t) {
-    int row, q;
-    dma_rows<C::NW>(t, row, q);
-    a_off[t] = (uint32_t)((size_t)b * BM + row) * I + q * 16;
+    a_off[t] = a_off0;
+    a_soff[t] = (uint32_t)(C::LW * 8 * t) * I;
   }
   int brow0, bq;
-  dma_rows<C::NW>(0, brow0, bq);
+  dma_rows<C::LW>(0, brow0, bq);
   const uint32_t b_off = (uint32_t)(ct * 256 + brow0) * I + bq * 16;
 #pragma unroll
-  for (int t = 0; t < C::B_INSTR; ++t) b_soff[t] = (uint32_t)(C::NW * 8 * t) * I;
+  for (int t = 0; t < C::B_INSTR; ++t) b_soff[t] = (uint32_t)(C::LW * 8 * t) * I;
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
   const int c0 = ct * 256 + wn * (256 / C::WN);  // this wave's first output column
   if constexpr (KIND == KIND_FP8B) {
@@ -580,15 +606,13 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   }
   f32x4 acc[MI][NI];
   // all NI subtiles of a wave are contiguous output columns (no gate/up split)
-  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, c0 / 128 - 2 * ct, IS, a_off, sa_off, sa_step,
+  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, c0 / 128 - 2 * ct, IS, a_off, a_soff, sa_off, sa_step,
                                      b_off, b_soff, sb_off, NI, e, [] {}, acc);
   // the tile's rows rounded to bf16, staged in LDS (rows of 512 bytes plus
   // 16 bytes of padding), then written out as whole 512-byte row pieces with
   // non-temporal stores: the combine reads them once, much later, so they
   // need not displace the weight stream in L2 (K=4096, I=2048, E=288,
   // top-8: 1-2% of this kernel at T = 4096 and 8192)
-  constexpr int YROW = 256 * 2 + 16;
-  static_assert(BM * YROW <= NS * C::STAGE, "the bf16 tile fits the pipeline LDS");
   const int cw = wn * (256 / C::WN);  // this wave's first column within the tile
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
