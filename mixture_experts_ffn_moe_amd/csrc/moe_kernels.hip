@@ -1171,10 +1171,17 @@ void launch_down_d(const MoeArgs& a, hipStream_t st) {
                      st, a);
 }
 
+// The caller's depth, else the register budget's, capped by the walk: a
+// down GEMM over I = 256 has two K steps, and the 16-row MX kernel's depth
+// of 4 then costs its staged scale runs for nothing (MXFP8 K=4096, I=256,
+// E=32, top-8, whole call at T=8: 45 against 41 us with depth 2).
 template <int KIND, int BM>
 void launch_down(const MoeArgs& a, hipStream_t st) {
   if constexpr (BM <= 32) {
-    switch (a.depth) {
+    int depth = a.depth;
+    const int walk = a.I / 128;
+    if (!depth && walk < prefetch_depth<KIND, BM>()) depth = walk >= 2 ? 2 : 1;
+    switch (depth) {
       case 1: return launch_down_d<KIND, BM, 1>(a, st);
       case 2: return launch_down_d<KIND, BM, 2>(a, st);
       case 4: return launch_down_d<KIND, BM, 4>(a, st);
