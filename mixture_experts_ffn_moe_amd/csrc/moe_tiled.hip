@@ -36,9 +36,6 @@ namespace {
 constexpr int kRowBytes = 128;  // one K step of e4m3
 constexpr int kChunks = 8;      // 16-byte chunks per row
 constexpr int kScaleRow = 128;  // K steps of a weight block-scale row in LDS (K, I <= 16384)
-#ifndef LOADER_WAVES_8
-#define LOADER_WAVES_8 4  // loading waves of an 8-wave tile
-#endif
 
 __device__ __forceinline__ int swz(int row) { return row & 7; }
 
@@ -78,12 +75,16 @@ struct TileCfg {
   static constexpr int WN = NW / WM;            // wave columns
   static constexpr int MI = 4;                  // 16-row subtiles per wave
   static constexpr int NI = BN / WN / 16;       // 16-column subtiles per wave
-  // Waves that issue the tile's DMA loads: with two waves per SIMD, only
-  // the first wave of each SIMD loads (twice the instructions), so the
-  // other never holds its MFMAs behind a queue of vector-memory issues
-  // (K=4096, I=2048, E=288, top-8, T=8192, 256-row tiles: gate/up GEMM 1.54
-  // -> 1.43 ms).
-  static constexpr int LW = NW == 8 ? LOADER_WAVES_8 : NW;
+  // Waves that issue the tile's DMA loads (waves 0 .. LW-1).  With two
+  // waves per SIMD only the first wave of each SIMD loads (twice the
+  // instructions), so the other never holds its MFMAs behind a queue of
+  // vector-memory issues (K=4096, I=2048, E=288, top-8, T=8192, 256-row
+  // tiles: gate/up GEMM 1.54 -> 1.43 ms).  With one wave per SIMD (64-row
+  // tiles), blockwise FP8 loads from two SIMDs and leaves the other two to
+  // compute (K=7168, I=3072, E=384, top-6, zipf, T=256: 941 -> 909 us per
+  // call); MX keeps four, as its weight scales then need one instruction
+  // per 64 rows.
+  static constexpr int LW = NW == 8 ? 4 : (KIND == KIND_MX ? NW : 2);
   static constexpr int A_BYTES = BM * kRowBytes;
   static constexpr int B_BYTES = BN * kRowBytes;
   // Row scales (fp32, or 4 x e8m0 per row): each loading wave stages
@@ -99,7 +100,7 @@ struct TileCfg {
   static constexpr int S_INSTR = 1 + ((KIND == KIND_MX) ? 1 : 0);
   static constexpr int LOADS = A_INSTR + B_INSTR + S_INSTR;  // per loading wave per stage
   static constexpr int THREADS = NW * 64;
-  static_assert(SA_ROWS <= 64 && SB_ROWS <= 64, "one scale instruction per wave");
+  static_assert(SA_ROWS <= 64 && (KIND != KIND_MX || SB_ROWS <= 64), "one scale instruction per wave");
 };
 
 // Operand sources of one tile GEMM.
