@@ -78,10 +78,12 @@ typedef enum {
  *             groups per workgroup, 1 or 2 (2 needs K >= 256); each group
  *             of 4 waves walks part of K and the groups' sums are added in
  *             a fixed order.
- *   k_split   split mode, block_m 16 or 32: gate/up workgroups per (block,
- *             128-wide slice) tile, 1 or 4 (4 needs K / 128 a multiple of 8
- *             and at least 16, two K groups, and workspace for the partial
- *             sums: moe_workspace_size with the same tune).
+ *   k_split   split mode, block_m 16 or 32, or 64 with an e4m3 dtype
+ *             (blockwise FP8, MXFP8: the LDS-tiled kernels): gate/up
+ *             workgroups per (block, 128-wide slice) tile, 1 or 4 (4 needs
+ *             K / 128 a multiple of 8 and at least 16, at block_m 16 or 32
+ *             two K groups, and workspace for the partial sums:
+ *             moe_workspace_size with the same tune).
  *   prefetch  streaming kernels (block_m 16 or 32, split 0 or 1, k_split 1):
  *             K steps each wave keeps in flight, 1, 2 or 4.
  *   stages    LDS-tiled kernels (e4m3 dtypes, split mode, block_m 64 or

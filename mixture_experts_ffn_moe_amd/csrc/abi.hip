@@ -95,28 +95,36 @@ int pick_split(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_
   return (T * top_k <= 512 && weight_bytes <= 32e6) ? 0 : 1;
 }
 
-// Gate/up K split over 4 workgroups per tile (split mode, 16- or 32-row
-// streaming blocks) where few (block, slice) tiles exist: at most 128 by the
-// even-spread estimate, K/128 a multiple of 8 and at least 16.  Measured
-// (MXFP8, K=4096, I=256, E=32, top-8): see the kernel.
-bool kw_supported(int64_t K, int32_t block_m, int split) {
+// Gate/up K split over 4 workgroups per tile (split mode: 16- or 32-row
+// streaming blocks, or 64-row LDS-tiled blocks of the e4m3 dtypes) where few
+// (block, slice) tiles exist: at most 128 by the even-spread estimate, K/128
+// a multiple of 8 and at least 16.  Measured (MXFP8, K=4096, I=256, E=32,
+// top-8): see the kernels.
+bool kw_supported(int32_t dtype, int64_t K, int64_t I, int32_t block_m, int split) {
   const int64_t KS = K / 128;
-  return split == 1 && block_m <= 32 && KS % 8 == 0 && KS >= 16;
+  if (split != 1 || KS % 8 || KS < 16) return false;
+  if (block_m <= 32) return true;
+  return block_m == 64 && tiled_supported(dtype, block_m, (int)K, (int)I);
 }
 
 int pick_kw(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E, int32_t top_k,
             int32_t block_m, int split, const moe_tune* tune = nullptr) {
   if (tune && tune->k_split) return tune->k_split;
-  if (!kw_supported(K, block_m, split)) return 1;
-  const int64_t R = T * top_k;
-  const int64_t tiles = (R < E ? R : (int64_t)E) * ((N / 2) / 128);
-  (void)dtype;
-  return tiles <= 128 ? 4 : 1;
+  if (!kw_supported(dtype, K, N / 2, block_m, split)) return 1;
+  const int64_t R = T * top_k, S = (N / 2) / 128;
+  const int64_t spread = R < E ? R : (int64_t)E;  // blocks if every route's expert differs
+  if (block_m <= 32) return spread * S <= 128 ? 4 : 1;
+  // 64-row tiles hold a CU each (their LDS): split while four workgroups per
+  // tile still fit on the 256 CUs at once (MXFP8, K=4096, I=256, E=32,
+  // top-8: gate/up GEMM 34.7 -> 26.6 us at T=128, 64 tiles; at T=512, 128
+  // tiles, 36.4 against 56.0 us split)
+  const int64_t blocks = spread > (R + block_m - 1) / block_m ? spread : (R + block_m - 1) / block_m;
+  return blocks * S * 4 <= 256 ? 4 : 1;
 }
 
 // Schedule overrides: every set field must name a variant the call's
 // kernels have (checked before anything is launched).
-int check_tune(int32_t dtype, int64_t K, int32_t block_m, int split, const moe_tune* t) {
+int check_tune(int32_t dtype, int64_t K, int64_t I, int32_t block_m, int split, const moe_tune* t) {
   if (!t) return MOE_OK;
   const bool streaming = block_m <= 32 || dtype == MOE_BF16 || dtype == MOE_MXFP4;
   if (t->k_groups) {
@@ -130,9 +138,10 @@ int check_tune(int32_t dtype, int64_t K, int32_t block_m, int split, const moe_t
   if (t->k_split) {
     if (t->k_split != 1 && t->k_split != 4)
       return fail(MOE_ERR_UNSUPPORTED, "tune.k_split must be 0, 1 or 4 (got %d)", t->k_split);
-    if (t->k_split == 4 && !kw_supported(K, block_m, split))
+    if (t->k_split == 4 && !kw_supported(dtype, K, I, block_m, split))
       return fail(MOE_ERR_UNSUPPORTED,
-                  "tune.k_split = 4 needs split 1, block_m 16 or 32, K/128 a multiple of 8 and >= 16");
+                  "tune.k_split = 4 needs split 1, block_m 16 or 32 (or 64 with an e4m3 dtype), K/128 "
+                  "a multiple of 8 and >= 16");
     if (t->k_split == 4 && t->k_groups == 1)
       return fail(MOE_ERR_UNSUPPORTED, "tune.k_split = 4 runs two K groups per workgroup");
   }
@@ -240,7 +249,7 @@ int run_ffn(int32_t dtype, const void* x, const void* xs, const void* w1, const 
   if (split == 2 && block_m > 32)
     return fail(MOE_ERR_UNSUPPORTED, "the ring mode runs block_m 16 or 32 (got %d)", block_m);
   const int sp = split < 0 ? pick_split(dtype, T, K, N, E_all, k_all, block_m) : split;
-  rc = check_tune(dtype, K, block_m, sp, tune);
+  rc = check_tune(dtype, K, N / 2, block_m, sp, tune);
   if (rc) return rc;
   if (T == 0) return ok();
   if (down_only) {
@@ -638,7 +647,7 @@ int moe_workspace_size(int32_t dtype, int64_t T, int64_t K, int64_t N, int32_t E
   if (split == 2 && block_m > 32)
     return fail(MOE_ERR_UNSUPPORTED, "the ring mode runs block_m 16 or 32 (got %d)", block_m);
   const int sp = split < 0 ? pick_split(dtype, T, K, N, E, top_k, block_m) : split;
-  rc = check_tune(dtype, K, block_m, sp, tune);
+  rc = check_tune(dtype, K, N / 2, block_m, sp, tune);
   if (rc) return rc;
   *bytes = layout(dtype, T, K, N, E, top_k, block_m, sp, tune).total;
   return ok();

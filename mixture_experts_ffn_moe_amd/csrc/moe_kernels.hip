@@ -1310,8 +1310,9 @@ hipError_t launch_kind_bm(int split, const MoeArgs& a, hipStream_t st, const Tim
   if (split) {
     size_t fbytes = (R * 4 + 15) / 16;
     if (a.kw > 1) {
-      // the tile tickets follow the flags: one clear for both
-      if constexpr (BM > 32) return hipErrorInvalidValue;
+      // the tile tickets follow the flags: one clear for both (streaming
+      // blocks, or the 64-row tiled kernels)
+      if (BM > 64 || (BM == 64 && !tiled_supported(KIND, BM, a.K, a.I))) return hipErrorInvalidValue;
       if (a.kw != kUpKW || reinterpret_cast<uint8_t*>(a.tickets) <
                                reinterpret_cast<uint8_t*>(a.flags) + R * 4)
         return hipErrorInvalidValue;

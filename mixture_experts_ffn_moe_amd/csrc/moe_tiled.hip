@@ -306,8 +306,9 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const fl
   }
 }
 
-// One workgroup tile: acc[mi][ni] over all K steps, visiting the steps from
-// a staggered start, NS stages in flight (stage slots in one LDS array).
+// One workgroup tile: acc[mi][ni] over the K steps [k0, k0 + ksteps),
+// visiting them from a staggered start, NS stages in flight (stage slots in
+// one LDS array).  kscale: K steps of the weight block-scale rows staged.
 // The tile's first requests go out before anything waits: the blockwise
 // weight-scale rows of the tile's two 128-row weight blocks (src.bsc and
 // src.bsc2, into `wsc`, 2 x kScaleRow floats of LDS; the wave reads them
@@ -318,7 +319,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* stage, int ks, const fl
 // explicit waits are the only ones.
 template <int KIND, int BM, int BN, int NS, bool B_NEXT, typename F>
 __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, float* wsc, int wsc_row,
-                                          int ksteps,
+                                          int ksteps, int k0, int kscale,
                                           const uint32_t (&a_off)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
                                           const uint32_t (&a_soff)[TileCfg<KIND, BM, BN, NS>::A_INSTR],
                                           const uint32_t& sa_off, uint32_t sa_step, uint32_t b_off,
@@ -337,7 +338,7 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, flo
     // descriptor's bound returns zeros)
     const int lane = threadIdx.x & 63;
     const uint32_t m0 = lds_addr(wsc);
-    const uint32_t bytes = (uint32_t)ksteps * 4;
+    const uint32_t bytes = (uint32_t)kscale * 4;
     const desc_t r1 = make_desc(src.bsc, bytes);
     const desc_t r2 = make_desc(src.bsc2 ? src.bsc2 : src.bsc, bytes);
     dma4(r1, m0, lane * 4, 0);
@@ -354,7 +355,7 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, flo
   // top-8, T=8192.)  Other experts start elsewhere, which spreads the weight
   // rows read at one moment over the HBM channels.
   const int rot = (int)((((uint32_t)group * 2654435761u) >> 16) % (uint32_t)ksteps);
-  auto step_at = [&](int i) { const int k = i + rot; return k >= ksteps ? k - ksteps : k; };
+  auto step_at = [&](int i) { const int k = i + rot; return k0 + (k >= ksteps ? k - ksteps : k); };
   const uint32_t lbase = lds_addr(smem);
   auto load = [&](int slot, int i) {
     tile_load<KIND, BM, BN, NS>(src, lbase, slot, step_at(i), a_off, a_soff, sa_off, sa_step, b_off, b_soff,
@@ -386,8 +387,13 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, flo
 }
 
 
-// gate/up GEMM + SwiGLU + requantization, one (block, 128-wide slice) tile
-template <int KIND, int BM, int NS>
+// gate/up GEMM + SwiGLU + requantization, one (block, 128-wide slice) tile.
+// KW > 1 (64-row tiles, few tiles): KW workgroups per tile, workgroup kw
+// summing the K steps [kw KS/KW, (kw+1) KS/KW).  Each stores its raw sums in
+// the workspace with device-scope stores and takes a ticket; the last of the
+// tile's workgroups adds the KW sums in the order kw = 0, 1, .. (the result
+// does not depend on which one is last) and runs the epilogue.
+template <int KIND, int BM, int NS, int KW>
 __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(1, BM >= 128 ? 2 : 1))) k_up_t(MoeArgs p) {
   using C = TileCfg<KIND, BM, 256, NS>;
   constexpr int MI = C::MI, NI = C::NI, HALF = NI / 2;
@@ -396,9 +402,11 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   __shared__ float lds_amax[C::WN * BM];
   __shared__ float wsc[2 * kScaleRow];
   const int S = p.I / 128;
-  const int logical = xcd_remap(blockIdx.x, (*p.ntp / BM) * S);
+  // the KW workgroups of a tile are consecutive, on one XCD
+  const int logical = xcd_remap(blockIdx.x, (*p.ntp / BM) * S * KW);
   if (logical < 0) return;
-  const int b = logical / S, s = logical % S;
+  const int tile = logical / KW, kw = logical % KW;
+  const int b = tile / S, s = tile % S;
   if (b >= p.blocks_cap || b * BM >= *p.ntp) return;
   const int e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);  // uniform: descriptors in SGPRs
   if ((unsigned)e >= (unsigned)p.E) return;
@@ -462,8 +470,44 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
     sa_off = (uint32_t)route_token(p, id_of(srow < BM ? srow : 0)) * sa_row;
   };
   f32x4 acc[MI][NI];
-  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, 0, KS, a_off, a_soff, sa_off, sa_step, b_off, b_soff,
-                                     sb_off, HALF, e, activation_offsets, acc);
+  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, 0, KS / KW, kw * (KS / KW), KS, a_off, a_soff,
+                                     sa_off, sa_step, b_off, b_soff, sb_off, HALF, e,
+                                     activation_offsets, acc);
+  if constexpr (KW > 1) {
+    constexpr int PER = MI * NI * 4;  // floats per lane
+    __shared__ int last;
+    float* const pt = p.part + (size_t)tile * KW * (C::THREADS * PER);
+    float* const dst = pt + ((size_t)kw * C::NW + wid) * PER * 64 + lane;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          __hip_atomic_store(dst + ((mi * NI + ni) * 4 + i) * 64, acc[mi][ni][i], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    // the sums have been acknowledged device-wide before the ticket moves
+    asm volatile("" ::: "memory");
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) last = atomicAdd(p.tickets + tile, 1) == KW - 1;
+    __syncthreads();
+    if (!last) return;
+    const float* const src_p = pt + (size_t)wid * PER * 64 + lane;
+#pragma unroll
+    for (int q = 0; q < KW; ++q)
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = __hip_atomic_load(src_p + (size_t)q * C::NW * PER * 64 + ((mi * NI + ni) * 4 + i) * 64,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            acc[mi][ni][i] = q == 0 ? v : acc[mi][ni][i] + v;
+          }
+  }
 
   // SwiGLU: gate subtile j pairs with up subtile HALF + j (same columns)
   float h[MI][HALF][4];
@@ -607,7 +651,7 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   }
   f32x4 acc[MI][NI];
   // all NI subtiles of a wave are contiguous output columns (no gate/up split)
-  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, c0 / 128 - 2 * ct, IS, a_off, a_soff, sa_off, sa_step,
+  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, c0 / 128 - 2 * ct, IS, 0, IS, a_off, a_soff, sa_off, sa_step,
                                      b_off, b_soff, sb_off, NI, e, [] {}, acc);
   // the tile's rows rounded to bf16, staged in LDS (rows of 512 bytes plus
   // 16 bytes of padding), then written out as whole 512-byte row pieces with
@@ -638,10 +682,17 @@ template <int KIND, int BM, int NS>
 hipError_t launch_tiled_ns(const MoeArgs& a, hipStream_t st, const TimingHook& hk) {
   constexpr int TH = TileCfg<KIND, BM, 256, NS>::THREADS;
   const int S = a.I / 128;
-  const unsigned g_up = (unsigned)(((size_t)a.blocks_cap * S + 7) / 8 * 8);
+  const int kw = a.kw > 1 ? a.kw : 1;
+  if (kw != 1 && (BM != 64 || kw != 4)) return hipErrorInvalidValue;
+  const unsigned g_up = (unsigned)(((size_t)a.blocks_cap * S * kw + 7) / 8 * 8);
   const unsigned g_dn = (unsigned)(((size_t)a.blocks_cap * (a.K / 256) + 7) / 8 * 8);
   if (hk.which == 1 && hk.before) (void)hipEventRecord(hk.before, st);
-  hipLaunchKernelGGL((k_up_t<KIND, BM, NS>), dim3(g_up), dim3(TH), 0, st, a);
+  if constexpr (BM == 64) {
+    if (kw == 4) hipLaunchKernelGGL((k_up_t<KIND, BM, NS, 4>), dim3(g_up), dim3(TH), 0, st, a);
+    else hipLaunchKernelGGL((k_up_t<KIND, BM, NS, 1>), dim3(g_up), dim3(TH), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_up_t<KIND, BM, NS, 1>), dim3(g_up), dim3(TH), 0, st, a);
+  }
   if (hk.which == 1 && hk.after) (void)hipEventRecord(hk.after, st);
   if (hk.which == 2 && hk.before) (void)hipEventRecord(hk.before, st);
   hipLaunchKernelGGL((k_down_t<KIND, BM, NS>), dim3(g_dn), dim3(TH), 0, st, a);

@@ -170,6 +170,11 @@ def test_tune_errors_before_launch(fn):
         assert _ffn(L, fn, T=0, bm=16, split=1, tune=t) == 0, t
         assert _ffn(L, fn, T=0, bm=32, split=0, tune={k: v for k, v in t.items()
                                                          if k != "k_split"}) == 0, t
+    # the gate/up K split: 16- and 32-row streaming blocks, and the 64-row
+    # LDS-tiled kernels of the e4m3 dtypes
+    assert _ffn(L, fn, T=0, bm=64, split=1, tune={"k_split": 4}) == (0 if tiled else -3)
+    assert _ffn(L, fn, bm=128, split=1, tune={"k_split": 4}) == -3
+    assert _ffn(L, fn, K=1024, bm=64, split=1, tune={"k_split": 4}) == -3   # K / 128 < 16
     if tiled:
         for st in (2, 3):
             assert _ffn(L, fn, T=0, bm=128, split=1, tune={"stages": st}) == 0

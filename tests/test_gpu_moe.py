@@ -291,6 +291,40 @@ def test_k_split_over_workgroups_parity(kind, bm):
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))
 
 
+@pytest.mark.parametrize("kind", ["fp8_blockwise", "mxfp8"])
+@pytest.mark.parametrize("T", [20, 300])
+def test_tiled_k_split_parity(kind, T):
+    """64-row LDS-tiled gate/up GEMM with few tiles (8 experts x 2 slices):
+    K split over four workgroups per tile, the last adding the four sums in
+    order; one block per expert (T = 20) and two, the second ragged (T =
+    300).  Against the oracle, bitwise repeatable, and through the same
+    kernels' K split = 1 within the gate."""
+    c = small_case(kind, T=T, E=8, k=2, K=2048, I=256, tag="gpu-kw-tiled")
+    assert moe.moe_workspace_size(kind, T, 2048, 512, 8, 2, 64, split=1) > \
+        moe.moe_workspace_size(kind, T, 2048, 512, 8, 2, 64, split=1, tune={"k_split": 1})
+    out, _, _ = check(c, 64, 1, label="tiled k split over workgroups")
+    again, _ = moe.run_case(c, block_m=64, split=1)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    check(c, 64, 1, tune={"k_split": 1}, label="tiled, one workgroup per tile")
+
+
+def test_tiled_k_split_reused_workspace():
+    """The tiled K split's tickets are cleared by every call: one workspace
+    for three calls in a row, the second smaller."""
+    a = small_case("fp8_blockwise", T=300, E=8, k=2, K=2048, I=256, tag="gpu-kwt-a")
+    b = small_case("fp8_blockwise", T=40, E=8, k=2, K=2048, I=256, tag="gpu-kwt-b")
+    need = moe.moe_workspace_size("fp8_blockwise", 300, 2048, 512, 8, 2, 64, split=1)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for c in (a, b, a):
+        out, _ = moe.run_case(c, block_m=64, split=1, workspace=ws)
+        torch.cuda.synchronize()
+        ref, _ = moe.run_case(c, block_m=64, split=1)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    check(b, 64, 1, label="tiled k split, second call")
+
+
 def test_k_split_over_workgroups_reused_workspace():
     """One workspace for two calls in a row, the second smaller: the tile
     tickets are cleared by each call."""
