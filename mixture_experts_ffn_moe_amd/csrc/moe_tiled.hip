@@ -586,18 +586,21 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   }
 }
 
-// down GEMM, one (block, 256 output columns) tile, bf16 per-route rows
-template <int KIND, int BM, int NS>
-__global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(1, BM >= 128 ? 2 : 1))) k_down_t(MoeArgs p) {
-  using C = TileCfg<KIND, BM, 256, NS>;
+// down GEMM, one (block, BN output columns) tile, bf16 per-route rows.
+// BN = 128 for short K walks at 64-row tiles (two workgroups then share a
+// CU; see the launcher), 256 otherwise.
+template <int KIND, int BM, int NS, int BN>
+__global__ void __launch_bounds__(BM >= 128 ? 512 : 256)
+__attribute__((amdgpu_waves_per_eu(1, BM >= 128 || BN == 128 ? 2 : 1))) k_down_t(MoeArgs p) {
+  using C = TileCfg<KIND, BM, BN, NS>;
   constexpr int MI = C::MI, NI = C::NI;
-  constexpr int YROW = 256 * 2 + 16;  // bytes per staged bf16 output row (epilogue)
+  constexpr int YROW = BN * 2 + 16;  // bytes per staged bf16 output row (epilogue)
   constexpr int SMEM = NS * C::STAGE > BM * YROW ? NS * C::STAGE : BM * YROW;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   __shared__ int ids[C::NW * 64];  // route id of row r at scale_slot<SA_ROWS>(r)
   __shared__ float wsc[2 * kScaleRow];
   const int K = p.K, I = p.I, IS = I / 128;
-  const int NT = K / 256;
+  const int NT = K / BN;
   const int logical = xcd_remap(blockIdx.x, (*p.ntp / BM) * NT);
   if (logical < 0) return;
   const int b = logical / NT, ct = logical % NT;
@@ -629,36 +632,36 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   }
   int brow0, bq;
   dma_rows<C::LW>(0, brow0, bq);
-  const uint32_t b_off = (uint32_t)(ct * 256 + brow0) * I + bq * 16;
+  const uint32_t b_off = (uint32_t)(ct * BN + brow0) * I + bq * 16;
 #pragma unroll
   for (int t = 0; t < C::B_INSTR; ++t) b_soff[t] = (uint32_t)(C::LW * 8 * t) * I;
   uint32_t sa_off = 0, sa_step = 4, sb_off = 0;
-  const int c0 = ct * 256 + wn * (256 / C::WN);  // this wave's first output column
+  const int c0 = ct * BN + wn * (BN / C::WN);  // this wave's first output column
   if constexpr (KIND == KIND_FP8B) {
     src.rsa = make_desc(p.hs, (uint32_t)(rows_cap * IS * 4));
     sa_off = (uint32_t)((size_t)b * BM + (srow < BM ? srow : 0)) * IS * 4;
-    // the tile's two 128-column weight blocks; the wave's is c0 / 128
-    src.bsc = reinterpret_cast<const float*>(p.w2s) + ((size_t)e * (K / 128) + 2 * ct) * IS;
-    src.bsc2 = src.bsc + IS;
+    // the tile's 128-column weight blocks (two at BN = 256); the wave's is c0 / 128
+    src.bsc = reinterpret_cast<const float*>(p.w2s) + ((size_t)e * (K / 128) + (BN / 128) * ct) * IS;
+    src.bsc2 = BN == 256 ? src.bsc + IS : src.bsc;
   } else {
     src.rsa = make_desc(p.hs, (uint32_t)(rows_cap * (I / 32)));
     sa_off = (uint32_t)((size_t)b * BM + (srow < BM ? srow : 0)) * (I / 32);
     src.rsb = make_desc(reinterpret_cast<const uint8_t*>(p.w2s) + (size_t)e * K * (I / 32),
                         (uint32_t)((size_t)K * (I / 32)));
-    sb_off = (uint32_t)(ct * 256 + (wid * C::SB_ROWS + lane) % 256) * (I / 32);
+    sb_off = (uint32_t)(ct * BN + (wid * C::SB_ROWS + lane) % BN) * (I / 32);
     src.bsc = nullptr;
     src.bsc2 = nullptr;
   }
   f32x4 acc[MI][NI];
   // all NI subtiles of a wave are contiguous output columns (no gate/up split)
-  tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, c0 / 128 - 2 * ct, IS, 0, IS, a_off, a_soff, sa_off, sa_step,
+  tile_gemm<KIND, BM, BN, NS, true>(src, smem, wsc, c0 / 128 - (BN / 128) * ct, IS, 0, IS, a_off, a_soff, sa_off, sa_step,
                                      b_off, b_soff, sb_off, NI, e, [] {}, acc);
-  // the tile's rows rounded to bf16, staged in LDS (rows of 512 bytes plus
-  // 16 bytes of padding), then written out as whole 512-byte row pieces with
+  // the tile's rows rounded to bf16, staged in LDS (rows of 2 BN bytes plus
+  // 16 bytes of padding), then written out as whole 2 BN-byte row pieces with
   // non-temporal stores: the combine reads them once, much later, so they
   // need not displace the weight stream in L2 (K=4096, I=2048, E=288,
   // top-8: 1-2% of this kernel at T = 4096 and 8192)
-  const int cw = wn * (256 / C::WN);  // this wave's first column within the tile
+  const int cw = wn * (BN / C::WN);  // this wave's first column within the tile
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -668,14 +671,37 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
       for (int ni = 0; ni < NI; ++ni) yrow[cw + ni * 16 + r16] = f32_to_bf16(acc[mi][ni][i4]);
     }
   __syncthreads();
-  for (int c = threadIdx.x; c < BM * 32; c += C::THREADS) {
-    const int row = c / 32, ch = c % 32;
+  for (int c = threadIdx.x; c < BM * (BN / 8); c += C::THREADS) {
+    const int row = c / (BN / 8), ch = c % (BN / 8);
     const int id = ids[scale_slot<C::SA_ROWS>(row)];
     if (id < 0) continue;
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(smem + row * YROW + ch * 16),
-                                reinterpret_cast<u32x4*>(p.yr + (size_t)id * K + ct * 256 + ch * 8));
+                                reinterpret_cast<u32x4*>(p.yr + (size_t)id * K + ct * BN + ch * 8));
   }
+}
+
+template <int KIND, int BM, int NS, int BN>
+void launch_down_bn(const MoeArgs& a, hipStream_t st) {
+  constexpr int TH = TileCfg<KIND, BM, BN, NS>::THREADS;
+  const unsigned g_dn = (unsigned)(((size_t)a.blocks_cap * (a.K / BN) + 7) / 8 * 8);
+  hipLaunchKernelGGL((k_down_t<KIND, BM, NS, BN>), dim3(g_dn), dim3(TH), 0, st, a);
+}
+
+// Output columns per down-GEMM tile: 256, or 128 at 64-row tiles whose K
+// walk is short (I <= 512).  There the tile's fixed costs (first loads,
+// epilogue) outweigh its four steps, and 128 columns bring its LDS to 77 KiB
+// in three stages, so two workgroups share a CU and overlap them (MXFP8,
+// K=4096, I=256, E=32, top-8: down GEMM 18.2 -> 14.5 us at T=128, 35.3 ->
+// 25.8 us at T=512).  Over longer walks the halved tile reads its
+// activation rows twice as often (blockwise FP8, I=2048: 454 against 478 us
+// at T=1024).
+template <int KIND, int BM, int NS>
+void launch_down_t(const MoeArgs& a, hipStream_t st) {
+  if constexpr (BM == 64) {
+    if (a.I <= 512) return launch_down_bn<KIND, BM, NS, 128>(a, st);
+  }
+  launch_down_bn<KIND, BM, NS, 256>(a, st);
 }
 
 template <int KIND, int BM, int NS>
@@ -685,7 +711,6 @@ hipError_t launch_tiled_ns(const MoeArgs& a, hipStream_t st, const TimingHook& h
   const int kw = a.kw > 1 ? a.kw : 1;
   if (kw != 1 && (BM != 64 || kw != 4)) return hipErrorInvalidValue;
   const unsigned g_up = (unsigned)(((size_t)a.blocks_cap * S * kw + 7) / 8 * 8);
-  const unsigned g_dn = (unsigned)(((size_t)a.blocks_cap * (a.K / 256) + 7) / 8 * 8);
   if (hk.which == 1 && hk.before) (void)hipEventRecord(hk.before, st);
   if constexpr (BM == 64) {
     if (kw == 4) hipLaunchKernelGGL((k_up_t<KIND, BM, NS, 4>), dim3(g_up), dim3(TH), 0, st, a);
@@ -695,17 +720,14 @@ hipError_t launch_tiled_ns(const MoeArgs& a, hipStream_t st, const TimingHook& h
   }
   if (hk.which == 1 && hk.after) (void)hipEventRecord(hk.after, st);
   if (hk.which == 2 && hk.before) (void)hipEventRecord(hk.before, st);
-  hipLaunchKernelGGL((k_down_t<KIND, BM, NS>), dim3(g_dn), dim3(TH), 0, st, a);
+  launch_down_t<KIND, BM, NS>(a, st);
   if (hk.which == 2 && hk.after) (void)hipEventRecord(hk.after, st);
   return hipGetLastError();
 }
 
 template <int KIND, int BM>
 hipError_t launch_tiled_down_kind(const MoeArgs& a, hipStream_t st) {
-  constexpr int NS = BM == 256 ? 2 : 3;
-  constexpr int TH = TileCfg<KIND, BM, 256, NS>::THREADS;
-  const unsigned g_dn = (unsigned)(((size_t)a.blocks_cap * (a.K / 256) + 7) / 8 * 8);
-  hipLaunchKernelGGL((k_down_t<KIND, BM, NS>), dim3(g_dn), dim3(TH), 0, st, a);
+  launch_down_t<KIND, BM, BM == 256 ? 2 : 3>(a, st);
   return hipGetLastError();
 }
 

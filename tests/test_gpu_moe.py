@@ -258,7 +258,8 @@ def test_ksplit_deterministic():
 
 @pytest.mark.parametrize("bm", [64, 128, 256])
 @pytest.mark.parametrize("kind,K,I", [("fp8_blockwise", 768, 384), ("mxfp8", 512, 256),
-                                      ("fp8_blockwise", 256, 128)])
+                                      ("fp8_blockwise", 256, 128), ("fp8_blockwise", 512, 640),
+                                      ("mxfp8", 256, 640)])
 def test_tiled_split_parity(kind, K, I, bm):
     """The LDS-tiled split-mode kernels (block_m 64 / 128, K a multiple of
     256): several blocks per expert, several K steps and slices, ragged last
