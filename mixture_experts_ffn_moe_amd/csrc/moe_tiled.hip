@@ -1,5 +1,5 @@
 // moe_tiled.hip -- LDS-tiled split-mode kernels for many rows per expert
-// (block_m 64 and 128, e4m3 paths: blockwise FP8 and MXFP8).
+// (block_m 64, 128 and 256, e4m3 paths: blockwise FP8 and MXFP8).
 //
 // Same computation as k_up / k_down in moe_kernels.hip ([hpc-ops RFC]
 // "Background" stages 2-4; [prime-flash] introduction, split=True), organized
@@ -8,8 +8,9 @@
 //
 //  * A (activation rows) and B (weight rows) of one 128-wide K step are
 //    staged in LDS with direct-to-LDS 16-byte buffer loads (no VGPR staging),
-//    NSTAGE steps in flight.  Every wave then reads its MFMA fragments from
-//    LDS, so each operand byte crosses the L2 -> CU path once per workgroup.
+//    NS steps in flight.  Every wave then reads its MFMA fragments from LDS,
+//    so each operand byte crosses the L2 -> CU path once per workgroup.  Only
+//    some waves issue those loads (see TileCfg::LW).
 //  * LDS rows are 128 bytes (8 chunks of 16 bytes); chunk q of row r is stored
 //    at chunk q ^ (r & 7).  Measured on gfx950 with the fragment pattern (lane
 //    (g, r) reading chunks g and 4 + g of row r of a 16-row group), this plain
@@ -19,15 +20,17 @@
 //    loads write LDS in lane order, so each lane fetches the logical chunk
 //    that belongs in its slot.
 //  * Workgroup tile: block_m rows x (128 gate + 128 up) for k_up_t,
-//    block_m rows x 256 output columns for k_down_t; 4 waves arranged
-//    (block_m / 64) x (4 / (block_m / 64)); a wave owns 64 rows.
+//    block_m rows x 256 (or 128) output columns for k_down_t; a wave owns 64
+//    rows, 4 waves at block_m 64, 8 (two per SIMD) from 128 on.
 //  * Blockwise scales: the activation row scales of each step ride along in
-//    LDS (4-byte direct loads); weight block scales are wave-uniform scalar
-//    loads.  MX: the e8m0 dwords of each row (4 K blocks per step) ride along
-//    in LDS and feed the block-scaled MFMA.
+//    LDS (4-byte direct loads); the weight block-scale rows of the tile are
+//    loaded into LDS once.  MX: the e8m0 dwords of each row (4 K blocks per
+//    step) ride along in LDS and feed the block-scaled MFMA.
 //  * Workgroup ids are remapped so that consecutive tiles (the slices of one
 //    block, then the next block of the same expert) land on one XCD and share
 //    its L2.
+//  * With few tiles (64-row blocks), the gate/up GEMM splits K over four
+//    workgroups per tile, reduced in a fixed order by the last one.
 #include "device.h"
 #include "launch.h"
 
