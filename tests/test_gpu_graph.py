@@ -26,8 +26,9 @@ pytestmark = pytest.mark.gpu
 
 # kind, T, E, top_k, block_m, split, shape overrides; together they run the
 # streaming split kernels, the gate/up GEMM with K split over workgroups
-# (K=2048, few tiles), the fused kernel, the LDS-tiled kernels, the ring
-# mode and the chunked planner (more than 16,384 routes)
+# (K=2048, few tiles: streaming and 64-row tiled), the fused kernel, the
+# LDS-tiled kernels at 64, 128 and 256 rows, the ring mode and the chunked
+# planner (more than 16,384 routes)
 CASES = [
     ("fp8_blockwise", 8, 16, 2, 16, 1, dict(K=2048, I=256)),
     ("fp8_blockwise", 200, 16, 4, 32, 1, {}),
@@ -38,6 +39,9 @@ CASES = [
     ("bf16", 2100, 64, 8, 64, 1, dict(K=256, I=128)),
     ("mxfp8", 200, 8, 4, 32, 1, {}),
     ("mxfp4", 50, 8, 2, 16, 1, {}),
+    ("mxfp8", 128, 8, 4, 64, 1, dict(K=2048, I=256)),
+    ("fp8_blockwise", 600, 8, 2, 128, 1, dict(K=512, I=256)),
+    ("fp8_blockwise", 1200, 4, 2, 256, 1, dict(K=512, I=256)),
 ]
 
 
