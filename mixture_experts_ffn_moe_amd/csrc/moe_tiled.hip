@@ -28,7 +28,8 @@
 //    step) ride along in LDS and feed the block-scaled MFMA.
 //  * Workgroup ids are remapped so that consecutive tiles (the slices of one
 //    block, then the next block of the same expert) land on one XCD and share
-//    its L2.
+//    its L2; where eight consecutive blocks belong to one expert, the slices
+//    run outermost over those blocks (tile_coords).
 //  * With few tiles (64-row blocks), the gate/up GEMM splits K over four
 //    workgroups per tile, reduced in a fixed order by the last one.
 #include "device.h"
@@ -65,6 +66,38 @@ __device__ __forceinline__ int xcd_remap(int bid, int valid) {
   const int per = (valid + 7) / 8;
   const int j = bid / 8;
   return j < per ? (bid % 8) * per + j : -1;
+}
+
+// Block b, column tile ct and expert e of logical tile `tile` (NT column
+// tiles per block: gate/up slices or down output tiles; nb planner blocks
+// hold routes).  Blocks go in aligned groups of kGroup.  A group whose
+// blocks all belong to one expert (a heavily loaded expert under skewed
+// routing) is walked column tile by column tile, its kGroup blocks inner, so
+// the workgroups that run together on one XCD read a few weight slices and
+// a few blocks' rows, both shared in its L2; block by block, every block
+// re-read the expert's whole weights from beyond L2 (K=7168, I=3072, E=384,
+// top-6, zipf, T=4096: 31 blocks of 128 rows on the busiest expert).  Other
+// groups, and the last partial one, go block by block.  Either order is a
+// permutation of the same tiles, so the result does not depend on it.
+constexpr int kGroup = 8;
+__device__ __forceinline__ void tile_coords(int tile, int NT, int nb, const int32_t* expert_ids,
+                                            int& b, int& ct, int& e) {
+  const int b0 = tile / (kGroup * NT) * kGroup;
+  const int lane = threadIdx.x & 63;
+  int eid = -1;  // lane j < kGroup: expert of block b0 + j (one load for the group)
+  if (lane < kGroup && b0 + lane < nb) eid = expert_ids[b0 + lane];
+  const int e_first = __builtin_amdgcn_readlane(eid, 0);
+  const int e_last = __builtin_amdgcn_readlane(eid, kGroup - 1);
+  if (b0 + kGroup <= nb && e_first == e_last) {
+    const int r = tile - b0 * NT;
+    ct = r / kGroup;
+    b = b0 + r % kGroup;
+    e = e_first;
+  } else {
+    b = tile / NT;
+    ct = tile % NT;
+    e = __builtin_amdgcn_readlane(eid, b - b0);
+  }
 }
 
 template <int KIND, int BM, int BN, int NS>
@@ -406,12 +439,13 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   __shared__ float wsc[2 * kScaleRow];
   const int S = p.I / 128;
   // the KW workgroups of a tile are consecutive, on one XCD
-  const int logical = xcd_remap(blockIdx.x, (*p.ntp / BM) * S * KW);
+  const int nb = *p.ntp / BM;
+  const int logical = xcd_remap(blockIdx.x, nb * S * KW);
   if (logical < 0) return;
   const int tile = logical / KW, kw = logical % KW;
-  const int b = tile / S, s = tile % S;
-  if (b >= p.blocks_cap || b * BM >= *p.ntp) return;
-  const int e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);  // uniform: descriptors in SGPRs
+  int b, s, e;  // e uniform: descriptors in SGPRs
+  tile_coords(tile, S, nb, p.expert_ids, b, s, e);
+  if (b >= p.blocks_cap) return;
   if ((unsigned)e >= (unsigned)p.E) return;
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int wn = wid % C::WN, wm = wid / C::WN;
@@ -604,11 +638,12 @@ __attribute__((amdgpu_waves_per_eu(1, BM >= 128 || BN == 128 ? 2 : 1))) k_down_t
   __shared__ float wsc[2 * kScaleRow];
   const int K = p.K, I = p.I, IS = I / 128;
   const int NT = K / BN;
-  const int logical = xcd_remap(blockIdx.x, (*p.ntp / BM) * NT);
+  const int nb = *p.ntp / BM;
+  const int logical = xcd_remap(blockIdx.x, nb * NT);
   if (logical < 0) return;
-  const int b = logical / NT, ct = logical % NT;
-  if (b >= p.blocks_cap || b * BM >= *p.ntp) return;
-  const int e = __builtin_amdgcn_readfirstlane(p.expert_ids[b]);  // uniform: descriptors in SGPRs
+  int b, ct, e;  // e uniform: descriptors in SGPRs
+  tile_coords(logical, NT, nb, p.expert_ids, b, ct, e);
+  if (b >= p.blocks_cap) return;
   if ((unsigned)e >= (unsigned)p.E) return;
   const int lane = threadIdx.x & 63, wid = wave_id();
   const int wn = wid % C::WN, wm = wid / C::WN;
