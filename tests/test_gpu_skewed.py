@@ -80,6 +80,25 @@ def test_routes_behind_padding(bm):
     assert d.max() <= 1e-3 * ref["out64"].std()
 
 
+def hot_expert_case(kind, bm, K):
+    """Zipf routing over 24 experts with route 0 of every one of 9 * bm + 37
+    tokens sent to expert 0 (each token's experts stay distinct)."""
+    T = 9 * bm + 37
+    c = datagen.make_case(kind, T, K, 256, 24, 4, routing="zipf", tag=f"hot-{kind}-{bm}",
+                          zipf_s=1.1)
+    ids = c.topk_ids.clone()
+    for t in range(T):
+        row = ids[t].tolist()
+        if 0 in row:
+            j = row.index(0)
+            row[0], row[j] = row[j], row[0]
+        else:
+            row[0] = 0
+        ids[t] = torch.tensor(row, dtype=ids.dtype)
+    c.topk_ids = ids.contiguous()
+    return to_gpu(c)
+
+
 @pytest.mark.parametrize("kind,bm", [("fp8_blockwise", 64), ("fp8_blockwise", 128),
                                      ("fp8_blockwise", 256), ("mxfp8", 64), ("mxfp8", 128)])
 def test_hot_expert_block_groups(kind, bm):
@@ -89,20 +108,7 @@ def test_hot_expert_block_groups(kind, bm):
     tile), followed by a group that mixes experts and goes block by block.
     Parity with the oracle over every token; for MXFP8 also the same bits as
     the 16-row streaming kernels."""
-    T = 9 * bm + 37
-    c = datagen.make_case(kind, T, 512, 256, 24, 4, routing="zipf", tag=f"hot-{kind}-{bm}",
-                          zipf_s=1.1)
-    ids = c.topk_ids.clone()
-    for t in range(T):  # route 0 of every token to expert 0, the token's experts stay distinct
-        row = ids[t].tolist()
-        if 0 in row:
-            j = row.index(0)
-            row[0], row[j] = row[j], row[0]
-        else:
-            row[0] = 0
-        ids[t] = torch.tensor(row, dtype=ids.dtype)
-    c.topk_ids = ids.contiguous()
-    c = to_gpu(c)
+    c = hot_expert_case(kind, bm, 512)
     out, align, ref = check(c, bm, 1, label="hot expert")
     eid = align[1].cpu().numpy()[: int(align[2].item()) // bm]
     say(f"      blocks {len(eid)}, of expert 0: {int((eid == 0).sum())}")
@@ -111,3 +117,15 @@ def test_hot_expert_block_groups(kind, bm):
         s16, _ = moe.run_case(c, block_m=16, split=1)
         torch.cuda.synchronize()
         assert np.array_equal(out_bits(out), out_bits(s16))
+
+
+@pytest.mark.parametrize("kind", ["fp8_blockwise", "mxfp8"])
+def test_hot_expert_block_groups_k_split(kind):
+    """The same plan at 64-row tiles with the gate/up K split over four
+    workgroups per tile (K = 2048: 16 K steps), whose partial sums and
+    tickets are indexed by the tile in walk order: parity with the oracle
+    over every token."""
+    c = hot_expert_case(kind, 64, 2048)
+    out, align, _ = check(c, 64, 1, label="hot expert, K split", tune={"k_split": 4})
+    eid = align[1].cpu().numpy()[: int(align[2].item()) // 64]
+    assert (eid[:8] == 0).all() and (eid == 0).sum() == 10
