@@ -924,8 +924,12 @@ k_ring(MoeArgs p) {
   }
 }
 
-// out[t, c:c+4] = bf16(sum_j w[t,j] * y[t*top_k+j, c:c+4] + sum_s y[shared s of t]),
-// j then s ascending.
+// out[t, c:c+8] = bf16(sum_j w[t,j] * y[t*top_k+j, c:c+8] + sum_s y[shared s of t]),
+// j then s ascending.  The routes are taken eight at a time: the placed
+// flags, weights and rows of all eight are requested before any is added,
+// so a token costs one memory round trip per eight routes rather than two
+// per route (a row whose flag is clear is loaded but not added: it lies in
+// the per-route buffer, and its contents are undefined).
 __global__ void __launch_bounds__(256) k_combine(MoeArgs p) {
   const int K = p.K;
   const int CT = (K + kCombineCols - 1) / kCombineCols;
@@ -935,24 +939,38 @@ __global__ void __launch_bounds__(256) k_combine(MoeArgs p) {
   float s[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) s[u] = 0.f;
-  // one route's 8 bf16 values, times w, added in route order
-  auto add = [&](size_t id, float w) {
-    const uint4 y = *reinterpret_cast<const uint4*>(p.yr + id * K + c);
-    const uint32_t v[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      s[2 * u] += w * __uint_as_float(v[u] << 16);
-      s[2 * u + 1] += w * __uint_as_float(v[u] & 0xFFFF0000u);
-    }
+  // route r of the token: routed r < top_k (its weight), then shared (weight 1)
+  const int nr = p.top_k + p.n_shared;
+  auto route_id = [&](int r) -> size_t {
+    return r < p.top_k ? (size_t)t * p.top_k + r
+                       : (size_t)p.T * p.top_k + (size_t)t * p.n_shared + (r - p.top_k);
   };
-  for (int j = 0; j < p.top_k; ++j) {
-    const size_t id = (size_t)t * p.top_k + j;
-    if (p.flags[id]) add(id, p.topk_w[id]);
-  }
-  // shared experts: every token, weight 1, after its routed experts
-  for (int j = 0; j < p.n_shared; ++j) {
-    const size_t id = (size_t)p.T * p.top_k + (size_t)t * p.n_shared + j;
-    if (p.flags[id]) add(id, 1.0f);
+  constexpr int kBatch = 8;
+  for (int r0 = 0; r0 < nr; r0 += kBatch) {
+    uint4 y[kBatch];
+    float w[kBatch];
+    int placed[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int r = r0 + u;
+      placed[u] = 0;
+      if (r < nr) {
+        const size_t id = route_id(r);
+        placed[u] = p.flags[id];
+        w[u] = r < p.top_k ? p.topk_w[id] : 1.0f;
+        y[u] = *reinterpret_cast<const uint4*>(p.yr + id * K + c);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (!placed[u]) continue;
+      const uint32_t v[4] = {y[u].x, y[u].y, y[u].z, y[u].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s[2 * q] += w[u] * __uint_as_float(v[q] << 16);
+        s[2 * q + 1] += w[u] * __uint_as_float(v[q] & 0xFFFF0000u);
+      }
+    }
   }
   uint4 o;
   o.x = (uint32_t)f32_to_bf16(s[0]) | ((uint32_t)f32_to_bf16(s[1]) << 16);
