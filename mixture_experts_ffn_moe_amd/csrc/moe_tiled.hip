@@ -361,7 +361,7 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, flo
                                           const uint32_t& sa_off, uint32_t sa_step, uint32_t b_off,
                                           const uint32_t (&b_soff)[TileCfg<KIND, BM, BN, NS>::B_INSTR],
                                           uint32_t sb_off, int up_split, int group,
-                                          F&& activation_offsets,
+                                          F&& activation_offsets, const bool& live,
                                           f32x4 (&acc)[4][TileCfg<KIND, BM, BN, NS>::NI]) {
   using C = TileCfg<KIND, BM, BN, NS>;
   constexpr int MI = C::MI, NI = C::NI;
@@ -416,7 +416,12 @@ __device__ __forceinline__ void tile_gemm(const TileSrc& src, uint8_t* smem, flo
     lds_barrier();
     const int ahead = slot + NS - 1;
     if (i + NS - 1 < ksteps) load(ahead >= NS ? ahead - NS : ahead, i + NS - 1);
-    tile_step<KIND, BM, BN, NS, B_NEXT>(smem + slot * C::STAGE, step_at(i), wsc_r, up_split, acc);
+    // blockwise: a wave whose 64 rows are all padding keeps its share of the
+    // loads and barriers but computes nothing (its sums stay zero; padding
+    // rows are never stored as results).  MX accumulates in place in the
+    // MFMA, and a branch around it costs the 256-row tiles register spills.
+    if (KIND != KIND_FP8B || live)
+      tile_step<KIND, BM, BN, NS, B_NEXT>(smem + slot * C::STAGE, step_at(i), wsc_r, up_split, acc);
     slot = slot + 1 == NS ? 0 : slot + 1;
   }
   __syncthreads();  // the caller reuses the LDS
@@ -494,10 +499,12 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   // after them, the weight-scale rows (blockwise: 4 loads) and, in a
   // loading wave, the weight side of the first stage (B, and the MX weight
   // scales) may be pending
+  bool live = true;  // this wave's rows hold a route (set once the route ids have arrived)
   auto activation_offsets = [&]() {
     if (wid < C::LW) wait_vmcnt<(KIND == KIND_FP8B ? 4 : 0) + C::B_INSTR + (KIND == KIND_MX ? 1 : 0)>();
     else wait_vmcnt<(KIND == KIND_FP8B ? 4 : 0)>();
     lds_barrier();
+    live = __ballot(id_of(wm * 64 + lane) >= 0) != 0;
 #pragma unroll
     for (int t = 0; t < C::A_INSTR; ++t) {
       int row, q;
@@ -509,7 +516,7 @@ __global__ void __launch_bounds__(BM >= 128 ? 512 : 256) __attribute__((amdgpu_w
   f32x4 acc[MI][NI];
   tile_gemm<KIND, BM, 256, NS, true>(src, smem, wsc, 0, KS / KW, kw * (KS / KW), KS, a_off, a_soff,
                                      sa_off, sa_step, b_off, b_soff, sb_off, HALF, e,
-                                     activation_offsets, acc);
+                                     activation_offsets, live, acc);
   if constexpr (KW > 1) {
     constexpr int PER = MI * NI * 4;  // floats per lane
     __shared__ int last;
@@ -692,8 +699,18 @@ __attribute__((amdgpu_waves_per_eu(1, BM >= 128 || BN == 128 ? 2 : 1))) k_down_t
   }
   f32x4 acc[MI][NI];
   // all NI subtiles of a wave are contiguous output columns (no gate/up split)
+  // once the route ids have arrived (issued first; the weight-scale rows,
+  // blockwise, and in a loading wave the weight side of the first stage may
+  // be pending): does this wave's row range hold a route
+  bool live = true;
+  auto rows_live = [&]() {
+    if (wid < C::LW) wait_vmcnt<(KIND == KIND_FP8B ? 4 : 0) + C::B_INSTR + (KIND == KIND_MX ? 1 : 0)>();
+    else wait_vmcnt<(KIND == KIND_FP8B ? 4 : 0)>();
+    lds_barrier();
+    live = __ballot(ids[scale_slot<C::SA_ROWS>(wm * 64 + lane)] >= 0) != 0;
+  };
   tile_gemm<KIND, BM, BN, NS, true>(src, smem, wsc, c0 / 128 - (BN / 128) * ct, IS, 0, IS, a_off, a_soff, sa_off, sa_step,
-                                     b_off, b_soff, sb_off, NI, e, [] {}, acc);
+                                     b_off, b_soff, sb_off, NI, e, rows_live, live, acc);
   // the tile's rows rounded to bf16, staged in LDS (rows of 2 BN bytes plus
   // 16 bytes of padding), then written out as whole 2 BN-byte row pieces with
   // non-temporal stores: the combine reads them once, much later, so they
